@@ -1,0 +1,258 @@
+"""Python binding of librx (``include/rx.h``): argument marshalling only.
+
+Every function here has the name of the C entry point it calls and takes
+torch tensors that live on the GPU; it checks dtype, device, contiguity and
+sizes, passes ``data_ptr()`` values and the current HIP stream, and raises
+``RxError`` on a non-zero status. All computation runs in librx's gfx950
+kernels; there is no CPU fallback. If ``librx.so`` is missing, importing the
+binding's entry points raises.
+
+The C ABI is asynchronous (stream-ordered); these wrappers do not
+synchronize.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+__all__ = [
+    "RX_FP32", "RX_BF16", "RX_FP8_E4M3", "RX_FP8_E5M2", "RX_DRR_SUM",
+    "RX_DRR_REQUANT", "RX_MAX_SRC", "RxError", "lib", "lib_path",
+    "rx_reduce_flat", "rx_reduce_scatter_chunk_bcast", "rx_tree_chunk",
+    "rx_quant_fp8", "rx_dequant_reduce_requant", "rx_status_string",
+    "EXPORTED_SYMBOLS",
+]
+
+RX_FP32, RX_BF16, RX_FP8_E4M3, RX_FP8_E5M2 = 0, 1, 2, 3
+RX_DRR_SUM, RX_DRR_REQUANT = 0, 1
+RX_MAX_SRC = 16
+
+EXPORTED_SYMBOLS = (
+    "rx_reduce_flat", "rx_reduce_scatter_chunk_bcast", "rx_tree_chunk",
+    "rx_quant_fp8", "rx_dequant_reduce_requant", "rx_status_string",
+    "rxtest_fp8_encode_bits", "rxtest_fp8_decode", "rxtest_bf16_round_bits",
+    "rxtest_group_max",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "librx.so")
+
+
+class RxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {rx_status_string(status)} ({status})")
+
+
+_lib = None
+_P = ctypes.c_void_p
+_PP = ctypes.POINTER(ctypes.c_void_p)
+_SZ = ctypes.c_size_t
+_I = ctypes.c_int
+
+
+def lib() -> ctypes.CDLL:
+    """Loads librx.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(path)
+        sig = {
+            "rx_reduce_flat": [_PP, _I, _SZ, _I, _P, _P],
+            "rx_reduce_scatter_chunk_bcast": [_PP, _I, _SZ, _I, _I, _PP, _P],
+            "rx_tree_chunk": [_SZ, _I, _I, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)],
+            "rx_quant_fp8": [_PP, _I, _SZ, _I, _I, _I, _PP, _PP, _P],
+            "rx_dequant_reduce_requant": [_PP, _PP, _I, _SZ, _I, _I, _I, _P, _P, _P, _I, _P],
+            "rxtest_fp8_encode_bits": [ctypes.c_uint32, _SZ, _I, _P, _P],
+            "rxtest_fp8_decode": [_P, _SZ, _I, _P, _P],
+            "rxtest_bf16_round_bits": [ctypes.c_uint32, _SZ, _P, _P],
+            "rxtest_group_max": [_P, _SZ, _I, _P, _P],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.rx_status_string.argtypes = [_I]
+        L.rx_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def rx_status_string(status: int) -> str:
+    return lib().rx_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise RxError(status, where)
+
+
+def _ptr_array(values: Sequence[int]):
+    return (ctypes.c_void_p * max(1, len(values)))(*values)
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _rx_dtype(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return RX_FP32
+    if t.dtype == torch.bfloat16:
+        return RX_BF16
+    raise TypeError(f"unsupported tensor dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _gpu(t, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _fp8_code(fmt) -> int:
+    if isinstance(fmt, str):
+        return {"e4m3": RX_FP8_E4M3, "e5m2": RX_FP8_E5M2}[fmt.lower()]
+    return int(fmt)
+
+
+def rx_reduce_flat(srcs: Sequence, dst, count: Optional[int] = None, stream=None) -> None:
+    """dst[i] = FP32 left fold of srcs[0][i] .. srcs[n-1][i], cast to dst's dtype."""
+    count = dst.numel() if count is None else count
+    dt = _rx_dtype(dst)
+    for k, s in enumerate(srcs):
+        _gpu(s, f"srcs[{k}]")
+        if s.dtype != dst.dtype or s.numel() < count:
+            raise ValueError(f"srcs[{k}] must be {dst.dtype} with >= {count} elements")
+    _gpu(dst, "dst")
+    if dst.numel() < count:
+        raise ValueError("dst too small")
+    arr = _ptr_array([s.data_ptr() for s in srcs])
+    _check(lib().rx_reduce_flat(arr, len(srcs), count, dt, dst.data_ptr(), _stream(stream)),
+           "rx_reduce_flat")
+
+
+def rx_tree_chunk(count: int, nsrc: int, dtype: int, rank: int) -> Tuple[int, int]:
+    lo, hi = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().rx_tree_chunk(count, nsrc, dtype, rank, ctypes.byref(lo), ctypes.byref(hi)),
+           "rx_tree_chunk")
+    return lo.value, hi.value
+
+
+def rx_reduce_scatter_chunk_bcast(srcs: Sequence, rank: int, dsts: Sequence,
+                                  count: Optional[int] = None, stream=None) -> None:
+    """Reduce chunk `rank` across srcs and write it into every dsts[j]."""
+    count = srcs[0].numel() if count is None else count
+    dt = _rx_dtype(srcs[0])
+    if len(dsts) != len(srcs):
+        raise ValueError("need one destination per source")
+    for k, t in enumerate(list(srcs) + list(dsts)):
+        _gpu(t, f"buffer {k}")
+        if t.dtype != srcs[0].dtype or t.numel() < count:
+            raise ValueError(f"buffer {k} must be {srcs[0].dtype} with >= {count} elements")
+    sa = _ptr_array([s.data_ptr() for s in srcs])
+    da = _ptr_array([d.data_ptr() for d in dsts])
+    _check(lib().rx_reduce_scatter_chunk_bcast(sa, len(srcs), count, dt, rank, da, _stream(stream)),
+           "rx_reduce_scatter_chunk_bcast")
+
+
+def rx_quant_fp8(srcs: Sequence, fmt, block: int, codes: Sequence, scales: Sequence,
+                 count: Optional[int] = None, stream=None) -> None:
+    """codes[j] (uint8, count) and scales[j] (float32, ceil(count/block)) from srcs[j]."""
+    import torch
+    count = srcs[0].numel() if count is None else count
+    dt = _rx_dtype(srcs[0])
+    nb = -(-count // block) if block > 0 else 0
+    if not (len(srcs) == len(codes) == len(scales)):
+        raise ValueError("need one code and one scale buffer per source")
+    for k, s in enumerate(srcs):
+        _gpu(s, f"srcs[{k}]")
+        if s.dtype != srcs[0].dtype or s.numel() < count:
+            raise ValueError(f"srcs[{k}] must be {srcs[0].dtype} with >= {count} elements")
+    for k, (c, sc) in enumerate(zip(codes, scales)):
+        _gpu(c, f"codes[{k}]")
+        _gpu(sc, f"scales[{k}]")
+        if c.dtype != torch.uint8 or c.numel() < count:
+            raise ValueError(f"codes[{k}] must be uint8 with >= {count} elements")
+        if sc.dtype != torch.float32 or sc.numel() < nb:
+            raise ValueError(f"scales[{k}] must be float32 with >= {nb} elements")
+    sa = _ptr_array([s.data_ptr() for s in srcs])
+    ca = _ptr_array([c.data_ptr() for c in codes])
+    qa = _ptr_array([s.data_ptr() for s in scales])
+    _check(lib().rx_quant_fp8(sa, len(srcs), count, dt, _fp8_code(fmt), block, ca, qa,
+                              _stream(stream)), "rx_quant_fp8")
+
+
+def rx_dequant_reduce_requant(codes: Sequence, scales: Sequence, fmt, block: int, mode: int,
+                              out_codes=None, out_scales=None, out_hp=None,
+                              count: Optional[int] = None, stream=None) -> None:
+    """Dequantize + FP32 sum; SUM writes out_hp, REQUANT writes out_codes /
+    out_scales (and out_hp = dequant(requant(sum)) when given)."""
+    import torch
+    count = codes[0].numel() if count is None else count
+    nb = -(-count // block) if block > 0 else 0
+    if len(codes) != len(scales):
+        raise ValueError("need one scale buffer per code buffer")
+    for k, (c, sc) in enumerate(zip(codes, scales)):
+        _gpu(c, f"codes[{k}]")
+        _gpu(sc, f"scales[{k}]")
+        if c.dtype != torch.uint8 or c.numel() < count:
+            raise ValueError(f"codes[{k}] must be uint8 with >= {count} elements")
+        if sc.dtype != torch.float32 or sc.numel() < nb:
+            raise ValueError(f"scales[{k}] must be float32 with >= {nb} elements")
+    hp_dt = RX_FP32
+    if out_hp is not None:
+        _gpu(out_hp, "out_hp")
+        hp_dt = _rx_dtype(out_hp)
+        if out_hp.numel() < count:
+            raise ValueError("out_hp too small")
+    if out_codes is not None:
+        _gpu(out_codes, "out_codes")
+        if out_codes.dtype != torch.uint8 or out_codes.numel() < count:
+            raise ValueError("out_codes must be uint8 with >= count elements")
+    if out_scales is not None:
+        _gpu(out_scales, "out_scales")
+        if out_scales.dtype != torch.float32 or out_scales.numel() < nb:
+            raise ValueError("out_scales must be float32 with >= ceil(count/block) elements")
+    ca = _ptr_array([c.data_ptr() for c in codes])
+    qa = _ptr_array([s.data_ptr() for s in scales])
+    ptr = lambda t: None if t is None else t.data_ptr()
+    _check(lib().rx_dequant_reduce_requant(ca, qa, len(codes), count, _fp8_code(fmt), block,
+                                           mode, ptr(out_codes), ptr(out_scales), ptr(out_hp),
+                                           hp_dt, _stream(stream)),
+           "rx_dequant_reduce_requant")
+
+
+# ---- test hooks (rx_testhooks.h) -------------------------------------------
+
+def rxtest_fp8_encode_bits(first: int, n: int, fmt, out, stream=None) -> None:
+    _check(lib().rxtest_fp8_encode_bits(first, n, _fp8_code(fmt), out.data_ptr(), _stream(stream)),
+           "rxtest_fp8_encode_bits")
+
+
+def rxtest_fp8_decode(codes, fmt, out, stream=None) -> None:
+    _check(lib().rxtest_fp8_decode(codes.data_ptr(), codes.numel(), _fp8_code(fmt),
+                                   out.data_ptr(), _stream(stream)), "rxtest_fp8_decode")
+
+
+def rxtest_bf16_round_bits(first: int, n: int, out, stream=None) -> None:
+    _check(lib().rxtest_bf16_round_bits(first, n, out.data_ptr(), _stream(stream)),
+           "rxtest_bf16_round_bits")
+
+
+def rxtest_group_max(values, g: int, out, stream=None) -> None:
+    _check(lib().rxtest_group_max(values.data_ptr(), values.numel() // 64, g, out.data_ptr(),
+                                  _stream(stream)), "rxtest_group_max")

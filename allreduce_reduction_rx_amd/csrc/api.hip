@@ -1,0 +1,252 @@
+// api.hip -- the C ABI of librx: argument validation, kernel-argument
+// packing and launch. Every check runs before the first HIP call, so an
+// invalid call enqueues nothing. The operations are documented in rx.h.
+#include <atomic>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "rx.h"
+#include "rx_internal.hpp"
+
+namespace rx {
+
+int device_cu_count()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        dev = 0;
+    if (dev < 64) {
+        int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (dev < 64)
+        cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+}  // namespace rx
+
+namespace {
+
+constexpr size_t kMaxCount = (size_t)1 << 38;  // elements per buffer
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+bool hp_type(rx_dtype_t t) { return t == RX_FP32 || t == RX_BF16; }
+bool fp8_type(rx_dtype_t t) { return t == RX_FP8_E4M3 || t == RX_FP8_E5M2; }
+bool valid_block(int b) { return b >= 32 && b <= 1024 && (b & (b - 1)) == 0; }
+
+rx_status_t launched(hipError_t e)
+{
+    if (e == hipSuccess)
+        return RX_OK;
+    const char* dbg = getenv("RX_DEBUG");
+    if (dbg && dbg[0] == '1')
+        fprintf(stderr, "librx: launch failed: %s\n", hipGetErrorString(e));
+    return RX_ERR_HIP;
+}
+
+// Shared checks of a source-pointer array: NULL array / entries, alignment.
+rx_status_t check_ptrs(const void* const* p, int n, bool align16)
+{
+    if (!p)
+        return RX_ERR_NULL;
+    for (int j = 0; j < n; ++j)
+        if (!p[j])
+            return RX_ERR_NULL;
+    for (int j = 0; j < n; ++j)
+        if (align16 ? !aligned16(p[j]) : !aligned4(p[j]))
+            return RX_ERR_ALIGN;
+    return RX_OK;
+}
+
+size_t tree_chunk_len(size_t count, int nsrc, rx_dtype_t dtype)
+{
+    const size_t ve = dtype == RX_BF16 ? 8 : 4;
+    size_t c = (count + (size_t)nsrc - 1) / (size_t)nsrc;
+    return (c + ve - 1) / ve * ve;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rx_status_string(rx_status_t s)
+{
+    switch (s) {
+    case RX_OK: return "RX_OK";
+    case RX_ERR_NULL: return "RX_ERR_NULL: a required pointer is NULL";
+    case RX_ERR_ARG: return "RX_ERR_ARG: invalid nsrc, rank, block, mode or count";
+    case RX_ERR_DTYPE: return "RX_ERR_DTYPE: dtype not supported by this operation";
+    case RX_ERR_ALIGN: return "RX_ERR_ALIGN: buffer misaligned (16 B data, 4 B scales)";
+    case RX_ERR_HIP: return "RX_ERR_HIP: the HIP runtime rejected the launch";
+    }
+    return "unknown rx_status_t";
+}
+
+rx_status_t rx_reduce_flat(const void* const* srcs, int nsrc, size_t count,
+                           rx_dtype_t dtype, void* dst, hipStream_t stream)
+{
+    if (!srcs || !dst)
+        return RX_ERR_NULL;
+    if (nsrc < 1 || nsrc > RX_MAX_SRC || count > kMaxCount)
+        return RX_ERR_ARG;
+    if (!hp_type(dtype))
+        return RX_ERR_DTYPE;
+    rx_status_t st = check_ptrs(srcs, nsrc, true);
+    if (st != RX_OK)
+        return st;
+    if (!aligned16(dst))
+        return RX_ERR_ALIGN;
+    if (count == 0)
+        return RX_OK;
+    rx::FlatArgs a = {};
+    for (int j = 0; j < nsrc; ++j)
+        a.src[j] = srcs[j];
+    a.dst = dst;
+    a.count = count;
+    return launched(rx::launch_reduce_flat(a, nsrc, dtype == RX_BF16 ? 1 : 0, stream));
+}
+
+rx_status_t rx_tree_chunk(size_t count, int nsrc, rx_dtype_t dtype, int rank,
+                          size_t* lo, size_t* hi)
+{
+    if (!lo || !hi)
+        return RX_ERR_NULL;
+    if (nsrc < 1 || nsrc > RX_MAX_SRC || rank < 0 || rank >= nsrc || count > kMaxCount)
+        return RX_ERR_ARG;
+    if (!hp_type(dtype))
+        return RX_ERR_DTYPE;
+    const size_t c = tree_chunk_len(count, nsrc, dtype);
+    size_t a = (size_t)rank * c;
+    if (a > count) a = count;
+    size_t b = a + c;
+    if (b > count) b = count;
+    *lo = a;
+    *hi = b;
+    return RX_OK;
+}
+
+rx_status_t rx_reduce_scatter_chunk_bcast(const void* const* srcs, int nsrc,
+                                          size_t count, rx_dtype_t dtype,
+                                          int rank, void* const* dsts,
+                                          hipStream_t stream)
+{
+    if (!srcs || !dsts)
+        return RX_ERR_NULL;
+    if (nsrc < 1 || nsrc > RX_MAX_SRC || rank < 0 || rank >= nsrc || count > kMaxCount)
+        return RX_ERR_ARG;
+    if (!hp_type(dtype))
+        return RX_ERR_DTYPE;
+    rx_status_t st = check_ptrs(srcs, nsrc, true);
+    if (st != RX_OK)
+        return st;
+    st = check_ptrs(reinterpret_cast<const void* const*>(dsts), nsrc, true);
+    if (st != RX_OK)
+        return st;
+    size_t lo = 0, hi = 0;
+    rx_tree_chunk(count, nsrc, dtype, rank, &lo, &hi);
+    if (lo >= hi)
+        return RX_OK;
+    rx::TreeArgs a = {};
+    for (int j = 0; j < nsrc; ++j) {
+        a.src[j] = srcs[j];
+        a.dst[j] = dsts[j];
+    }
+    a.lo = lo;
+    a.hi = hi;
+    return launched(rx::launch_tree(a, nsrc, dtype == RX_BF16 ? 1 : 0, stream));
+}
+
+rx_status_t rx_quant_fp8(const void* const* srcs, int nsrc, size_t count,
+                         rx_dtype_t src_dtype, rx_dtype_t fp8_dtype, int block,
+                         void* const* codes, float* const* scales,
+                         hipStream_t stream)
+{
+    if (!srcs || !codes || !scales)
+        return RX_ERR_NULL;
+    if (nsrc < 1 || nsrc > RX_MAX_SRC || !valid_block(block) || count > kMaxCount)
+        return RX_ERR_ARG;
+    if (!hp_type(src_dtype) || !fp8_type(fp8_dtype))
+        return RX_ERR_DTYPE;
+    rx_status_t st = check_ptrs(srcs, nsrc, true);
+    if (st != RX_OK)
+        return st;
+    st = check_ptrs(reinterpret_cast<const void* const*>(codes), nsrc, true);
+    if (st != RX_OK)
+        return st;
+    st = check_ptrs(reinterpret_cast<const void* const*>(scales), nsrc, false);
+    if (st != RX_OK)
+        return st;
+    if (count == 0)
+        return RX_OK;
+    rx::QuantArgs a = {};
+    for (int j = 0; j < nsrc; ++j) {
+        a.src[j] = srcs[j];
+        a.codes[j] = codes[j];
+        a.scales[j] = scales[j];
+    }
+    a.count = count;
+    a.nsrc = nsrc;
+    return launched(rx::launch_quant(a, src_dtype == RX_BF16 ? 1 : 0,
+                                     fp8_dtype == RX_FP8_E5M2 ? 1 : 0, block, stream));
+}
+
+rx_status_t rx_dequant_reduce_requant(const void* const* codes,
+                                      const float* const* scales, int nsrc,
+                                      size_t count, rx_dtype_t fp8_dtype,
+                                      int block, rx_drr_mode_t mode,
+                                      void* out_codes, float* out_scales,
+                                      void* out_hp, rx_dtype_t hp_dtype,
+                                      hipStream_t stream)
+{
+    if (!codes || !scales)
+        return RX_ERR_NULL;
+    if (nsrc < 1 || nsrc > RX_MAX_SRC || !valid_block(block) || count > kMaxCount)
+        return RX_ERR_ARG;
+    if (mode != RX_DRR_SUM && mode != RX_DRR_REQUANT)
+        return RX_ERR_ARG;
+    const bool requant = mode == RX_DRR_REQUANT;
+    if (requant) {
+        if (!out_codes || !out_scales)
+            return RX_ERR_NULL;
+    } else {
+        if (out_codes || out_scales)
+            return RX_ERR_ARG;
+        if (!out_hp)
+            return RX_ERR_NULL;
+    }
+    if (!fp8_type(fp8_dtype) || (out_hp && !hp_type(hp_dtype)))
+        return RX_ERR_DTYPE;
+    rx_status_t st = check_ptrs(codes, nsrc, true);
+    if (st != RX_OK)
+        return st;
+    st = check_ptrs(reinterpret_cast<const void* const*>(scales), nsrc, false);
+    if (st != RX_OK)
+        return st;
+    if ((out_codes && !aligned16(out_codes)) || (out_scales && !aligned4(out_scales)) ||
+        (out_hp && !aligned16(out_hp)))
+        return RX_ERR_ALIGN;
+    if (count == 0)
+        return RX_OK;
+    rx::DrrArgs a = {};
+    for (int j = 0; j < nsrc; ++j) {
+        a.codes[j] = codes[j];
+        a.scales[j] = scales[j];
+    }
+    a.out_codes = out_codes;
+    a.out_scales = out_scales;
+    a.out_hp = out_hp;
+    a.count = count;
+    a.block = block;
+    a.hp_bf16 = hp_dtype == RX_BF16 ? 1 : 0;
+    return launched(rx::launch_drr(a, nsrc, fp8_dtype == RX_FP8_E5M2 ? 1 : 0, requant, stream));
+}
+
+}  // extern "C"

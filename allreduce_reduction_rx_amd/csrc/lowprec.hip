@@ -1,0 +1,404 @@
+// lowprec.hip -- the low-precision collective path on gfx950: FP32/BF16 ->
+// OCP FP8 block quantizer, and the fused dequantize -> FP32 sum ->
+// requantize step (RCCLX article, code-journey.com, "Core feature 2:
+// Low-Precision Collectives": FP8 quantization with up to 4:1 compression,
+// FP32 compute; table rows "Data types" and "Compute precision").
+//
+// Encoding (a reading; the pages give only "FP8"): one FP32 scale per block
+// of B elements, s = A / FMAX with A the block absmax; elements multiplied
+// by r = FMAX / A, clamped to +-FMAX and converted with round-to-nearest-even
+// on the hardware converters (v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32).
+//
+// Both kernels are single streaming passes with no LDS: every load is a
+// coalesced 16-byte load (lane l of a wave reads vector base + l), the block
+// absmax is reduced across the lanes that hold the block with DPP and
+// permlane swaps, and each lane stores its own codes.
+#include <array>
+#include <utility>
+
+#include "rx_device.hpp"
+#include "rx_internal.hpp"
+
+namespace rx {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Quantizer
+// ---------------------------------------------------------------------------
+
+template <int DT, int F, int BLOCK>
+struct QuantShape {
+    static constexpr int kVE = DT == 0 ? 4 : 8;          // elements per 16-B vector
+    static constexpr int kLanesRaw = BLOCK / kVE;        // vectors per block
+    static constexpr int kLPB = kLanesRaw < 64 ? kLanesRaw : 64;  // lanes per block
+    static constexpr int kUPB = kLanesRaw / kLPB;        // loads per block (1, 2, 4)
+    static constexpr int kU = 4;                         // loads per lane per tile
+    static constexpr int kTileVec = kWave * kU;
+    static constexpr int kTileElems = kTileVec * kVE;    // 1024 (FP32) / 2048 (BF16)
+    static_assert(kU % kUPB == 0, "a tile holds whole blocks");
+    static_assert(kLanesRaw >= 1, "block of at least one vector");
+};
+
+// Widen vector x (16 bytes) to kVE floats.
+template <int DT>
+__device__ __forceinline__ void widen(const u32x4& x, float* f)
+{
+    if constexpr (DT == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) f[k] = bits_f32(x[k]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            f[2 * k] = bf16_lo(x[k]);
+            f[2 * k + 1] = bf16_hi(x[k]);
+        }
+    }
+}
+
+// Partial vector at the end of a ragged source: elements [e, count) loaded
+// one by one, the rest zero (zero is neutral for the absmax).
+template <int DT>
+__device__ __forceinline__ u32x4 load_partial(const void* src, size_t e, size_t count)
+{
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if constexpr (DT == 0) {
+        const uint32_t* p = static_cast<const uint32_t*>(src);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (e + k < count) x[k] = p[e + k];
+    } else {
+        const uint16_t* p = static_cast<const uint16_t*>(src);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (e + k < count) x[k / 2] |= (uint32_t)p[e + k] << (16 * (k & 1));
+    }
+    return x;
+}
+
+template <int DT, int F, int BLOCK>
+__global__ __launch_bounds__(256) void k_quant(QuantArgs a)
+{
+    using Sh = QuantShape<DT, F, BLOCK>;
+    constexpr int VE = Sh::kVE, U = Sh::kU, LPB = Sh::kLPB, UPB = Sh::kUPB;
+    const int lane = lane_id();
+    const uint32_t wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t waves_per_wg = blockDim.x / kWave;
+    const uint32_t wave = blockIdx.x * waves_per_wg + wave_in_wg;
+    const uint32_t nwaves = gridDim.x * waves_per_wg;
+    const uint32_t tiles_per_src = (uint32_t)((a.count + Sh::kTileElems - 1) / Sh::kTileElems);
+    const uint32_t total = tiles_per_src * (uint32_t)a.nsrc;
+
+    for (uint32_t t = wave; t < total; t += nwaves) {
+        const uint32_t j = t / tiles_per_src;
+        const uint32_t tile = t - j * tiles_per_src;
+        const void* src = a.src[j];
+        uint8_t* codes = static_cast<uint8_t*>(a.codes[j]);
+        float* scales = a.scales[j];
+        const size_t e0 = (size_t)tile * Sh::kTileElems;   // first element of the tile
+        const size_t v0 = e0 / VE;
+        const bool full = e0 + Sh::kTileElems <= a.count;
+
+        u32x4 x[U];
+        if (full) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                x[u] = ld16_stream(src, v0 + u * kWave + lane);
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const size_t e = (v0 + u * kWave + lane) * VE;
+                if (e + VE <= a.count)
+                    x[u] = ld16(src, v0 + u * kWave + lane);
+                else
+                    x[u] = load_partial<DT>(src, e, a.count);
+            }
+        }
+
+        float f[U][VE];
+        float amax[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            widen<DT>(x[u], f[u]);
+            float m = __builtin_fabsf(f[u][0]);
+#pragma unroll
+            for (int k = 1; k < VE; ++k)
+                m = __builtin_fmaxf(m, __builtin_fabsf(f[u][k]));
+            amax[u] = m;
+        }
+
+        // Block absmax across the lanes (and loads) that hold the block.
+        float s[U], r[U];
+        if constexpr (UPB == 1) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float A = bits_f32(group_max<LPB>(__builtin_bit_cast(uint32_t, amax[u])));
+                block_scale<F>(A, s[u], r[u]);
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < U / UPB; ++g) {
+                float m = amax[g * UPB];
+#pragma unroll
+                for (int q = 1; q < UPB; ++q)
+                    m = __builtin_fmaxf(m, amax[g * UPB + q]);
+                float A = bits_f32(group_max<64>(__builtin_bit_cast(uint32_t, m)));
+                float sg, rg;
+                block_scale<F>(A, sg, rg);
+#pragma unroll
+                for (int q = 0; q < UPB; ++q) {
+                    s[g * UPB + q] = sg;
+                    r[g * UPB + q] = rg;
+                }
+            }
+        }
+
+        // Encode and store: VE codes per lane per load (4 or 8 bytes).
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            uint32_t w[VE / 4];
+#pragma unroll
+            for (int q = 0; q < VE / 4; ++q) {
+                float y0 = clamp_fmax<F>(f[u][4 * q + 0] * r[u]);
+                float y1 = clamp_fmax<F>(f[u][4 * q + 1] * r[u]);
+                float y2 = clamp_fmax<F>(f[u][4 * q + 2] * r[u]);
+                float y3 = clamp_fmax<F>(f[u][4 * q + 3] * r[u]);
+                w[q] = f32x4_to_fp8<F>(y0, y1, y2, y3);
+            }
+            const size_t vi = v0 + u * kWave + lane;
+            const size_t e = vi * VE;
+            if (full || e + VE <= a.count) {
+                if constexpr (VE == 4) {
+                    reinterpret_cast<uint32_t*>(codes)[vi] = w[0];
+                } else {
+                    u32x2 p = {w[0], w[1]};
+                    reinterpret_cast<u32x2*>(codes)[vi] = p;
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < VE; ++k)
+                    if (e + k < a.count)
+                        codes[e + k] = (uint8_t)(w[k / 4] >> (8 * (k & 3)));
+            }
+            // one lane per block writes the scale
+            const bool leader = UPB == 1 ? (lane % LPB) == 0 : (lane == 0 && u % UPB == 0);
+            if (leader && e < a.count)
+                scales[e / BLOCK] = s[u];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize -> FP32 sum -> (requantize)
+// ---------------------------------------------------------------------------
+
+// Partial 16-code vector: codes [e, count) byte by byte, the rest code 0.
+__device__ __forceinline__ u32x4 load_codes_partial(const uint8_t* p, size_t e, size_t count)
+{
+    u32x4 x = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        if (e + k < count) x[k / 4] |= (uint32_t)p[e + k] << (8 * (k & 3));
+    return x;
+}
+
+template <int F>
+__device__ __forceinline__ void dequant16(const u32x4& c, float sc, float* v)
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float d[4];
+        fp8x4_to_f32<F>(c[q], d);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            v[4 * q + k] = d[k] * sc;
+    }
+}
+
+// Store 16 high-precision values of vector v (elements 16 v .. 16 v + 15).
+__device__ __forceinline__ void store_hp16(void* out, bool bf16, size_t v, size_t count,
+                                           const float* h)
+{
+    const size_t e = v * 16;
+    if (e + 16 <= count) {
+        if (bf16) {
+            u32x4 p0 = {pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]),
+                        pack_bf16(h[4], h[5]), pack_bf16(h[6], h[7])};
+            u32x4 p1 = {pack_bf16(h[8], h[9]), pack_bf16(h[10], h[11]),
+                        pack_bf16(h[12], h[13]), pack_bf16(h[14], h[15])};
+            st16(out, 2 * v, p0);
+            st16(out, 2 * v + 1, p1);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                u32x4 p = {__builtin_bit_cast(uint32_t, h[4 * q]),
+                           __builtin_bit_cast(uint32_t, h[4 * q + 1]),
+                           __builtin_bit_cast(uint32_t, h[4 * q + 2]),
+                           __builtin_bit_cast(uint32_t, h[4 * q + 3])};
+                st16(out, 4 * v + q, p);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if (e + k < count) {
+                if (bf16)
+                    static_cast<uint16_t*>(out)[e + k] = (uint16_t)(pack_bf16(h[k], 0.0f) & 0xFFFFu);
+                else
+                    static_cast<float*>(out)[e + k] = h[k];
+            }
+        }
+    }
+}
+
+template <int F, int N, bool REQUANT>
+__global__ __launch_bounds__(256) void k_drr(DrrArgs a)
+{
+    const int lane = lane_id();
+    const uint32_t wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t waves_per_wg = blockDim.x / kWave;
+    const uint32_t wave = blockIdx.x * waves_per_wg + wave_in_wg;
+    const uint32_t nwaves = gridDim.x * waves_per_wg;
+    const size_t count = a.count;
+    const uint32_t ntiles = (uint32_t)((count + 1023) / 1024);  // 64 lanes x 16 codes
+    const int lpb = a.block / 16;                                 // lanes per block: 2..64
+    const int bshift = __builtin_ctz((unsigned)a.block);
+
+    for (uint32_t t = wave; t < ntiles; t += nwaves) {
+        const size_t v = (size_t)t * kWave + lane;   // this lane's 16-code vector
+        const size_t e = v * 16;
+        const bool full = ((size_t)t + 1) * 1024 <= count;
+        const size_t b = e >> bshift;
+        const bool valid = e < count;
+
+        u32x4 c[N];
+        float sc[N];
+#pragma unroll
+        for (int r = 0; r < N; ++r) {
+            const uint8_t* cp = static_cast<const uint8_t*>(a.codes[r]);
+            if (full || e + 16 <= count)
+                c[r] = ld16_stream(cp, v);
+            else
+                c[r] = load_codes_partial(cp, e, count);
+            sc[r] = valid ? a.scales[r][b] : 0.0f;
+        }
+
+        float S[16];
+        dequant16<F>(c[0], sc[0], S);
+#pragma unroll
+        for (int r = 1; r < N; ++r) {
+            float d[16];
+            dequant16<F>(c[r], sc[r], d);
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                S[k] = S[k] + d[k];
+        }
+
+        if constexpr (!REQUANT) {
+            store_hp16(a.out_hp, a.hp_bf16 != 0, v, count, S);
+            continue;
+        }
+
+        // Requantize the FP32 sum with the same block size and format.
+        float m = __builtin_fabsf(S[0]);
+#pragma unroll
+        for (int k = 1; k < 16; ++k)
+            m = __builtin_fmaxf(m, __builtin_fabsf(S[k]));
+        const float A = bits_f32(group_max_rt(__builtin_bit_cast(uint32_t, m), lpb));
+        float s2, r2;
+        block_scale<F>(A, s2, r2);
+        u32x4 q;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            q[p] = f32x4_to_fp8<F>(clamp_fmax<F>(S[4 * p + 0] * r2), clamp_fmax<F>(S[4 * p + 1] * r2),
+                                   clamp_fmax<F>(S[4 * p + 2] * r2), clamp_fmax<F>(S[4 * p + 3] * r2));
+        uint8_t* oc = static_cast<uint8_t*>(a.out_codes);
+        if (full || e + 16 <= count) {
+            st16(oc, v, q);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                if (e + k < count) oc[e + k] = (uint8_t)(q[k / 4] >> (8 * (k & 3)));
+        }
+        if (valid && (lane % lpb) == 0)
+            a.out_scales[b] = s2;
+
+        if (a.out_hp) {
+            float h[16];
+            dequant16<F>(q, s2, h);
+            store_hp16(a.out_hp, a.hp_bf16 != 0, v, count, h);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch tables
+// ---------------------------------------------------------------------------
+
+using QuantFn = void (*)(QuantArgs);
+using DrrFn = void (*)(DrrArgs);
+
+template <int DT, int F, int... L>
+constexpr std::array<QuantFn, sizeof...(L)> quant_row(std::integer_sequence<int, L...>)
+{
+    return {{&k_quant<DT, F, (32 << L)>...}};
+}
+
+// [src dtype][fmt][log2(block) - 5]
+const std::array<QuantFn, 6> kQuant[2][2] = {
+    {quant_row<0, 0>(std::make_integer_sequence<int, 6>{}), quant_row<0, 1>(std::make_integer_sequence<int, 6>{})},
+    {quant_row<1, 0>(std::make_integer_sequence<int, 6>{}), quant_row<1, 1>(std::make_integer_sequence<int, 6>{})}};
+
+template <int F, bool R, int... I>
+constexpr std::array<DrrFn, sizeof...(I)> drr_row(std::integer_sequence<int, I...>)
+{
+    return {{&k_drr<F, I + 1, R>...}};
+}
+
+// [fmt][requant][nsrc - 1]
+const std::array<DrrFn, kMaxSrc> kDrr[2][2] = {
+    {drr_row<0, false>(std::make_integer_sequence<int, kMaxSrc>{}),
+     drr_row<0, true>(std::make_integer_sequence<int, kMaxSrc>{})},
+    {drr_row<1, false>(std::make_integer_sequence<int, kMaxSrc>{}),
+     drr_row<1, true>(std::make_integer_sequence<int, kMaxSrc>{})}};
+
+// One wave per tile; small jobs use 64-thread workgroups so that the tiles
+// spread over every CU, large ones 256 threads and at most 8 workgroups per
+// CU with a grid-stride loop.
+void wave_geometry(size_t tiles, dim3& grid, dim3& block)
+{
+    const size_t cus = (size_t)device_cu_count();
+    if (tiles == 0) tiles = 1;
+    unsigned wg = tiles < cus * 4 * 2 ? 64u : 256u;
+    size_t waves_per_wg = wg / kWave;
+    size_t blocks = (tiles + waves_per_wg - 1) / waves_per_wg;
+    size_t cap = cus * (2048 / wg);
+    if (blocks > cap) blocks = cap;
+    grid = dim3((unsigned)blocks);
+    block = dim3(wg);
+}
+
+}  // namespace
+
+hipError_t launch_quant(const QuantArgs& a, int src_dtype, int fmt, int block, hipStream_t s)
+{
+    const int lb = __builtin_ctz((unsigned)block) - 5;
+    const size_t tile_elems = src_dtype == 0 ? 1024 : 2048;
+    const size_t tiles = (a.count + tile_elems - 1) / tile_elems * (size_t)a.nsrc;
+    dim3 grid, blk;
+    wave_geometry(tiles, grid, blk);
+    QuantArgs arg = a;
+    void* params[] = {&arg};
+    return hipLaunchKernel((const void*)kQuant[src_dtype][fmt][lb], grid, blk, params, 0, s);
+}
+
+hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStream_t s)
+{
+    const size_t tiles = (a.count + 1023) / 1024;
+    dim3 grid, blk;
+    wave_geometry(tiles, grid, blk);
+    DrrArgs arg = a;
+    void* params[] = {&arg};
+    return hipLaunchKernel((const void*)kDrr[fmt][requant ? 1 : 0][nsrc - 1], grid, blk, params, 0, s);
+}
+
+}  // namespace rx

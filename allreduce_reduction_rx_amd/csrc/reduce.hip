@@ -1,0 +1,185 @@
+// reduce.hip -- DDA flat local reduce and DDA tree per-rank step (gfx950).
+//
+// DDA flat: each rank reads all peers' buffers directly and reduces locally
+// (RCCLX article, code-journey.com, "Core feature 1: Direct Data Access
+// (DDA)", DDA Flat item). DDA tree: reduce-scatter then all-gather with
+// direct access (same section, DDA Tree item); one rank reduces its chunk
+// and pushes it to every destination. Sums are FP32 ("Core feature 2", table
+// row "Compute precision"), folded in source order 0..N-1.
+//
+// Both kernels are HBM-bound streams: one 16-byte load per source per lane
+// (all N issued before the first add), FP32 adds, one 16-byte store per
+// destination. N is a template parameter so the source loop unrolls and the
+// pointer table is read with scalar loads from the kernarg segment.
+#include <array>
+#include <utility>
+
+#include "rx_device.hpp"
+#include "rx_internal.hpp"
+
+namespace rx {
+namespace {
+
+template <int DT> struct Elem;
+template <> struct Elem<0> { static constexpr int kVE = 4; };  // FP32: 4 per 16 B
+template <> struct Elem<1> { static constexpr int kVE = 8; };  // BF16: 8 per 16 B
+
+// Fold vector `v` (16 bytes) of N sources; returns the narrowed 16 bytes.
+template <int DT, int N>
+__device__ __forceinline__ u32x4 fold_vec(const void* const* src, size_t v)
+{
+    u32x4 x[N];
+#pragma unroll
+    for (int r = 0; r < N; ++r)
+        x[r] = ld16(src[r], v);
+    u32x4 out;
+    if constexpr (DT == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float acc = bits_f32(x[0][k]);
+#pragma unroll
+            for (int r = 1; r < N; ++r)
+                acc = acc + bits_f32(x[r][k]);
+            out[k] = __builtin_bit_cast(uint32_t, acc);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float lo = bf16_lo(x[0][k]);
+            float hi = bf16_hi(x[0][k]);
+#pragma unroll
+            for (int r = 1; r < N; ++r) {
+                lo = lo + bf16_lo(x[r][k]);
+                hi = hi + bf16_hi(x[r][k]);
+            }
+            out[k] = pack_bf16(lo, hi);
+        }
+    }
+    return out;
+}
+
+// One element i (tail of a count that is not a multiple of 16 bytes).
+template <int DT, int N>
+__device__ __forceinline__ float fold_elem(const void* const* src, size_t i)
+{
+    float acc;
+    if constexpr (DT == 0) {
+        acc = static_cast<const float*>(src[0])[i];
+#pragma unroll
+        for (int r = 1; r < N; ++r)
+            acc = acc + static_cast<const float*>(src[r])[i];
+    } else {
+        acc = bits_f32((uint32_t)static_cast<const uint16_t*>(src[0])[i] << 16);
+#pragma unroll
+        for (int r = 1; r < N; ++r)
+            acc = acc + bits_f32((uint32_t)static_cast<const uint16_t*>(src[r])[i] << 16);
+    }
+    return acc;
+}
+
+template <int DT>
+__device__ __forceinline__ void store_elem(void* dst, size_t i, float v)
+{
+    if constexpr (DT == 0)
+        static_cast<float*>(dst)[i] = v;
+    else
+        static_cast<uint16_t*>(dst)[i] = (uint16_t)(pack_bf16(v, 0.0f) & 0xFFFFu);
+}
+
+template <int DT, int N>
+__global__ __launch_bounds__(256) void k_reduce_flat(FlatArgs a)
+{
+    constexpr int VE = Elem<DT>::kVE;
+    const size_t nvec = a.count / VE;
+    const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t v = gid; v < nvec; v += stride)
+        st16(a.dst, v, fold_vec<DT, N>(a.src, v));
+    const size_t i = nvec * VE + gid;
+    if (i < a.count)
+        store_elem<DT>(a.dst, i, fold_elem<DT, N>(a.src, i));
+}
+
+template <int DT, int N>
+__global__ __launch_bounds__(256) void k_tree(TreeArgs a)
+{
+    constexpr int VE = Elem<DT>::kVE;
+    const size_t v0 = a.lo / VE;          // lo is 16-B aligned (or == hi)
+    const size_t v1 = a.hi / VE;
+    const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t v = v0 + gid; v < v1; v += stride) {
+        u32x4 y = fold_vec<DT, N>(a.src, v);
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+            st16(a.dst[j], v, y);
+    }
+    // hi is a multiple of VE unless it is the end of a ragged message
+    const size_t i = (v1 > v0 ? v1 : v0) * VE + gid;
+    if (i >= a.lo && i < a.hi) {
+        float z = fold_elem<DT, N>(a.src, i);
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+            store_elem<DT>(a.dst[j], i, z);
+    }
+}
+
+using FlatFn = void (*)(FlatArgs);
+using TreeFn = void (*)(TreeArgs);
+
+template <int DT, int... I>
+constexpr std::array<FlatFn, sizeof...(I)> flat_table(std::integer_sequence<int, I...>)
+{
+    return {{&k_reduce_flat<DT, I + 1>...}};
+}
+template <int DT, int... I>
+constexpr std::array<TreeFn, sizeof...(I)> tree_table(std::integer_sequence<int, I...>)
+{
+    return {{&k_tree<DT, I + 1>...}};
+}
+
+const std::array<FlatFn, kMaxSrc> kFlat[2] = {
+    flat_table<0>(std::make_integer_sequence<int, kMaxSrc>{}),
+    flat_table<1>(std::make_integer_sequence<int, kMaxSrc>{})};
+const std::array<TreeFn, kMaxSrc> kTree[2] = {
+    tree_table<0>(std::make_integer_sequence<int, kMaxSrc>{}),
+    tree_table<1>(std::make_integer_sequence<int, kMaxSrc>{})};
+
+// Threads = one per 16-byte output vector. Small messages (decode sizes) use
+// 64-thread workgroups so the vectors spread over every CU; large ones use
+// 256 threads and a grid of at most 8 workgroups per CU, looping.
+void geometry(size_t nvec, dim3& grid, dim3& block)
+{
+    const size_t cus = (size_t)device_cu_count();
+    size_t threads = nvec ? nvec : 1;
+    unsigned wg = threads < cus * 256 * 2 ? 64u : 256u;
+    size_t blocks = (threads + wg - 1) / wg;
+    size_t cap = cus * (2048 / wg);
+    if (blocks > cap) blocks = cap;
+    grid = dim3((unsigned)blocks);
+    block = dim3(wg);
+}
+
+}  // namespace
+
+hipError_t launch_reduce_flat(const FlatArgs& a, int nsrc, int dtype, hipStream_t s)
+{
+    const int ve = dtype == 0 ? 4 : 8;
+    dim3 grid, block;
+    geometry(a.count / ve, grid, block);
+    FlatArgs arg = a;
+    void* params[] = {&arg};
+    return hipLaunchKernel((const void*)kFlat[dtype][nsrc - 1], grid, block, params, 0, s);
+}
+
+hipError_t launch_tree(const TreeArgs& a, int nsrc, int dtype, hipStream_t s)
+{
+    const int ve = dtype == 0 ? 4 : 8;
+    dim3 grid, block;
+    geometry((a.hi - a.lo) / ve, grid, block);
+    TreeArgs arg = a;
+    void* params[] = {&arg};
+    return hipLaunchKernel((const void*)kTree[dtype][nsrc - 1], grid, block, params, 0, s);
+}
+
+}  // namespace rx

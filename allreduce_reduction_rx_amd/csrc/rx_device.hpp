@@ -1,0 +1,182 @@
+// rx_device.hpp -- gfx950 device helpers shared by the rx kernels:
+// 16-byte vector memory access, BF16/FP8 conversions on the hardware
+// converters, and cross-lane maxima on DPP / permlane swaps.
+//
+// Everything here is written for CDNA4 (gfx950), wave64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rx {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// FP8 formats (OCP). E4M3 = E4M3FN: largest finite 448; E5M2: 57344.
+enum Fp8 { kE4M3 = 0, kE5M2 = 1 };
+
+template <int F> struct Fp8Traits;
+template <> struct Fp8Traits<kE4M3> { static constexpr float kMax = 448.0f; };
+template <> struct Fp8Traits<kE5M2> { static constexpr float kMax = 57344.0f; };
+
+// ---------------------------------------------------------------------------
+// Memory
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ u32x4 ld16(const void* base, size_t vec)
+{
+    return reinterpret_cast<const u32x4*>(base)[vec];
+}
+
+// Streaming load: data read once, not worth keeping in the caches.
+__device__ __forceinline__ u32x4 ld16_stream(const void* base, size_t vec)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + vec);
+}
+
+__device__ __forceinline__ void st16(void* base, size_t vec, u32x4 v)
+{
+    reinterpret_cast<u32x4*>(base)[vec] = v;
+}
+
+__device__ __forceinline__ void st16_stream(void* base, size_t vec, u32x4 v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base) + vec);
+}
+
+// ---------------------------------------------------------------------------
+// BF16 <-> FP32
+// ---------------------------------------------------------------------------
+
+// The two BF16 halves of a dword, widened exactly to FP32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// Two FP32 -> packed BF16 pair (lo in bits 0..15), round to nearest even on
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    f32x2 v = {lo, hi};
+    bf16x2 b = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 (OCP) on the gfx950 converters
+// ---------------------------------------------------------------------------
+
+// Four codes of a dword -> FP32 (byte k -> out[k]); exact.
+template <int F>
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* out)
+{
+    f32x2 a, b;
+    if constexpr (F == kE4M3) {
+        a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+        b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    } else {
+        a = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+        b = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+    }
+    out[0] = a[0]; out[1] = a[1]; out[2] = b[0]; out[3] = b[1];
+}
+
+// Four FP32 values, already inside [-FMAX, FMAX], -> four codes (x[k] -> byte
+// k), round to nearest even. Pre-clamping makes the conversion saturating.
+template <int F>
+__device__ __forceinline__ uint32_t f32x4_to_fp8(float x0, float x1, float x2, float x3)
+{
+    int w;
+    if constexpr (F == kE4M3) {
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+    } else {
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(x0, x1, 0, false);
+        w = __builtin_amdgcn_cvt_pk_bf8_f32(x2, x3, w, true);
+    }
+    return (uint32_t)w;
+}
+
+template <int F>
+__device__ __forceinline__ float clamp_fmax(float y)
+{
+    constexpr float m = Fp8Traits<F>::kMax;
+    return __builtin_amdgcn_fmed3f(y, -m, m);
+}
+
+// Block scale and its reciprocal from the block absmax A: s = A / FMAX and
+// r = FMAX / A, each one correctly rounded FP32 division; A == 0, s == 0 or
+// r not finite gives s = r = 1.
+template <int F>
+__device__ __forceinline__ void block_scale(float a, float& s, float& r)
+{
+    constexpr float m = Fp8Traits<F>::kMax;
+    float sv = a / m;
+    float rv = m / a;
+    bool degenerate = (a == 0.0f) | (sv == 0.0f) | !__builtin_isfinite(rv);
+    s = degenerate ? 1.0f : sv;
+    r = degenerate ? 1.0f : rv;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane maximum over aligned groups of G lanes (G = 1..64, power of 2).
+// Operates on |x| bit patterns: for non-NaN values the unsigned order of the
+// magnitude bits is the order of the magnitudes, and max is exact.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+template <int Ctrl>
+__device__ __forceinline__ uint32_t dpp(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, Ctrl, 0xF, 0xF, false);
+}
+
+template <int G>
+__device__ __forceinline__ uint32_t group_max(uint32_t v)
+{
+    static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "group size");
+    if constexpr (G >= 2) v = umax(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) v = umax(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) v = umax(v, dpp<0x141>(v));  // row_half_mirror
+    if constexpr (G >= 16) v = umax(v, dpp<0x140>(v)); // row_mirror
+    if constexpr (G >= 32) {                           // rows 0<->1, 2<->3
+        auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = umax(p[0], p[1]);
+    }
+    if constexpr (G >= 64) {                           // halves 0<->1
+        auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        v = umax(p[0], p[1]);
+    }
+    return v;
+}
+
+// Runtime group size (wave-uniform), for kernels whose block size is an
+// argument.
+__device__ __forceinline__ uint32_t group_max_rt(uint32_t v, int g)
+{
+    if (g >= 2) v = umax(v, dpp<0xB1>(v));
+    if (g >= 4) v = umax(v, dpp<0x4E>(v));
+    if (g >= 8) v = umax(v, dpp<0x141>(v));
+    if (g >= 16) v = umax(v, dpp<0x140>(v));
+    if (g >= 32) {
+        auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = umax(p[0], p[1]);
+    }
+    if (g >= 64) {
+        auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        v = umax(p[0], p[1]);
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __builtin_bit_cast(uint32_t, x) & 0x7FFFFFFFu; }
+__device__ __forceinline__ float bits_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+}  // namespace rx

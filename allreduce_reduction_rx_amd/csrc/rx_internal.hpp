@@ -1,0 +1,57 @@
+// rx_internal.hpp -- host-side declarations shared by the entry points
+// (api.hip) and the kernel translation units. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rx {
+
+constexpr int kMaxSrc = 16;
+
+// Kernel arguments are passed by value, so the pointer tables travel in the
+// kernarg segment and the caller's host arrays can be freed on return.
+struct FlatArgs {
+    const void* src[kMaxSrc];
+    void* dst;
+    size_t count;     // elements
+};
+
+struct TreeArgs {
+    const void* src[kMaxSrc];
+    void* dst[kMaxSrc];
+    size_t lo, hi;    // element range of this rank's chunk
+};
+
+struct QuantArgs {
+    const void* src[kMaxSrc];
+    void* codes[kMaxSrc];
+    float* scales[kMaxSrc];
+    size_t count;     // elements per source
+    int nsrc;
+};
+
+struct DrrArgs {
+    const void* codes[kMaxSrc];
+    const float* scales[kMaxSrc];
+    void* out_codes;   // REQUANT only
+    float* out_scales; // REQUANT only
+    void* out_hp;      // SUM: required; REQUANT: optional
+    size_t count;
+    int block;         // elements per scale block
+    int hp_bf16;       // out_hp element type: 1 = BF16, 0 = FP32
+};
+
+// Launch geometry helper: number of compute units of the current device
+// (cached per device on first use).
+int device_cu_count();
+
+// Launchers (return the hipError_t of the launch). dtype: 0 FP32, 1 BF16.
+// fmt: 0 E4M3, 1 E5M2.
+hipError_t launch_reduce_flat(const FlatArgs& a, int nsrc, int dtype, hipStream_t s);
+hipError_t launch_tree(const TreeArgs& a, int nsrc, int dtype, hipStream_t s);
+hipError_t launch_quant(const QuantArgs& a, int src_dtype, int fmt, int block, hipStream_t s);
+hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStream_t s);
+
+}  // namespace rx

@@ -1,0 +1,173 @@
+/*
+ * rx.h -- C ABI of librx, the one-GPU data-parallel core of the RCCLX
+ * allreduce paths, written for AMD Instinct MI355X (gfx950).
+ *
+ * The pages this library follows describe Meta's RCCLX (the RCCLX article on
+ * code-journey.com, pt and ko editions, and its Chinese summary on
+ * ai-stack.site). On one GPU, the N "rank" buffers of a collective are N
+ * separate device allocations; every entry point takes an array of those
+ * pointers and performs one rank's local share of the collective.
+ *
+ * Conventions shared by every entry point
+ *   - Pointer ARRAYS (srcs, dsts, codes, scales) live in host memory and are
+ *     read only during the call (copied by value into kernel arguments); the
+ *     caller may free them on return. Every pointer IN them is a device
+ *     pointer.
+ *   - The caller owns all device memory. The library allocates nothing and
+ *     keeps no state beyond a per-device cache of the compute-unit count.
+ *   - Calls are stream-ordered and asynchronous: they return after enqueueing
+ *     on `stream` (0 = the null stream). Synchronize the stream to observe
+ *     results.
+ *   - Validation happens before any HIP call; on any error nothing is
+ *     enqueued. count == 0 returns RX_OK without launching anything.
+ *   - Data buffers (sources, destinations, FP8 code buffers, high-precision
+ *     outputs) must be 16-byte aligned; scale arrays 4-byte aligned.
+ *   - Exact aliasing of an output with a source of the same element is
+ *     allowed where stated (each element is read from every source before
+ *     the same thread writes it); any partial overlap is undefined.
+ *   - Sums are FP32, folded left in source order 0..nsrc-1 starting from
+ *     source 0, one FP32 rounding per addition; BF16 results are rounded to
+ *     nearest even. No NaN/Inf inputs are supported.
+ *   - Stateless and reentrant; concurrent calls on different streams are
+ *     independent.
+ */
+#ifndef RX_H
+#define RX_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RX_FP32 = 0,     /* IEEE binary32                                        */
+    RX_BF16 = 1,     /* bfloat16                                             */
+    RX_FP8_E4M3 = 2, /* OCP E4M3 (E4M3FN): bias 7, max 448, no Inf           */
+    RX_FP8_E5M2 = 3  /* OCP E5M2: bias 15, max 57344                         */
+} rx_dtype_t;
+
+typedef enum {
+    RX_OK = 0,
+    RX_ERR_NULL = 1,  /* a required pointer or pointer array is NULL        */
+    RX_ERR_ARG = 2,   /* nsrc, rank, block or mode/pointer combination      */
+    RX_ERR_DTYPE = 3, /* dtype not supported by this operation              */
+    RX_ERR_ALIGN = 4, /* data buffer not 16-B aligned / scales not 4-B      */
+    RX_ERR_HIP = 5    /* the HIP runtime reported an error at launch        */
+} rx_status_t;
+
+typedef enum {
+    RX_DRR_SUM = 0,     /* dequantize + FP32 sum -> high-precision output     */
+    RX_DRR_REQUANT = 1  /* dequantize + FP32 sum -> requantized FP8 (+ hp)    */
+} rx_drr_mode_t;
+
+#define RX_MAX_SRC 16
+
+/*
+ * DDA flat, one rank's local reduce. Each rank reads every peer's buffer
+ * directly and reduces locally, which turns an O(N)-step allreduce into one
+ * step for small messages (RCCLX article, "Core feature 1: Direct Data
+ * Access (DDA)", DDA Flat item); SUM with FP32 accumulation ("Core feature
+ * 2: Low-Precision Collectives", feature table row "Compute precision";
+ * "Practical guide", usage example).
+ *
+ *   dst[i] = cast( (((x_0[i] + x_1[i]) + x_2[i]) + ... ) + x_{nsrc-1}[i] )
+ *
+ * srcs   : nsrc device pointers, each `count` elements of `dtype`.
+ * nsrc   : 1 .. RX_MAX_SRC.
+ * dtype  : RX_FP32 or RX_BF16 (sources and dst share it).
+ * dst    : `count` elements of `dtype`; may equal one srcs[j] exactly
+ *          (in-place allreduce).
+ */
+rx_status_t rx_reduce_flat(const void* const* srcs, int nsrc, size_t count,
+                           rx_dtype_t dtype, void* dst, hipStream_t stream);
+
+/*
+ * DDA tree, one rank's step: the reduce-scatter phase reduces this rank's
+ * chunk across all sources, and the all-gather phase pushes the reduced
+ * chunk into every destination, both by direct access (RCCLX article, "Core
+ * feature 1: Direct Data Access (DDA)", DDA Tree item). Each rank reads and
+ * writes one message's worth of bytes, the same volume as a ring.
+ *
+ * Chunking (the pages do not fix it): c = roundup(ceil(count/nsrc), V) with
+ * V = 16 / sizeof(dtype), so every chunk starts 16-B aligned; chunk k is
+ * [min(k c, count), min(k c + c, count)) and trailing ranks may own a short
+ * or empty chunk. rx_tree_chunk() returns the bounds.
+ *
+ * srcs   : nsrc device pointers, each `count` elements of `dtype`.
+ * rank   : 0 .. nsrc-1, the chunk this call reduces.
+ * dsts   : nsrc device pointers, each `count` elements of `dtype`; only the
+ *          chunk is written, everything outside it is left untouched.
+ *          dsts[j] may equal srcs[j] exactly.
+ */
+rx_status_t rx_reduce_scatter_chunk_bcast(const void* const* srcs, int nsrc,
+                                          size_t count, rx_dtype_t dtype,
+                                          int rank, void* const* dsts,
+                                          hipStream_t stream);
+
+/* Host helper: bounds [*lo, *hi) of chunk `rank` (no HIP call). */
+rx_status_t rx_tree_chunk(size_t count, int nsrc, rx_dtype_t dtype, int rank,
+                          size_t* lo, size_t* hi);
+
+/*
+ * Low-precision path, sender side: FP32/BF16 -> FP8 with one FP32 scale per
+ * block, up to 4:1 compression (RCCLX article, "Core feature 2:
+ * Low-Precision Collectives", opening paragraph and feature table row "Data
+ * types"). The pages do not give the encoding; this library fixes:
+ *   block b = elements [b*block, min((b+1)*block, count)) of each source,
+ *   A = max |x| over the block,
+ *   s = A / FMAX, r = FMAX / A (each one correctly rounded FP32 division),
+ *   (A == 0, s == 0 or r not finite: s = r = 1),
+ *   code_i = OCP FP8 of fl32(x_i * r), round to nearest even, saturating.
+ *
+ * srcs      : nsrc device pointers, `count` elements of src_dtype each.
+ * src_dtype : RX_FP32 or RX_BF16.
+ * fp8_dtype : RX_FP8_E4M3 or RX_FP8_E5M2.
+ * block     : 32, 64, 128, 256, 512 or 1024.
+ * codes     : nsrc device pointers, `count` bytes each (16-B aligned).
+ * scales    : nsrc device pointers, ceil(count/block) floats each.
+ * Codes and scales must not overlap the sources.
+ */
+rx_status_t rx_quant_fp8(const void* const* srcs, int nsrc, size_t count,
+                         rx_dtype_t src_dtype, rx_dtype_t fp8_dtype, int block,
+                         void* const* codes, float* const* scales,
+                         hipStream_t stream);
+
+/*
+ * Low-precision path, reducing side: dequantize nsrc FP8 inputs, sum them in
+ * FP32 (RCCLX article, "Core feature 2: Low-Precision Collectives", table row
+ * "Compute precision"), and either return the sum or requantize it for the
+ * all-gather.
+ *   v_{r,i} = fl32(decode(code_{r,i}) * s_{r,b})      (never fused with +)
+ *   S_i     = left fold of v_{0,i} .. v_{nsrc-1,i} in FP32
+ *   RX_DRR_SUM     : out_hp[i] = cast(S_i). out_hp required; out_codes and
+ *                    out_scales must be NULL.
+ *   RX_DRR_REQUANT : S is quantized per block exactly as rx_quant_fp8 does
+ *                    (same block and fp8_dtype) into out_codes/out_scales
+ *                    (both required). When out_hp is not NULL it receives
+ *                    cast(fl32(decode(out_code_i) * out_scale_b)), the value
+ *                    every rank holds after the all-gather.
+ * With nsrc == 1 and RX_DRR_SUM this is a plain dequantization.
+ *
+ * codes, scales : nsrc device pointers each (`count` bytes, ceil(count/block)
+ *                 floats).
+ * fp8_dtype     : RX_FP8_E4M3 or RX_FP8_E5M2; block as for rx_quant_fp8.
+ * hp_dtype      : RX_FP32 or RX_BF16 (checked only when out_hp != NULL).
+ * Outputs must not overlap the inputs.
+ */
+rx_status_t rx_dequant_reduce_requant(const void* const* codes,
+                                      const float* const* scales, int nsrc,
+                                      size_t count, rx_dtype_t fp8_dtype,
+                                      int block, rx_drr_mode_t mode,
+                                      void* out_codes, float* out_scales,
+                                      void* out_hp, rx_dtype_t hp_dtype,
+                                      hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* rx_status_string(rx_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RX_H */

@@ -1,0 +1,41 @@
+/*
+ * rx_testhooks.h -- test entry points of librx that expose the device
+ * conversion and cross-lane helpers the kernels are built from, so tests can
+ * sweep them exhaustively against the CPU oracle. Same conventions as rx.h:
+ * device pointers, asynchronous on `stream`, validation before any launch.
+ */
+#ifndef RX_TESTHOOKS_H
+#define RX_TESTHOOKS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include "rx.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* out[i] = OCP FP8 code of the FP32 pattern (first + i), after the kernels'
+ * pre-clamp to [-FMAX, FMAX]; n <= 2^32 - first. fmt: RX_FP8_E4M3/E5M2.
+ * NaN patterns give unspecified codes. out: n bytes. */
+rx_status_t rxtest_fp8_encode_bits(uint32_t first, size_t n, rx_dtype_t fmt,
+                                   uint8_t* out, hipStream_t stream);
+
+/* out[i] = FP32 value of code in[i] (hardware decode). */
+rx_status_t rxtest_fp8_decode(const uint8_t* in, size_t n, rx_dtype_t fmt,
+                              float* out, hipStream_t stream);
+
+/* out[i] = BF16 (round to nearest even) of the FP32 pattern (first + i). */
+rx_status_t rxtest_bf16_round_bits(uint32_t first, size_t n, uint16_t* out,
+                                   hipStream_t stream);
+
+/* For each wave of 64 values in in[0 .. 64*nwaves): out[l] = max of in over
+ * the aligned group of g lanes that holds lane l (g = 1, 2, 4, ..., 64),
+ * computed with the kernels' DPP / permlane group maximum. */
+rx_status_t rxtest_group_max(const uint32_t* in, size_t nwaves, int g,
+                             uint32_t* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RX_TESTHOOKS_H */

@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, it
+exports every function its headers declare, and argument validation returns
+the documented status before any HIP call (no kernel is launched: every
+call here fails validation or has count == 0). Device pointers are fake
+addresses that are never dereferenced on the host."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import allreduce_reduction_rx_amd as rx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, ARG, DTYPE, ALIGN = 0, 1, 2, 3, 4
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    names = set()
+    for h in os.listdir(os.path.join(ROOT, "include")):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            names |= set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(rx\w*)\s*\(", text, re.M))
+    return names
+
+
+def test_headers_declare_the_four_entry_points():
+    names = declared_functions()
+    for n in ("rx_reduce_flat", "rx_reduce_scatter_chunk_bcast", "rx_quant_fp8",
+              "rx_dequant_reduce_requant"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = rx.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) <= set(rx.EXPORTED_SYMBOLS)
+
+
+def ptrs(*vals):
+    return (ctypes.c_void_p * max(1, len(vals)))(*vals)
+
+
+def test_status_strings():
+    for s in range(6):
+        assert rx.rx_status_string(s).startswith("RX_")
+
+
+def test_reduce_flat_validation():
+    L = rx.lib()
+    f = L.rx_reduce_flat
+    src = ptrs(FAKE, FAKE + 4096)
+    assert f(None, 2, 10, rx.RX_FP32, FAKE, None) == NULL
+    assert f(src, 2, 10, rx.RX_FP32, None, None) == NULL
+    assert f(src, 0, 10, rx.RX_FP32, FAKE, None) == ARG
+    assert f(src, 17, 10, rx.RX_FP32, FAKE, None) == ARG
+    assert f(src, 2, 10, rx.RX_FP8_E4M3, FAKE, None) == DTYPE
+    assert f(src, 2, 10, 9, FAKE, None) == DTYPE
+    assert f(ptrs(FAKE, 0), 2, 10, rx.RX_FP32, FAKE, None) == NULL
+    assert f(ptrs(FAKE, FAKE + 8), 2, 10, rx.RX_FP32, FAKE, None) == ALIGN
+    assert f(src, 2, 10, rx.RX_FP32, FAKE + 4, None) == ALIGN
+    assert f(src, 2, 0, rx.RX_BF16, FAKE, None) == OK  # nothing to do, no launch
+    assert f(src, 2, (1 << 38) + 1, rx.RX_FP32, FAKE, None) == ARG
+
+
+def test_tree_validation_and_chunks():
+    L = rx.lib()
+    f = L.rx_reduce_scatter_chunk_bcast
+    src, dst = ptrs(FAKE, FAKE + 4096), ptrs(FAKE + 8192, FAKE + 12288)
+    assert f(src, 2, 10, rx.RX_FP32, 2, dst, None) == ARG
+    assert f(src, 2, 10, rx.RX_FP32, -1, dst, None) == ARG
+    assert f(src, 2, 10, rx.RX_FP32, 0, None, None) == NULL
+    assert f(src, 2, 10, rx.RX_FP32, 0, ptrs(FAKE + 8192, FAKE + 2), None) == ALIGN
+    assert f(src, 2, 0, rx.RX_FP32, 1, dst, None) == OK
+    # chunk bounds of the 4 MiB BF16 tree message, 8 ranks: 262,144 each
+    for k in range(8):
+        assert rx.rx_tree_chunk(2_097_152, 8, rx.RX_BF16, k) == (k * 262_144, (k + 1) * 262_144)
+    # ragged: 10 FP32 over 4 ranks -> chunks of 4: [0,4) [4,8) [8,10) [10,10)
+    assert [rx.rx_tree_chunk(10, 4, rx.RX_FP32, k) for k in range(4)] == [(0, 4), (4, 8), (8, 10), (10, 10)]
+    # an empty chunk launches nothing
+    assert f(src, 2, 3, rx.RX_FP32, 1, dst, None) == OK
+
+
+def test_quant_validation():
+    L = rx.lib()
+    f = L.rx_quant_fp8
+    src, codes, sc = ptrs(FAKE), ptrs(FAKE + 4096), ptrs(FAKE + 8192)
+    assert f(src, 1, 100, rx.RX_FP32, rx.RX_FP8_E4M3, 128, None, sc, None) == NULL
+    assert f(src, 1, 100, rx.RX_FP32, rx.RX_FP8_E4M3, 100, codes, sc, None) == ARG
+    assert f(src, 1, 100, rx.RX_FP32, rx.RX_FP8_E4M3, 16, codes, sc, None) == ARG
+    assert f(src, 1, 100, rx.RX_FP32, rx.RX_FP8_E4M3, 2048, codes, sc, None) == ARG
+    assert f(src, 1, 100, rx.RX_FP8_E5M2, rx.RX_FP8_E4M3, 128, codes, sc, None) == DTYPE
+    assert f(src, 1, 100, rx.RX_FP32, rx.RX_BF16, 128, codes, sc, None) == DTYPE
+    assert f(src, 1, 100, rx.RX_FP32, rx.RX_FP8_E4M3, 128, ptrs(FAKE + 1), sc, None) == ALIGN
+    assert f(src, 1, 100, rx.RX_FP32, rx.RX_FP8_E4M3, 128, codes, ptrs(FAKE + 2), None) == ALIGN
+    assert f(src, 1, 0, rx.RX_BF16, rx.RX_FP8_E5M2, 256, codes, sc, None) == OK
+
+
+def test_drr_validation():
+    L = rx.lib()
+    f = L.rx_dequant_reduce_requant
+    c, s = ptrs(FAKE, FAKE + 4096), ptrs(FAKE + 8192, FAKE + 12288)
+    E4, SUM, REQ = rx.RX_FP8_E4M3, rx.RX_DRR_SUM, rx.RX_DRR_REQUANT
+    out = FAKE + 65536
+    assert f(None, s, 2, 10, E4, 128, SUM, None, None, out, rx.RX_FP32, None) == NULL
+    assert f(c, s, 2, 10, E4, 128, 7, None, None, out, rx.RX_FP32, None) == ARG
+    assert f(c, s, 2, 10, E4, 128, SUM, None, None, None, rx.RX_FP32, None) == NULL
+    assert f(c, s, 2, 10, E4, 128, SUM, out, None, out, rx.RX_FP32, None) == ARG
+    assert f(c, s, 2, 10, E4, 128, REQ, None, out, None, rx.RX_FP32, None) == NULL
+    assert f(c, s, 2, 10, rx.RX_BF16, 128, SUM, None, None, out, rx.RX_FP32, None) == DTYPE
+    assert f(c, s, 2, 10, E4, 128, SUM, None, None, out, rx.RX_FP8_E5M2, None) == DTYPE
+    assert f(c, s, 2, 10, E4, 48, SUM, None, None, out, rx.RX_FP32, None) == ARG
+    assert f(c, s, 2, 10, E4, 128, REQ, out + 3, out, None, rx.RX_FP32, None) == ALIGN
+    assert f(c, s, 2, 10, E4, 128, REQ, out, out + 1, None, rx.RX_FP32, None) == ALIGN
+    assert f(c, s, 2, 10, E4, 128, SUM, None, None, out + 8, rx.RX_BF16, None) == ALIGN
+    assert f(c, ptrs(FAKE, FAKE + 3), 2, 10, E4, 128, SUM, None, None, out, rx.RX_FP32, None) == ALIGN
+    assert f(c, s, 2, 0, E4, 128, REQ, out, out, None, rx.RX_FP32, None) == OK
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(8)
+    with pytest.raises(ValueError):
+        rx.rx_reduce_flat([x], x)

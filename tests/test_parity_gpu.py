@@ -1,0 +1,423 @@
+"""GPU parity: every librx entry point against the CPU oracle, bit for bit
+(FP32 sums at fixed source order reach the oracle exactly, BF16 narrowing
+and FP8 codes and scales are exact), through the C ABI.
+
+Workloads (named in rxgen): the RCCLX article's rank-id example
+(code-journey.com, "Practical guide"), a decode-size flat reduce, the DDA
+tree step on 4 MiB messages, and the two >= 16 MB low-precision messages
+("Core feature 2: Low-Precision Collectives").
+"""
+import numpy as np
+import pytest
+import torch
+
+import allreduce_reduction_rx_amd as rx
+import oracle as O
+import rxgen as G
+from gpu_util import (DEV, Guarded, bits_equal, empty_like_np, first_mismatch, log,
+                      to_gpu, to_host)
+
+pytestmark = pytest.mark.gpu
+
+NP = {O.FP32: np.float32, O.BF16: np.uint16}
+TD = {O.FP32: torch.float32, O.BF16: torch.bfloat16}
+FMTS = {O.E4M3: "e4m3", O.E5M2: "e5m2"}
+
+SHAPES = [1, 2, 3, 7, 8, 9, 15, 16, 17, 127, 128, 129, 255, 256, 257, 1000, 4133, 70001]
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# DDA flat
+# ---------------------------------------------------------------------------
+
+def test_flat_rank_id_example():
+    w = G.WORKLOADS["flat_rank"]
+    log("flat_rank")
+    srcs = w.sources()
+    dst = torch.empty(w.count, dtype=torch.float32, device=DEV)
+    rx.rx_reduce_flat([to_gpu(s) for s in srcs], dst)
+    sync()
+    assert torch.all(dst == 28.0).item()
+
+
+@pytest.mark.parametrize("name", ["flat_uniform", "decode"])
+def test_flat_workloads(name):
+    w = G.WORKLOADS[name]
+    log(f"flat workload {name}")
+    srcs = w.sources()
+    g = Guarded(w.count, TD[w.dtype])
+    rx.rx_reduce_flat([to_gpu(s) for s in srcs], g.t)
+    sync()
+    ref = O.reduce_flat(srcs, w.dtype)
+    got = to_host(g.t)
+    assert bits_equal(got, ref), first_mismatch(got, ref)
+    assert g.guards_intact()
+
+
+@pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8, 13, 16])
+def test_flat_shapes(n, dtype):
+    for count in SHAPES:
+        log(f"flat n={n} dtype={dtype} count={count}")
+        srcs = [G.fill(count, dtype, G.NORMAL_OUTLIER, seed=1000 + count, rank=r) for r in range(n)]
+        g = Guarded(count, TD[dtype])
+        rx.rx_reduce_flat([to_gpu(s) for s in srcs], g.t)
+        sync()
+        ref = O.reduce_flat(srcs, dtype)
+        got = to_host(g.t)
+        assert bits_equal(got, ref), f"count={count}: " + first_mismatch(got, ref)
+        assert g.guards_intact(), f"count={count}: guard overwritten"
+
+
+@pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
+def test_flat_in_place(dtype):
+    n, count = 8, 100_003
+    srcs = [G.fill(count, dtype, G.NORMAL, seed=77, rank=r) for r in range(n)]
+    ref = O.reduce_flat(srcs, dtype)
+    for j in (0, 5, 7):
+        ts = [to_gpu(s) for s in srcs]
+        rx.rx_reduce_flat(ts, ts[j])
+        sync()
+        got = to_host(ts[j])
+        assert bits_equal(got, ref), f"alias {j}: " + first_mismatch(got, ref)
+
+
+def test_flat_order_and_accumulation():
+    # FP32 left fold in source order: ((1e8 + 1) - 1e8) == 0 but
+    # ((1e8 - 1e8) + 1) == 1; BF16 {256, 1 x 7} -> 264 needs FP32 accumulation.
+    a = np.full(64, 1e8, np.float32)
+    b = np.full(64, 1.0, np.float32)
+    c = np.full(64, -1e8, np.float32)
+    for order, want in (((a, b, c), 0.0), ((a, c, b), 1.0)):
+        dst = torch.empty(64, dtype=torch.float32, device=DEV)
+        rx.rx_reduce_flat([to_gpu(x) for x in order], dst)
+        sync()
+        assert torch.all(dst == want).item()
+    vals = [torch.full((40,), v, dtype=torch.bfloat16, device=DEV) for v in [256.0] + [1.0] * 7]
+    dst = torch.empty(40, dtype=torch.bfloat16, device=DEV)
+    rx.rx_reduce_flat(vals, dst)
+    sync()
+    assert torch.all(dst.float() == 264.0).item()
+
+
+def test_flat_deterministic():
+    w = G.WORKLOADS["decode"]
+    ts = [to_gpu(s) for s in w.sources()]
+    outs = []
+    for _ in range(3):
+        d = torch.empty(w.count, dtype=torch.bfloat16, device=DEV)
+        rx.rx_reduce_flat(ts, d)
+        outs.append(d)
+    sync()
+    assert all(torch.equal(outs[0].view(torch.int16), o.view(torch.int16)) for o in outs)
+
+
+# ---------------------------------------------------------------------------
+# DDA tree
+# ---------------------------------------------------------------------------
+
+def _tree_case(srcs, dtype, count, rank):
+    n = len(srcs)
+    gs = [Guarded(count, TD[dtype]) for _ in range(n)]   # interior holds a sentinel too
+    sentinel = [to_host(g.t).copy() for g in gs]
+    rx.rx_reduce_scatter_chunk_bcast([to_gpu(s) for s in srcs], rank, [g.t for g in gs])
+    sync()
+    ref = [s.copy() for s in sentinel]
+    O.reduce_scatter_chunk_bcast(srcs, dtype, rank, ref)
+    for j, g in enumerate(gs):
+        got = to_host(g.t)
+        assert bits_equal(got, ref[j]), f"rank={rank} dst={j}: " + first_mismatch(got, ref[j])
+        assert g.guards_intact()
+
+
+def test_tree_workload_all_ranks():
+    w = G.WORKLOADS["tree"]
+    srcs = w.sources()
+    for k in range(w.nsrc):
+        log(f"tree workload rank={k}")
+        _tree_case(srcs, w.dtype, w.count, k)
+
+
+@pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
+@pytest.mark.parametrize("n", [1, 3, 8, 16])
+def test_tree_shapes(n, dtype):
+    for count in [1, 7, 8, 9, 33, 127, 1000, 4133]:
+        srcs = [G.fill(count, dtype, G.NORMAL, seed=2000 + count, rank=r) for r in range(n)]
+        for k in range(n):
+            log(f"tree n={n} dtype={dtype} count={count} rank={k}")
+            _tree_case(srcs, dtype, count, k)
+
+
+def test_tree_in_place():
+    n, count, dtype = 8, 65536 + 24, O.BF16
+    srcs = [G.fill(count, dtype, G.NORMAL, seed=99, rank=r) for r in range(n)]
+    for k in (0, 7):
+        ts = [to_gpu(s) for s in srcs]
+        rx.rx_reduce_scatter_chunk_bcast(ts, k, ts)
+        sync()
+        ref = [s.copy() for s in srcs]
+        O.reduce_scatter_chunk_bcast(srcs, dtype, k, ref)
+        for j in range(n):
+            assert bits_equal(to_host(ts[j]), ref[j])
+
+
+# ---------------------------------------------------------------------------
+# Low-precision path
+# ---------------------------------------------------------------------------
+
+def _quant_gpu(srcs, dtype, fmt, block, count):
+    nb = -(-count // block)
+    codes = [Guarded(count, torch.uint8) for _ in srcs]
+    scales = [Guarded(nb, torch.float32) for _ in srcs]
+    rx.rx_quant_fp8([to_gpu(s) for s in srcs], FMTS[fmt], block,
+                    [c.t for c in codes], [s.t for s in scales], count=count)
+    sync()
+    for g in codes + scales:
+        assert g.guards_intact()
+    return [to_host(c.t) for c in codes], [to_host(s.t) for s in scales]
+
+
+@pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
+@pytest.mark.parametrize("fmt", [O.E4M3, O.E5M2])
+@pytest.mark.parametrize("block", [32, 64, 128, 256, 512, 1024])
+def test_quant_shapes(dtype, fmt, block):
+    n = 3
+    for count in [1, 5, 17, block - 1, block, block + 3, 4 * block + 7, 5000, 33_333]:
+        log(f"quant dtype={dtype} fmt={fmt} block={block} count={count}")
+        srcs = [G.fill(count, dtype, G.NORMAL_OUTLIER, seed=3000 + count, rank=r) for r in range(n)]
+        gc, gs = _quant_gpu(srcs, dtype, fmt, block, count)
+        rc, rs = O.quant_fp8(srcs, dtype, fmt, block)
+        for j in range(n):
+            assert bits_equal(gc[j], rc[j]), f"codes count={count} src={j}: " + first_mismatch(gc[j], rc[j])
+            assert bits_equal(gs[j], rs[j]), f"scales count={count} src={j}: " + first_mismatch(gs[j], rs[j])
+
+
+def test_quant_degenerate_blocks():
+    # zero blocks, tiny blocks (FMAX / A overflows), huge values, -0
+    count, block = 1024, 128
+    x = np.zeros(count, np.float32)
+    x[128:256] = np.float32(1e-40) * (np.arange(128) % 3 - 1)
+    x[256:384] = np.float32(3e38) * np.where(np.arange(128) % 2 == 0, 1, -1)
+    x[384:512] = -0.0
+    x[512:640] = np.float32(2.0 ** -140)
+    x[640:768] = 448.0
+    x[768:] = np.linspace(-1, 1, 256, dtype=np.float32)
+    for fmt in (O.E4M3, O.E5M2):
+        gc, gs = _quant_gpu([x], O.FP32, fmt, block, count)
+        rc, rs = O.quant_fp8([x], O.FP32, fmt, block)
+        assert bits_equal(gc[0], rc[0]), first_mismatch(gc[0], rc[0])
+        assert bits_equal(gs[0], rs[0]), first_mismatch(gs[0], rs[0])
+
+
+def _drr_gpu(codes, scales, fmt, block, mode, hp_dtype, want_hp, count):
+    nb = -(-count // block)
+    oc = os_ = hp = None
+    if mode == O.DRR_REQUANT:
+        oc = Guarded(count, torch.uint8)
+        os_ = Guarded(nb, torch.float32)
+    if mode == O.DRR_SUM or want_hp:
+        hp = Guarded(count, TD[hp_dtype])
+    rx.rx_dequant_reduce_requant([to_gpu(c) for c in codes], [to_gpu(s) for s in scales],
+                                 FMTS[fmt], block, mode,
+                                 None if oc is None else oc.t, None if os_ is None else os_.t,
+                                 None if hp is None else hp.t, count=count)
+    sync()
+    out = []
+    for g in (oc, os_, hp):
+        if g is None:
+            out.append(None)
+        else:
+            assert g.guards_intact()
+            out.append(to_host(g.t))
+    return out
+
+
+@pytest.mark.parametrize("fmt", [O.E4M3, O.E5M2])
+@pytest.mark.parametrize("block", [32, 128, 256, 1024])
+@pytest.mark.parametrize("n", [1, 2, 8, 16])
+def test_drr_shapes(fmt, block, n):
+    for count in [1, 15, 16, 17, block + 5, 3 * block, 5000, 40_001]:
+        srcs = [G.fill(count, O.FP32, G.LAPLACE, seed=4000 + count, rank=r) for r in range(n)]
+        codes, scales = O.quant_fp8(srcs, O.FP32, fmt, block)
+        for mode, hp_dtype, want_hp in ((O.DRR_SUM, O.FP32, True), (O.DRR_SUM, O.BF16, True),
+                                        (O.DRR_REQUANT, O.FP32, False),
+                                        (O.DRR_REQUANT, O.FP32, True),
+                                        (O.DRR_REQUANT, O.BF16, True)):
+            log(f"drr fmt={fmt} block={block} n={n} count={count} mode={mode} hp={hp_dtype}/{want_hp}")
+            got = _drr_gpu(codes, scales, fmt, block, mode, hp_dtype, want_hp, count)
+            ref = O.dequant_reduce_requant(codes, scales, fmt, block, mode, hp_dtype, want_hp)
+            for name, g, r in zip(("codes", "scales", "hp"), got, ref):
+                assert (g is None) == (r is None)
+                if g is not None:
+                    assert bits_equal(g, r), f"{name} count={count}: " + first_mismatch(g, r)
+
+
+def test_lp_fp32_workload_full():
+    """Low-precision allreduce on 8 x 16,777,216 FP32 (N(0,1), 1% outliers
+    x100), E4M3, blocks of 128: quant and DRR-REQUANT (+FP32 output)
+    compared in full."""
+    w = G.WORKLOADS["lp_fp32"]
+    fmt, block = O.FMT[w.fp8], w.block
+    log("lp_fp32 generate")
+    srcs = w.sources()
+    log("lp_fp32 gpu")
+    gc, gs = _quant_gpu(srcs, w.dtype, fmt, block, w.count)
+    log("lp_fp32 oracle quant")
+    rc, rs = O.quant_fp8(srcs, w.dtype, fmt, block)
+    for j in range(w.nsrc):
+        assert bits_equal(gc[j], rc[j]), f"codes src={j}: " + first_mismatch(gc[j], rc[j])
+        assert bits_equal(gs[j], rs[j]), f"scales src={j}: " + first_mismatch(gs[j], rs[j])
+    del gc, gs
+    log("lp_fp32 drr")
+    oc, osc, hp = _drr_gpu(rc, rs, fmt, block, O.DRR_REQUANT, O.FP32, True, w.count)
+    r_oc, r_os, r_hp = O.dequant_reduce_requant(rc, rs, fmt, block, O.DRR_REQUANT, O.FP32, True)
+    assert bits_equal(oc, r_oc), first_mismatch(oc, r_oc)
+    assert bits_equal(osc, r_os), first_mismatch(osc, r_os)
+    assert bits_equal(hp, r_hp), first_mismatch(hp, r_hp)
+    # end-to-end error against the unquantized FP32 sum: N * 2^-4 * blockabsmax
+    T = O.reduce_flat(srcs, O.FP32).astype(np.float64)
+    X_absmax = np.zeros(w.count // block)
+    for s in srcs:
+        X_absmax = np.maximum(X_absmax, np.abs(s.astype(np.float64)).reshape(-1, block).max(axis=1))
+    bound = w.nsrc * 2.0 ** -4 * np.repeat(X_absmax, block)
+    err = np.abs(hp.astype(np.float64) - T)
+    log(f"lp_fp32 max err/bound = {np.max(err / bound):.4f}")
+    assert np.all(err <= bound)
+
+
+def test_lp_bf16_workload_sampled():
+    """Low-precision large message: 8 x 268,435,456 BF16 (Laplace(0,1)),
+    E5M2, blocks of 256, in the launch configuration the benchmark times;
+    quant, fused DRR-REQUANT with BF16 output and the separate N=1 dequant,
+    compared with the oracle on 4096 sampled blocks."""
+    w = G.WORKLOADS["lp_bf16"]
+    fmt, block, n, count = O.FMT[w.fp8], w.block, w.nsrc, w.count
+    nb = count // block
+    rng = np.random.default_rng(505)
+    sample = np.unique(np.concatenate([[0, nb - 1], rng.integers(0, nb, 4094)]))
+    log("lp_bf16 generate + upload")
+    ts = []
+    for r in range(n):
+        ts.append(to_gpu(w.source(r)))
+    codes = [torch.empty(count, dtype=torch.uint8, device=DEV) for _ in range(n)]
+    scales = [torch.empty(nb, dtype=torch.float32, device=DEV) for _ in range(n)]
+    log("lp_bf16 quant")
+    rx.rx_quant_fp8(ts, w.fp8, block, codes, scales)
+    oc = torch.empty(count, dtype=torch.uint8, device=DEV)
+    osc = torch.empty(nb, dtype=torch.float32, device=DEV)
+    hp = torch.empty(count, dtype=torch.bfloat16, device=DEV)
+    log("lp_bf16 drr")
+    rx.rx_dequant_reduce_requant(codes, scales, w.fp8, block, rx.RX_DRR_REQUANT, oc, osc, hp)
+    hp2 = torch.empty(count, dtype=torch.bfloat16, device=DEV)
+    rx.rx_dequant_reduce_requant([oc], [osc], w.fp8, block, rx.RX_DRR_SUM, out_hp=hp2)
+    sync()
+    idx = torch.from_numpy((sample[:, None] * block + np.arange(block)[None, :]).ravel()).to(DEV)
+    sidx = torch.from_numpy(sample).to(DEV)
+    g_src = [to_host(t[idx]) for t in ts]
+    g_codes = [codes[r][idx].cpu().numpy() for r in range(n)]
+    g_scales = [scales[r][sidx].cpu().numpy() for r in range(n)]
+    g_oc, g_os = oc[idx].cpu().numpy(), osc[sidx].cpu().numpy()
+    g_hp, g_hp2 = to_host(hp[idx]), to_host(hp2[idx])
+    del ts, codes, scales, oc, osc, hp, hp2
+    torch.cuda.empty_cache()
+    log("lp_bf16 oracle on sampled blocks")
+    # the sampled blocks are independent: the oracle runs on them as one
+    # message of len(sample) blocks
+    rc, rs = O.quant_fp8(g_src, O.BF16, fmt, block)
+    for r in range(n):
+        assert bits_equal(g_codes[r], rc[r]), first_mismatch(g_codes[r], rc[r])
+        assert bits_equal(g_scales[r], rs[r]), first_mismatch(g_scales[r], rs[r])
+    r_oc, r_os, r_hp = O.dequant_reduce_requant(rc, rs, fmt, block, O.DRR_REQUANT, O.BF16, True)
+    assert bits_equal(g_oc, r_oc) and bits_equal(g_os, r_os)
+    assert bits_equal(g_hp, r_hp), first_mismatch(g_hp, r_hp)
+    assert bits_equal(g_hp2, r_hp), first_mismatch(g_hp2, r_hp)
+
+
+# ---------------------------------------------------------------------------
+# Hardware converters and the cross-lane maximum, swept exhaustively
+# ---------------------------------------------------------------------------
+
+CHUNK = 1 << 28
+
+
+def _oracle_encode_parallel(first, n, fmt, threads=16):
+    from concurrent.futures import ThreadPoolExecutor
+    out = np.empty(n, np.uint8)
+    per = -(-n // threads)
+
+    def job(t):
+        lo = t * per
+        hi = min(n, lo + per)
+        if lo < hi:
+            out[lo:hi] = O.fp8_encode_bits(first + lo, hi - lo, fmt)
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(job, range(threads)))
+    return out
+
+
+@pytest.mark.parametrize("fmt", [O.E4M3, O.E5M2])
+def test_fp8_encode_exhaustive(fmt):
+    """All 2^32 FP32 patterns (NaNs excluded) through the kernels' clamp +
+    hardware encode, against the oracle's encode."""
+    out = torch.empty(CHUNK, dtype=torch.uint8, device=DEV)
+    for first in range(0, 1 << 32, CHUNK):
+        log(f"fp8 encode sweep fmt={fmt} first={first:#x}")
+        rx.rxtest_fp8_encode_bits(first, CHUNK, FMTS[fmt], out)
+        sync()
+        got = out.cpu().numpy()
+        ref = _oracle_encode_parallel(first, CHUNK, fmt)
+        u = np.arange(CHUNK, dtype=np.uint32) + np.uint32(first)
+        notnan = (u & 0x7FFFFFFF) <= 0x7F800000
+        bad = np.nonzero((got != ref) & notnan)[0]
+        assert bad.size == 0, f"{bad.size} mismatches, first pattern {first + bad[0]:#010x}: got {got[bad[0]]:#x} want {ref[bad[0]]:#x}"
+
+
+@pytest.mark.parametrize("fmt", [O.E4M3, O.E5M2])
+def test_fp8_decode_all_codes(fmt):
+    codes = torch.arange(256, dtype=torch.int32, device=DEV).to(torch.uint8)
+    out = torch.empty(256, dtype=torch.float32, device=DEV)
+    rx.rxtest_fp8_decode(codes, FMTS[fmt], out)
+    sync()
+    got = out.cpu().numpy()
+    ref = O.fp8_decode(np.arange(256, dtype=np.uint8), fmt)
+    ok = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(got), ~ok)
+    assert bits_equal(got[ok], ref[ok])
+
+
+def test_bf16_round_exhaustive():
+    from concurrent.futures import ThreadPoolExecutor
+    out = torch.empty(CHUNK, dtype=torch.bfloat16, device=DEV)
+    for first in range(0, 1 << 32, CHUNK):
+        log(f"bf16 sweep first={first:#x}")
+        rx.rxtest_bf16_round_bits(first, CHUNK, out)
+        sync()
+        got = to_host(out)
+        x = (np.arange(CHUNK, dtype=np.uint32) + np.uint32(first)).view(np.float32)
+        ref = np.empty(CHUNK, np.uint16)
+        per = CHUNK // 16
+
+        def job(t):
+            ref[t * per:(t + 1) * per] = O.f32_to_bf16(x[t * per:(t + 1) * per])
+        with ThreadPoolExecutor(16) as ex:
+            list(ex.map(job, range(16)))
+        notnan = ~np.isnan(x)
+        bad = np.nonzero((got != ref) & notnan)[0]
+        assert bad.size == 0, f"{bad.size} mismatches, first pattern {first + bad[0]:#010x}"
+
+
+def test_group_max_lane_layout():
+    rng = np.random.default_rng(17)
+    vals = rng.integers(0, 2 ** 31, size=64 * 64, dtype=np.uint32)
+    t = torch.from_numpy(vals.view(np.int32)).to(DEV)
+    out = torch.empty_like(t)
+    for g in (1, 2, 4, 8, 16, 32, 64):
+        rx.rxtest_group_max(t, g, out)
+        sync()
+        got = out.cpu().numpy().view(np.uint32)
+        ref = np.repeat(vals.reshape(-1, g).max(axis=1), g)
+        assert np.array_equal(got, ref), f"g={g}"
