@@ -268,6 +268,8 @@ def main():
     traffic = read_traffic(dominant, args.workload)
     value = step_bytes / (step_ms * 1e-3) / 1e9
 
+    copy = copy_ceiling(torch, stream)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, host, lp_fmt, lp_block, args.cpu_seconds, step_bytes)
@@ -306,11 +308,36 @@ def main():
         "kernels": per_kernel,
         "us_reduce_flat": per_kernel["reduce_flat"]["us"],
         "tree_matches_flat": bool(tree_ok),
+        "copy_ceiling": copy,
         "wall_s": round(wall_s, 4),
         "launch": "python loop" if args.no_graph else "HIP graph replay",
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def copy_ceiling(torch, stream):
+    """A plain device-to-device copy of 1 GiB (4x the Infinity Cache), the
+    practical streaming ceiling on this GPU: (read + write bytes) / time."""
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    reps = 20
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    z.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(z) * 1000.0 / reps
+    gbs = 2 * nbytes / (us * 1e-6) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "bytes": 2 * nbytes, "us": round(us, 1)}
 
 
 def cpu_baseline(w, host, lp_fmt, lp_block, seconds, step_bytes):
