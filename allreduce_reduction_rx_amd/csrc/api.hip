@@ -30,6 +30,20 @@ int device_cu_count()
     return cus;
 }
 
+void launch_geometry(size_t threads, const LaunchPolicy& p, dim3& grid, dim3& block)
+{
+    const size_t cus = (size_t)device_cu_count();
+    if (threads == 0)
+        threads = 1;
+    const bool small = threads < cus * p.small_per_cu;
+    const unsigned wg = small ? p.wg_small : p.wg_large;
+    size_t blocks = (threads + wg - 1) / wg;
+    if (!small && blocks > cus * p.max_wgs_per_cu)
+        blocks = cus * p.max_wgs_per_cu;
+    grid = dim3((unsigned)blocks);
+    block = dim3(wg);
+}
+
 }  // namespace rx
 
 namespace {

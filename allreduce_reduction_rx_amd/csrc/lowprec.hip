@@ -26,18 +26,28 @@ namespace {
 // Quantizer
 // ---------------------------------------------------------------------------
 
-template <int DT, int F, int BLOCK>
+// A wave processes tiles of U loads per lane (U x 1 KiB per tile): U = 4 for
+// large messages (more bytes in flight per wave), U = the loads per block
+// (usually 1) for decode-size messages (4x the waves, shorter serial chains).
+template <int DT, int F, int BLOCK, int U>
 struct QuantShape {
     static constexpr int kVE = DT == 0 ? 4 : 8;          // elements per 16-B vector
     static constexpr int kLanesRaw = BLOCK / kVE;        // vectors per block
     static constexpr int kLPB = kLanesRaw < 64 ? kLanesRaw : 64;  // lanes per block
     static constexpr int kUPB = kLanesRaw / kLPB;        // loads per block (1, 2, 4)
-    static constexpr int kU = 4;                         // loads per lane per tile
+    static constexpr int kU = U;                         // loads per lane per tile
     static constexpr int kTileVec = kWave * kU;
-    static constexpr int kTileElems = kTileVec * kVE;    // 1024 (FP32) / 2048 (BF16)
+    static constexpr int kTileElems = kTileVec * kVE;
     static_assert(kU % kUPB == 0, "a tile holds whole blocks");
     static_assert(kLanesRaw >= 1, "block of at least one vector");
 };
+
+template <int DT, int BLOCK>
+constexpr int loads_per_block()
+{
+    constexpr int lanes = BLOCK / (DT == 0 ? 4 : 8);
+    return lanes <= 64 ? 1 : lanes / 64;
+}
 
 // Widen vector x (16 bytes) to kVE floats.
 template <int DT>
@@ -75,10 +85,10 @@ __device__ __forceinline__ u32x4 load_partial(const void* src, size_t e, size_t 
     return x;
 }
 
-template <int DT, int F, int BLOCK>
+template <int DT, int F, int BLOCK, int UL>
 __global__ __launch_bounds__(256) void k_quant(QuantArgs a)
 {
-    using Sh = QuantShape<DT, F, BLOCK>;
+    using Sh = QuantShape<DT, F, BLOCK, UL>;
     constexpr int VE = Sh::kVE, U = Sh::kU, LPB = Sh::kLPB, UPB = Sh::kUPB;
     const int lane = lane_id();
     const uint32_t wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -191,55 +201,100 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a)
 // Dequantize -> FP32 sum -> (requantize)
 // ---------------------------------------------------------------------------
 
-// Partial 16-code vector: codes [e, count) byte by byte, the rest code 0.
-__device__ __forceinline__ u32x4 load_codes_partial(const uint8_t* p, size_t e, size_t count)
+// Each lane owns CPL consecutive codes per rank: CPL = 16 (one dwordx4 per
+// rank) for large messages, CPL = 4 (one dword) for decode-size messages,
+// which gives 4x the waves and a quarter of the per-wave ALU chain.
+template <int CPL>
+struct Codes {
+    uint32_t w[CPL / 4];
+};
+
+template <int CPL>
+__device__ __forceinline__ Codes<CPL> load_codes(const uint8_t* p, size_t v, size_t e,
+                                                 size_t count, bool whole)
 {
-    u32x4 x = {0u, 0u, 0u, 0u};
+    Codes<CPL> c;
+    if (whole) {
+        if constexpr (CPL == 16) {
+            u32x4 x = ld16_stream(p, v);
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
-        if (e + k < count) x[k / 4] |= (uint32_t)p[e + k] << (8 * (k & 3));
-    return x;
+            for (int q = 0; q < 4; ++q) c.w[q] = x[q];
+        } else {
+            c.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p) + v);
+        }
+    } else {  // codes [e, count) byte by byte, the rest code 0 (decodes to +0)
+#pragma unroll
+        for (int q = 0; q < CPL / 4; ++q) c.w[q] = 0u;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k)
+            if (e + k < count) c.w[k / 4] |= (uint32_t)p[e + k] << (8 * (k & 3));
+    }
+    return c;
 }
 
-template <int F>
-__device__ __forceinline__ void dequant16(const u32x4& c, float sc, float* v)
+template <int F, int CPL>
+__device__ __forceinline__ void dequant(const uint32_t* w, float sc, float* v)
 {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < CPL / 4; ++q) {
         float d[4];
-        fp8x4_to_f32<F>(c[q], d);
+        fp8x4_to_f32<F>(w[q], d);
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             v[4 * q + k] = d[k] * sc;
     }
 }
 
-// Store 16 high-precision values of vector v (elements 16 v .. 16 v + 15).
-__device__ __forceinline__ void store_hp16(void* out, bool bf16, size_t v, size_t count,
-                                           const float* h)
+template <int CPL>
+__device__ __forceinline__ void store_codes(uint8_t* p, size_t v, size_t e, size_t count,
+                                            bool whole, const uint32_t* w)
 {
-    const size_t e = v * 16;
-    if (e + 16 <= count) {
+    if (whole) {
+        if constexpr (CPL == 16) {
+            u32x4 x = {w[0], w[1], w[2], w[3]};
+            st16(p, v, x);
+        } else {
+            reinterpret_cast<uint32_t*>(p)[v] = w[0];
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k)
+            if (e + k < count) p[e + k] = (uint8_t)(w[k / 4] >> (8 * (k & 3)));
+    }
+}
+
+// High-precision values of elements e .. e + CPL - 1 (lane vector v).
+template <int CPL>
+__device__ __forceinline__ void store_hp(void* out, bool bf16, size_t v, size_t e, size_t count,
+                                         bool whole, const float* h)
+{
+    if (whole) {
         if (bf16) {
-            u32x4 p0 = {pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]),
-                        pack_bf16(h[4], h[5]), pack_bf16(h[6], h[7])};
-            u32x4 p1 = {pack_bf16(h[8], h[9]), pack_bf16(h[10], h[11]),
-                        pack_bf16(h[12], h[13]), pack_bf16(h[14], h[15])};
-            st16(out, 2 * v, p0);
-            st16(out, 2 * v + 1, p1);
+            uint32_t p[CPL / 2];
+#pragma unroll
+            for (int i = 0; i < CPL / 2; ++i) p[i] = pack_bf16(h[2 * i], h[2 * i + 1]);
+            if constexpr (CPL == 16) {
+                u32x4 p0 = {p[0], p[1], p[2], p[3]};
+                u32x4 p1 = {p[4], p[5], p[6], p[7]};
+                st16(out, 2 * v, p0);
+                st16(out, 2 * v + 1, p1);
+            } else {
+                u32x2 p0 = {p[0], p[1]};
+                reinterpret_cast<u32x2*>(out)[v] = p0;
+            }
         } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                u32x4 p = {__builtin_bit_cast(uint32_t, h[4 * q]),
+            for (int q = 0; q < CPL / 4; ++q) {
+                u32x4 x = {__builtin_bit_cast(uint32_t, h[4 * q]),
                            __builtin_bit_cast(uint32_t, h[4 * q + 1]),
                            __builtin_bit_cast(uint32_t, h[4 * q + 2]),
                            __builtin_bit_cast(uint32_t, h[4 * q + 3])};
-                st16(out, 4 * v + q, p);
+                st16(out, (CPL / 4) * v + q, x);
             }
         }
     } else {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < CPL; ++k) {
             if (e + k < count) {
                 if (bf16)
                     static_cast<uint16_t*>(out)[e + k] = (uint16_t)(pack_bf16(h[k], 0.0f) & 0xFFFFu);
@@ -250,7 +305,7 @@ __device__ __forceinline__ void store_hp16(void* out, bool bf16, size_t v, size_
     }
 }
 
-template <int F, int N, bool REQUANT>
+template <int F, int N, bool REQUANT, int CPL>
 __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
 {
     const int lane = lane_id();
@@ -259,73 +314,63 @@ __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
     const uint32_t wave = blockIdx.x * waves_per_wg + wave_in_wg;
     const uint32_t nwaves = gridDim.x * waves_per_wg;
     const size_t count = a.count;
-    const uint32_t ntiles = (uint32_t)((count + 1023) / 1024);  // 64 lanes x 16 codes
-    const int lpb = a.block / 16;                                 // lanes per block: 2..64
+    constexpr size_t kTile = (size_t)kWave * CPL;                 // codes per wave tile
+    const uint32_t ntiles = (uint32_t)((count + kTile - 1) / kTile);
+    const int lpb = a.block / CPL;                                // lanes per block: 2..64
     const int bshift = __builtin_ctz((unsigned)a.block);
 
     for (uint32_t t = wave; t < ntiles; t += nwaves) {
-        const size_t v = (size_t)t * kWave + lane;   // this lane's 16-code vector
-        const size_t e = v * 16;
-        const bool full = ((size_t)t + 1) * 1024 <= count;
-        const size_t b = e >> bshift;
+        const size_t v = (size_t)t * kWave + lane;   // this lane's CPL-code vector
+        const size_t e = v * CPL;
+        const bool whole = e + CPL <= count;
         const bool valid = e < count;
+        const size_t b = e >> bshift;
 
-        u32x4 c[N];
+        Codes<CPL> c[N];
         float sc[N];
 #pragma unroll
         for (int r = 0; r < N; ++r) {
-            const uint8_t* cp = static_cast<const uint8_t*>(a.codes[r]);
-            if (full || e + 16 <= count)
-                c[r] = ld16_stream(cp, v);
-            else
-                c[r] = load_codes_partial(cp, e, count);
+            c[r] = load_codes<CPL>(static_cast<const uint8_t*>(a.codes[r]), v, e, count, whole);
             sc[r] = valid ? a.scales[r][b] : 0.0f;
         }
 
-        float S[16];
-        dequant16<F>(c[0], sc[0], S);
+        float S[CPL];
+        dequant<F, CPL>(c[0].w, sc[0], S);
 #pragma unroll
         for (int r = 1; r < N; ++r) {
-            float d[16];
-            dequant16<F>(c[r], sc[r], d);
+            float d[CPL];
+            dequant<F, CPL>(c[r].w, sc[r], d);
 #pragma unroll
-            for (int k = 0; k < 16; ++k)
+            for (int k = 0; k < CPL; ++k)
                 S[k] = S[k] + d[k];
         }
 
         if constexpr (!REQUANT) {
-            store_hp16(a.out_hp, a.hp_bf16 != 0, v, count, S);
+            store_hp<CPL>(a.out_hp, a.hp_bf16 != 0, v, e, count, whole, S);
             continue;
         }
 
         // Requantize the FP32 sum with the same block size and format.
         float m = __builtin_fabsf(S[0]);
 #pragma unroll
-        for (int k = 1; k < 16; ++k)
+        for (int k = 1; k < CPL; ++k)
             m = __builtin_fmaxf(m, __builtin_fabsf(S[k]));
         const float A = bits_f32(group_max_rt(__builtin_bit_cast(uint32_t, m), lpb));
         float s2, r2;
         block_scale<F>(A, s2, r2);
-        u32x4 q;
+        uint32_t q[CPL / 4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
+        for (int p = 0; p < CPL / 4; ++p)
             q[p] = f32x4_to_fp8<F>(clamp_fmax<F>(S[4 * p + 0] * r2), clamp_fmax<F>(S[4 * p + 1] * r2),
                                    clamp_fmax<F>(S[4 * p + 2] * r2), clamp_fmax<F>(S[4 * p + 3] * r2));
-        uint8_t* oc = static_cast<uint8_t*>(a.out_codes);
-        if (full || e + 16 <= count) {
-            st16(oc, v, q);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 16; ++k)
-                if (e + k < count) oc[e + k] = (uint8_t)(q[k / 4] >> (8 * (k & 3)));
-        }
+        store_codes<CPL>(static_cast<uint8_t*>(a.out_codes), v, e, count, whole, q);
         if (valid && (lane % lpb) == 0)
             a.out_scales[b] = s2;
 
         if (a.out_hp) {
-            float h[16];
-            dequant16<F>(q, s2, h);
-            store_hp16(a.out_hp, a.hp_bf16 != 0, v, count, h);
+            float h[CPL];
+            dequant<F, CPL>(q, s2, h);
+            store_hp<CPL>(a.out_hp, a.hp_bf16 != 0, v, e, count, whole, h);
         }
     }
 }
@@ -337,68 +382,87 @@ __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
 using QuantFn = void (*)(QuantArgs);
 using DrrFn = void (*)(DrrArgs);
 
-template <int DT, int F, int... L>
+template <int DT, int F, bool SMALL, int... L>
 constexpr std::array<QuantFn, sizeof...(L)> quant_row(std::integer_sequence<int, L...>)
 {
-    return {{&k_quant<DT, F, (32 << L)>...}};
+    return {{&k_quant<DT, F, (32 << L), SMALL ? loads_per_block<DT, (32 << L)>() : 4>...}};
 }
 
-// [src dtype][fmt][log2(block) - 5]
-const std::array<QuantFn, 6> kQuant[2][2] = {
-    {quant_row<0, 0>(std::make_integer_sequence<int, 6>{}), quant_row<0, 1>(std::make_integer_sequence<int, 6>{})},
-    {quant_row<1, 0>(std::make_integer_sequence<int, 6>{}), quant_row<1, 1>(std::make_integer_sequence<int, 6>{})}};
+template <bool SMALL>
+struct QuantTable {
+    // [src dtype][fmt][log2(block) - 5]
+    std::array<QuantFn, 6> fn[2][2] = {
+        {quant_row<0, 0, SMALL>(std::make_integer_sequence<int, 6>{}),
+         quant_row<0, 1, SMALL>(std::make_integer_sequence<int, 6>{})},
+        {quant_row<1, 0, SMALL>(std::make_integer_sequence<int, 6>{}),
+         quant_row<1, 1, SMALL>(std::make_integer_sequence<int, 6>{})}};
+};
+const QuantTable<false> kQuantLarge;
+const QuantTable<true> kQuantSmall;
 
-template <int F, bool R, int... I>
+template <int F, bool R, int CPL, int... I>
 constexpr std::array<DrrFn, sizeof...(I)> drr_row(std::integer_sequence<int, I...>)
 {
-    return {{&k_drr<F, I + 1, R>...}};
+    return {{&k_drr<F, I + 1, R, CPL>...}};
 }
 
-// [fmt][requant][nsrc - 1]
-const std::array<DrrFn, kMaxSrc> kDrr[2][2] = {
-    {drr_row<0, false>(std::make_integer_sequence<int, kMaxSrc>{}),
-     drr_row<0, true>(std::make_integer_sequence<int, kMaxSrc>{})},
-    {drr_row<1, false>(std::make_integer_sequence<int, kMaxSrc>{}),
-     drr_row<1, true>(std::make_integer_sequence<int, kMaxSrc>{})}};
+template <int CPL>
+struct DrrTable {
+    // [fmt][requant][nsrc - 1]
+    std::array<DrrFn, kMaxSrc> fn[2][2] = {
+        {drr_row<0, false, CPL>(std::make_integer_sequence<int, kMaxSrc>{}),
+         drr_row<0, true, CPL>(std::make_integer_sequence<int, kMaxSrc>{})},
+        {drr_row<1, false, CPL>(std::make_integer_sequence<int, kMaxSrc>{}),
+         drr_row<1, true, CPL>(std::make_integer_sequence<int, kMaxSrc>{})}};
+};
+const DrrTable<16> kDrr16;
+const DrrTable<4> kDrr4;
 
-// One wave per tile; small jobs use 64-thread workgroups so that the tiles
-// spread over every CU, large ones 256 threads and at most 8 workgroups per
-// CU with a grid-stride loop.
-void wave_geometry(size_t tiles, dim3& grid, dim3& block)
-{
-    const size_t cus = (size_t)device_cu_count();
-    if (tiles == 0) tiles = 1;
-    unsigned wg = tiles < cus * 4 * 2 ? 64u : 256u;
-    size_t waves_per_wg = wg / kWave;
-    size_t blocks = (tiles + waves_per_wg - 1) / waves_per_wg;
-    size_t cap = cus * (2048 / wg);
-    if (blocks > cap) blocks = cap;
-    grid = dim3((unsigned)blocks);
-    block = dim3(wg);
-}
+// One wave per tile (64 threads per work item). Large messages: 256-thread
+// workgroups, at most 3 per CU (a narrow HBM access window measured best on
+// MI355X); decode-size messages: 64-thread workgroups over every CU.
+LaunchPolicy policy_quant() { return {64u, 256u, 512u, 3u}; }
+LaunchPolicy policy_drr() { return {64u, 256u, 512u, 3u}; }
+
+// Below this many large-variant wave tiles per CU a message counts as
+// decode-size and takes the narrow variant.
+constexpr size_t kSmallTilesPerCu = 8;
 
 }  // namespace
 
 hipError_t launch_quant(const QuantArgs& a, int src_dtype, int fmt, int block, hipStream_t s)
 {
     const int lb = __builtin_ctz((unsigned)block) - 5;
-    const size_t tile_elems = src_dtype == 0 ? 1024 : 2048;
+    const size_t vec_elems = src_dtype == 0 ? 4 : 8;
+    const size_t cus = (size_t)device_cu_count();
+    const size_t large_tiles = (a.count + 4 * 64 * vec_elems - 1) / (4 * 64 * vec_elems) * (size_t)a.nsrc;
+    const bool small = large_tiles < kSmallTilesPerCu * cus;
+    // loads per tile of the chosen variant
+    size_t lanes_per_block = (size_t)block / vec_elems;
+    size_t u = small ? (lanes_per_block <= 64 ? 1 : lanes_per_block / 64) : 4;
+    const size_t tile_elems = u * 64 * vec_elems;
     const size_t tiles = (a.count + tile_elems - 1) / tile_elems * (size_t)a.nsrc;
     dim3 grid, blk;
-    wave_geometry(tiles, grid, blk);
+    launch_geometry(tiles * kWave, policy_quant(), grid, blk);
     QuantArgs arg = a;
     void* params[] = {&arg};
-    return hipLaunchKernel((const void*)kQuant[src_dtype][fmt][lb], grid, blk, params, 0, s);
+    QuantFn fn = small ? kQuantSmall.fn[src_dtype][fmt][lb] : kQuantLarge.fn[src_dtype][fmt][lb];
+    return hipLaunchKernel((const void*)fn, grid, blk, params, 0, s);
 }
 
 hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStream_t s)
 {
-    const size_t tiles = (a.count + 1023) / 1024;
+    const size_t cus = (size_t)device_cu_count();
+    const bool small = a.block <= 256 && (a.count + 1023) / 1024 < kSmallTilesPerCu * cus / 2;
+    const size_t tile = small ? 256 : 1024;
+    const size_t tiles = (a.count + tile - 1) / tile;
     dim3 grid, blk;
-    wave_geometry(tiles, grid, blk);
+    launch_geometry(tiles * kWave, policy_drr(), grid, blk);
     DrrArgs arg = a;
     void* params[] = {&arg};
-    return hipLaunchKernel((const void*)kDrr[fmt][requant ? 1 : 0][nsrc - 1], grid, blk, params, 0, s);
+    const int r = requant ? 1 : 0;
+    DrrFn fn = small ? kDrr4.fn[fmt][r][nsrc - 1] : kDrr16.fn[fmt][r][nsrc - 1];
+    return hipLaunchKernel((const void*)fn, grid, blk, params, 0, s);
 }
 
 }  // namespace rx

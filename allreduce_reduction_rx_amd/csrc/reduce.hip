@@ -7,9 +7,9 @@
 // and pushes it to every destination. Sums are FP32 ("Core feature 2", table
 // row "Compute precision"), folded in source order 0..N-1.
 //
-// Both kernels are HBM-bound streams: one 16-byte load per source per lane
-// (all N issued before the first add), FP32 adds, one 16-byte store per
-// destination. N is a template parameter so the source loop unrolls and the
+// Both kernels are HBM-bound streams: one 16-byte nontemporal load per
+// source per lane (all N issued before the first add), FP32 adds, one
+// 16-byte store per destination. N is a template parameter so the source loop unrolls and the
 // pointer table is read with scalar loads from the kernarg segment.
 #include <array>
 #include <utility>
@@ -31,7 +31,7 @@ __device__ __forceinline__ u32x4 fold_vec(const void* const* src, size_t v)
     u32x4 x[N];
 #pragma unroll
     for (int r = 0; r < N; ++r)
-        x[r] = ld16(src[r], v);
+        x[r] = ld16_stream(src[r], v);   // read once: do not keep in the caches
     u32x4 out;
     if constexpr (DT == 0) {
 #pragma unroll
@@ -145,20 +145,12 @@ const std::array<TreeFn, kMaxSrc> kTree[2] = {
     tree_table<0>(std::make_integer_sequence<int, kMaxSrc>{}),
     tree_table<1>(std::make_integer_sequence<int, kMaxSrc>{})};
 
-// Threads = one per 16-byte output vector. Small messages (decode sizes) use
-// 64-thread workgroups so the vectors spread over every CU; large ones use
-// 256 threads and a grid of at most 8 workgroups per CU, looping.
-void geometry(size_t nvec, dim3& grid, dim3& block)
-{
-    const size_t cus = (size_t)device_cu_count();
-    size_t threads = nvec ? nvec : 1;
-    unsigned wg = threads < cus * 256 * 2 ? 64u : 256u;
-    size_t blocks = (threads + wg - 1) / wg;
-    size_t cap = cus * (2048 / wg);
-    if (blocks > cap) blocks = cap;
-    grid = dim3((unsigned)blocks);
-    block = dim3(wg);
-}
+// One thread per 16-byte output vector. Large messages run one 256-thread
+// workgroup per CU (flat) or two 128-thread ones (tree) with a grid-stride
+// loop: on MI355X a narrow window of in-flight addresses measured up to 20%
+// faster than filling every CU with 8 workgroups.
+LaunchPolicy policy_flat() { return {128u, 256u, 512u, 1u}; }
+LaunchPolicy policy_tree() { return {64u, 128u, 512u, 2u}; }
 
 }  // namespace
 
@@ -166,7 +158,7 @@ hipError_t launch_reduce_flat(const FlatArgs& a, int nsrc, int dtype, hipStream_
 {
     const int ve = dtype == 0 ? 4 : 8;
     dim3 grid, block;
-    geometry(a.count / ve, grid, block);
+    launch_geometry(a.count / ve, policy_flat(), grid, block);
     FlatArgs arg = a;
     void* params[] = {&arg};
     return hipLaunchKernel((const void*)kFlat[dtype][nsrc - 1], grid, block, params, 0, s);
@@ -176,7 +168,7 @@ hipError_t launch_tree(const TreeArgs& a, int nsrc, int dtype, hipStream_t s)
 {
     const int ve = dtype == 0 ? 4 : 8;
     dim3 grid, block;
-    geometry((a.hi - a.lo) / ve, grid, block);
+    launch_geometry((a.hi - a.lo) / ve, policy_tree(), grid, block);
     TreeArgs arg = a;
     void* params[] = {&arg};
     return hipLaunchKernel((const void*)kTree[dtype][nsrc - 1], grid, block, params, 0, s);

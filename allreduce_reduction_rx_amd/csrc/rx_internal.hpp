@@ -47,6 +47,21 @@ struct DrrArgs {
 // (cached per device on first use).
 int device_cu_count();
 
+// How a kernel spreads `threads` work items (one per 16-byte vector, or 64
+// per wave tile) over the GPU. Jobs with fewer than `small_per_cu` threads
+// per CU use `wg_small`-thread workgroups, one work item per thread, so that
+// a decode-size message still reaches every CU; larger jobs use `wg_large`
+// threads and at most `max_wgs_per_cu` workgroups per CU with a grid-stride
+// loop (fewer waves in flight keep the HBM access window narrow).
+struct LaunchPolicy {
+    unsigned wg_small;
+    unsigned wg_large;
+    unsigned small_per_cu;
+    unsigned max_wgs_per_cu;
+};
+
+void launch_geometry(size_t threads, const LaunchPolicy& p, dim3& grid, dim3& block);
+
 // Launchers (return the hipError_t of the launch). dtype: 0 FP32, 1 BF16.
 // fmt: 0 E4M3, 1 E5M2.
 hipError_t launch_reduce_flat(const FlatArgs& a, int nsrc, int dtype, hipStream_t s);

@@ -196,6 +196,20 @@ def test_quant_shapes(dtype, fmt, block):
             assert bits_equal(gs[j], rs[j]), f"scales count={count} src={j}: " + first_mismatch(gs[j], rs[j])
 
 
+@pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
+@pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 256), (O.E4M3, 1024), (O.E5M2, 32)])
+def test_quant_large_variant_ragged(dtype, fmt, block):
+    # > 2048 large-variant tiles on a 256-CU MI355X: the 4-loads-per-lane
+    # kernel with a grid-stride loop, ragged tail and partial last block
+    count = 5 * (1 << 20) + 5
+    log(f"quant large variant dtype={dtype} fmt={fmt} block={block}")
+    srcs = [G.fill(count, dtype, G.NORMAL_OUTLIER, seed=3500 + block, rank=0)]
+    gc, gs = _quant_gpu(srcs, dtype, fmt, block, count)
+    rc, rs = O.quant_fp8(srcs, dtype, fmt, block)
+    assert bits_equal(gc[0], rc[0]), first_mismatch(gc[0], rc[0])
+    assert bits_equal(gs[0], rs[0]), first_mismatch(gs[0], rs[0])
+
+
 def test_quant_degenerate_blocks():
     # zero blocks, tiny blocks (FMAX / A overflows), huge values, -0
     count, block = 1024, 128
@@ -254,6 +268,23 @@ def test_drr_shapes(fmt, block, n):
                 assert (g is None) == (r is None)
                 if g is not None:
                     assert bits_equal(g, r), f"{name} count={count}: " + first_mismatch(g, r)
+
+
+@pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 256), (O.E4M3, 32)])
+def test_drr_large_variant_ragged(fmt, block):
+    # > 1024 tiles of 1024 codes: the 16-codes-per-lane kernel, grid-stride,
+    # ragged tail and partial last block
+    n, count = 4, (1 << 21) + 7
+    srcs = [G.fill(count, O.FP32, G.LAPLACE, seed=4500 + block, rank=r) for r in range(n)]
+    codes, scales = O.quant_fp8(srcs, O.FP32, fmt, block)
+    for mode, hp_dtype, want_hp in ((O.DRR_SUM, O.BF16, True), (O.DRR_REQUANT, O.FP32, True)):
+        log(f"drr large variant fmt={fmt} block={block} mode={mode}")
+        got = _drr_gpu(codes, scales, fmt, block, mode, hp_dtype, want_hp, count)
+        ref = O.dequant_reduce_requant(codes, scales, fmt, block, mode, hp_dtype, want_hp)
+        for name, g, r in zip(("codes", "scales", "hp"), got, ref):
+            assert (g is None) == (r is None)
+            if g is not None:
+                assert bits_equal(g, r), f"{name}: " + first_mismatch(g, r)
 
 
 def test_lp_fp32_workload_full():
