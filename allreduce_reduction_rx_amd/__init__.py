@@ -21,7 +21,7 @@ __all__ = [
     "RX_DRR_REQUANT", "RX_MAX_SRC", "RxError", "lib", "lib_path",
     "rx_reduce_flat", "rx_reduce_scatter_chunk_bcast", "rx_tree_chunk",
     "rx_quant_fp8", "rx_dequant_reduce_requant", "rx_status_string",
-    "EXPORTED_SYMBOLS",
+    "rx_lp_reduce_scatter_chunk_bcast", "rx_lp_tree_chunk", "EXPORTED_SYMBOLS",
 ]
 
 RX_FP32, RX_BF16, RX_FP8_E4M3, RX_FP8_E5M2 = 0, 1, 2, 3
@@ -31,7 +31,7 @@ RX_MAX_SRC = 16
 EXPORTED_SYMBOLS = (
     "rx_reduce_flat", "rx_reduce_scatter_chunk_bcast", "rx_tree_chunk",
     "rx_quant_fp8", "rx_dequant_reduce_requant", "rx_status_string",
-    "rxtest_fp8_encode_bits", "rxtest_fp8_decode", "rxtest_bf16_round_bits",
+    "rx_lp_reduce_scatter_chunk_bcast", "rx_lp_tree_chunk", "rxtest_fp8_encode_bits", "rxtest_fp8_decode", "rxtest_bf16_round_bits",
     "rxtest_group_max",
 )
 
@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
             "rx_tree_chunk": [_SZ, _I, _I, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)],
             "rx_quant_fp8": [_PP, _I, _SZ, _I, _I, _I, _PP, _PP, _P],
             "rx_dequant_reduce_requant": [_PP, _PP, _I, _SZ, _I, _I, _I, _P, _P, _P, _I, _P],
+            "rx_lp_reduce_scatter_chunk_bcast": [_PP, _PP, _I, _SZ, _I, _I, _I, _PP, _PP, _P,
+                                                 _I, _P],
+            "rx_lp_tree_chunk": [_SZ, _I, _I, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)],
             "rxtest_fp8_encode_bits": [ctypes.c_uint32, _SZ, _I, _P, _P],
             "rxtest_fp8_decode": [_P, _SZ, _I, _P, _P],
             "rxtest_bf16_round_bits": [ctypes.c_uint32, _SZ, _P, _P],
@@ -234,6 +237,46 @@ def rx_dequant_reduce_requant(codes: Sequence, scales: Sequence, fmt, block: int
                                            mode, ptr(out_codes), ptr(out_scales), ptr(out_hp),
                                            hp_dt, _stream(stream)),
            "rx_dequant_reduce_requant")
+
+
+def rx_lp_tree_chunk(count: int, nsrc: int, block: int, rank: int) -> Tuple[int, int]:
+    lo, hi = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().rx_lp_tree_chunk(count, nsrc, block, rank, ctypes.byref(lo), ctypes.byref(hi)),
+           "rx_lp_tree_chunk")
+    return lo.value, hi.value
+
+
+def rx_lp_reduce_scatter_chunk_bcast(codes: Sequence, scales: Sequence, fmt, block: int,
+                                     rank: int, dst_codes: Sequence, dst_scales: Sequence,
+                                     out_hp=None, count: Optional[int] = None,
+                                     stream=None) -> None:
+    """Requantized chunk `rank` of the FP32 sum of the dequantized inputs,
+    pushed into every dst_codes[j] / dst_scales[j] (and out_hp when given)."""
+    import torch
+    count = codes[0].numel() if count is None else count
+    nb = -(-count // block) if block > 0 else 0
+    n = len(codes)
+    if not (len(scales) == len(dst_codes) == len(dst_scales) == n):
+        raise ValueError("need one scale, destination-code and destination-scale buffer per rank")
+    for k in range(n):
+        for name, t, dt, need in (("codes", codes[k], torch.uint8, count),
+                                  ("scales", scales[k], torch.float32, nb),
+                                  ("dst_codes", dst_codes[k], torch.uint8, count),
+                                  ("dst_scales", dst_scales[k], torch.float32, nb)):
+            _gpu(t, f"{name}[{k}]")
+            if t.dtype != dt or t.numel() < need:
+                raise ValueError(f"{name}[{k}] must be {dt} with >= {need} elements")
+    hp_dt = RX_FP32
+    if out_hp is not None:
+        _gpu(out_hp, "out_hp")
+        hp_dt = _rx_dtype(out_hp)
+        if out_hp.numel() < count:
+            raise ValueError("out_hp too small")
+    arr = lambda ts: _ptr_array([t.data_ptr() for t in ts])
+    _check(lib().rx_lp_reduce_scatter_chunk_bcast(
+        arr(codes), arr(scales), n, count, _fp8_code(fmt), block, rank, arr(dst_codes),
+        arr(dst_scales), None if out_hp is None else out_hp.data_ptr(), hp_dt, _stream(stream)),
+        "rx_lp_reduce_scatter_chunk_bcast")
 
 
 # ---- test hooks (rx_testhooks.h) -------------------------------------------

@@ -30,12 +30,11 @@ int device_cu_count()
     return cus;
 }
 
-void launch_geometry(size_t threads, const LaunchPolicy& p, dim3& grid, dim3& block)
+void launch_geometry(size_t threads, bool small, const LaunchPolicy& p, dim3& grid, dim3& block)
 {
     const size_t cus = (size_t)device_cu_count();
     if (threads == 0)
         threads = 1;
-    const bool small = threads < cus * p.small_per_cu;
     const unsigned wg = small ? p.wg_small : p.wg_large;
     size_t blocks = (threads + wg - 1) / wg;
     if (!small && blocks > cus * p.max_wgs_per_cu)
@@ -78,6 +77,12 @@ rx_status_t check_ptrs(const void* const* p, int n, bool align16)
         if (align16 ? !aligned16(p[j]) : !aligned4(p[j]))
             return RX_ERR_ALIGN;
     return RX_OK;
+}
+
+size_t lp_chunk_len(size_t count, int nsrc, int block)
+{
+    size_t c = (count + (size_t)nsrc - 1) / (size_t)nsrc;
+    return (c + (size_t)block - 1) / (size_t)block * (size_t)block;
 }
 
 size_t tree_chunk_len(size_t count, int nsrc, rx_dtype_t dtype)
@@ -254,13 +259,80 @@ rx_status_t rx_dequant_reduce_requant(const void* const* codes,
         a.codes[j] = codes[j];
         a.scales[j] = scales[j];
     }
-    a.out_codes = out_codes;
-    a.out_scales = out_scales;
+    a.out_codes[0] = out_codes;
+    a.out_scales[0] = out_scales;
+    a.nout = requant ? 1 : 0;
     a.out_hp = out_hp;
-    a.count = count;
+    a.lo = 0;
+    a.hi = count;
     a.block = block;
     a.hp_bf16 = hp_dtype == RX_BF16 ? 1 : 0;
     return launched(rx::launch_drr(a, nsrc, fp8_dtype == RX_FP8_E5M2 ? 1 : 0, requant, stream));
+}
+
+rx_status_t rx_lp_tree_chunk(size_t count, int nsrc, int block, int rank,
+                             size_t* lo, size_t* hi)
+{
+    if (!lo || !hi)
+        return RX_ERR_NULL;
+    if (nsrc < 1 || nsrc > RX_MAX_SRC || rank < 0 || rank >= nsrc || !valid_block(block) ||
+        count > kMaxCount)
+        return RX_ERR_ARG;
+    const size_t c = lp_chunk_len(count, nsrc, block);
+    size_t a = (size_t)rank * c;
+    if (a > count) a = count;
+    size_t b = a + c;
+    if (b > count) b = count;
+    *lo = a;
+    *hi = b;
+    return RX_OK;
+}
+
+rx_status_t rx_lp_reduce_scatter_chunk_bcast(const void* const* codes,
+                                             const float* const* scales, int nsrc,
+                                             size_t count, rx_dtype_t fp8_dtype,
+                                             int block, int rank,
+                                             void* const* dst_codes,
+                                             float* const* dst_scales,
+                                             void* out_hp, rx_dtype_t hp_dtype,
+                                             hipStream_t stream)
+{
+    if (!codes || !scales || !dst_codes || !dst_scales)
+        return RX_ERR_NULL;
+    if (nsrc < 1 || nsrc > RX_MAX_SRC || rank < 0 || rank >= nsrc || !valid_block(block) ||
+        count > kMaxCount)
+        return RX_ERR_ARG;
+    if (!fp8_type(fp8_dtype) || (out_hp && !hp_type(hp_dtype)))
+        return RX_ERR_DTYPE;
+    rx_status_t st = check_ptrs(codes, nsrc, true);
+    if (st == RX_OK)
+        st = check_ptrs(reinterpret_cast<const void* const*>(scales), nsrc, false);
+    if (st == RX_OK)
+        st = check_ptrs(reinterpret_cast<const void* const*>(dst_codes), nsrc, true);
+    if (st == RX_OK)
+        st = check_ptrs(reinterpret_cast<const void* const*>(dst_scales), nsrc, false);
+    if (st != RX_OK)
+        return st;
+    if (out_hp && !aligned16(out_hp))
+        return RX_ERR_ALIGN;
+    size_t lo = 0, hi = 0;
+    rx_lp_tree_chunk(count, nsrc, block, rank, &lo, &hi);
+    if (lo >= hi)
+        return RX_OK;
+    rx::DrrArgs a = {};
+    for (int j = 0; j < nsrc; ++j) {
+        a.codes[j] = codes[j];
+        a.scales[j] = scales[j];
+        a.out_codes[j] = dst_codes[j];
+        a.out_scales[j] = dst_scales[j];
+    }
+    a.nout = nsrc;
+    a.out_hp = out_hp;
+    a.lo = lo;
+    a.hi = hi;
+    a.block = block;
+    a.hp_bf16 = hp_dtype == RX_BF16 ? 1 : 0;
+    return launched(rx::launch_drr(a, nsrc, fp8_dtype == RX_FP8_E5M2 ? 1 : 0, true, stream));
 }
 
 }  // extern "C"

@@ -313,14 +313,15 @@ __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
     const uint32_t waves_per_wg = blockDim.x / kWave;
     const uint32_t wave = blockIdx.x * waves_per_wg + wave_in_wg;
     const uint32_t nwaves = gridDim.x * waves_per_wg;
-    const size_t count = a.count;
+    const size_t count = a.hi;                                    // end of the range
     constexpr size_t kTile = (size_t)kWave * CPL;                 // codes per wave tile
-    const uint32_t ntiles = (uint32_t)((count + kTile - 1) / kTile);
+    const uint32_t ntiles = (uint32_t)((a.hi - a.lo + kTile - 1) / kTile);
+    const size_t v0 = a.lo / CPL;                                 // lo is a block multiple
     const int lpb = a.block / CPL;                                // lanes per block: 2..64
     const int bshift = __builtin_ctz((unsigned)a.block);
 
     for (uint32_t t = wave; t < ntiles; t += nwaves) {
-        const size_t v = (size_t)t * kWave + lane;   // this lane's CPL-code vector
+        const size_t v = v0 + (size_t)t * kWave + lane;  // this lane's CPL-code vector
         const size_t e = v * CPL;
         const bool whole = e + CPL <= count;
         const bool valid = e < count;
@@ -363,9 +364,11 @@ __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
         for (int p = 0; p < CPL / 4; ++p)
             q[p] = f32x4_to_fp8<F>(clamp_fmax<F>(S[4 * p + 0] * r2), clamp_fmax<F>(S[4 * p + 1] * r2),
                                    clamp_fmax<F>(S[4 * p + 2] * r2), clamp_fmax<F>(S[4 * p + 3] * r2));
-        store_codes<CPL>(static_cast<uint8_t*>(a.out_codes), v, e, count, whole, q);
+        for (int j = 0; j < a.nout; ++j)   // push the chunk to every destination
+            store_codes<CPL>(static_cast<uint8_t*>(a.out_codes[j]), v, e, count, whole, q);
         if (valid && (lane % lpb) == 0)
-            a.out_scales[b] = s2;
+            for (int j = 0; j < a.nout; ++j)
+                a.out_scales[j][b] = s2;
 
         if (a.out_hp) {
             float h[CPL];
@@ -420,9 +423,9 @@ const DrrTable<4> kDrr4;
 
 // One wave per tile (64 threads per work item). Large messages: 256-thread
 // workgroups, at most 3 per CU (a narrow HBM access window measured best on
-// MI355X); decode-size messages: 64-thread workgroups over every CU.
-LaunchPolicy policy_quant() { return {64u, 256u, 512u, 3u}; }
-LaunchPolicy policy_drr() { return {64u, 256u, 512u, 3u}; }
+// MI355X); decode-size messages: one tile per wave over every CU.
+LaunchPolicy policy_quant() { return {256u, 256u, 3u}; }
+LaunchPolicy policy_drr() { return {64u, 256u, 3u}; }
 
 // Below this many large-variant wave tiles per CU a message counts as
 // decode-size and takes the narrow variant.
@@ -443,7 +446,7 @@ hipError_t launch_quant(const QuantArgs& a, int src_dtype, int fmt, int block, h
     const size_t tile_elems = u * 64 * vec_elems;
     const size_t tiles = (a.count + tile_elems - 1) / tile_elems * (size_t)a.nsrc;
     dim3 grid, blk;
-    launch_geometry(tiles * kWave, policy_quant(), grid, blk);
+    launch_geometry(tiles * kWave, small, policy_quant(), grid, blk);
     QuantArgs arg = a;
     void* params[] = {&arg};
     QuantFn fn = small ? kQuantSmall.fn[src_dtype][fmt][lb] : kQuantLarge.fn[src_dtype][fmt][lb];
@@ -453,15 +456,17 @@ hipError_t launch_quant(const QuantArgs& a, int src_dtype, int fmt, int block, h
 hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStream_t s)
 {
     const size_t cus = (size_t)device_cu_count();
-    const bool small = a.block <= 256 && (a.count + 1023) / 1024 < kSmallTilesPerCu * cus / 2;
-    const size_t tile = small ? 256 : 1024;
-    const size_t tiles = (a.count + tile - 1) / tile;
+    const size_t len = a.hi - a.lo;
+    const bool small = (len + 1023) / 1024 < kSmallTilesPerCu * cus / 2;
+    const bool narrow = small && a.block <= 256;   // 4 codes per lane
+    const size_t tile = narrow ? 256 : 1024;
+    const size_t tiles = (len + tile - 1) / tile;
     dim3 grid, blk;
-    launch_geometry(tiles * kWave, policy_drr(), grid, blk);
+    launch_geometry(tiles * kWave, small, policy_drr(), grid, blk);
     DrrArgs arg = a;
     void* params[] = {&arg};
     const int r = requant ? 1 : 0;
-    DrrFn fn = small ? kDrr4.fn[fmt][r][nsrc - 1] : kDrr16.fn[fmt][r][nsrc - 1];
+    DrrFn fn = narrow ? kDrr4.fn[fmt][r][nsrc - 1] : kDrr16.fn[fmt][r][nsrc - 1];
     return hipLaunchKernel((const void*)fn, grid, blk, params, 0, s);
 }
 

@@ -25,13 +25,15 @@ template <> struct Elem<0> { static constexpr int kVE = 4; };  // FP32: 4 per 16
 template <> struct Elem<1> { static constexpr int kVE = 8; };  // BF16: 8 per 16 B
 
 // Fold vector `v` (16 bytes) of N sources; returns the narrowed 16 bytes.
-template <int DT, int N>
+// NT: nontemporal source loads (data read once; measured faster for flat,
+// slower for the tree step's short chunks).
+template <int DT, int N, bool NT>
 __device__ __forceinline__ u32x4 fold_vec(const void* const* src, size_t v)
 {
     u32x4 x[N];
 #pragma unroll
     for (int r = 0; r < N; ++r)
-        x[r] = ld16_stream(src[r], v);   // read once: do not keep in the caches
+        x[r] = NT ? ld16_stream(src[r], v) : ld16(src[r], v);
     u32x4 out;
     if constexpr (DT == 0) {
 #pragma unroll
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(256) void k_reduce_flat(FlatArgs a)
     const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (size_t v = gid; v < nvec; v += stride)
-        st16(a.dst, v, fold_vec<DT, N>(a.src, v));
+        st16(a.dst, v, fold_vec<DT, N, true>(a.src, v));
     const size_t i = nvec * VE + gid;
     if (i < a.count)
         store_elem<DT>(a.dst, i, fold_elem<DT, N>(a.src, i));
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(256) void k_tree(TreeArgs a)
     const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (size_t v = v0 + gid; v < v1; v += stride) {
-        u32x4 y = fold_vec<DT, N>(a.src, v);
+        u32x4 y = fold_vec<DT, N, false>(a.src, v);
 #pragma unroll
         for (int j = 0; j < N; ++j)
             st16(a.dst[j], v, y);
@@ -149,8 +151,10 @@ const std::array<TreeFn, kMaxSrc> kTree[2] = {
 // workgroup per CU (flat) or two 128-thread ones (tree) with a grid-stride
 // loop: on MI355X a narrow window of in-flight addresses measured up to 20%
 // faster than filling every CU with 8 workgroups.
-LaunchPolicy policy_flat() { return {128u, 256u, 512u, 1u}; }
-LaunchPolicy policy_tree() { return {64u, 128u, 512u, 2u}; }
+LaunchPolicy policy_flat() { return {128u, 256u, 1u}; }
+LaunchPolicy policy_tree() { return {64u, 128u, 2u}; }
+
+bool small_job(size_t threads) { return threads < kSmallThreadsPerCu * (size_t)device_cu_count(); }
 
 }  // namespace
 
@@ -158,7 +162,7 @@ hipError_t launch_reduce_flat(const FlatArgs& a, int nsrc, int dtype, hipStream_
 {
     const int ve = dtype == 0 ? 4 : 8;
     dim3 grid, block;
-    launch_geometry(a.count / ve, policy_flat(), grid, block);
+    launch_geometry(a.count / ve, small_job(a.count / ve), policy_flat(), grid, block);
     FlatArgs arg = a;
     void* params[] = {&arg};
     return hipLaunchKernel((const void*)kFlat[dtype][nsrc - 1], grid, block, params, 0, s);
@@ -168,7 +172,7 @@ hipError_t launch_tree(const TreeArgs& a, int nsrc, int dtype, hipStream_t s)
 {
     const int ve = dtype == 0 ? 4 : 8;
     dim3 grid, block;
-    launch_geometry((a.hi - a.lo) / ve, policy_tree(), grid, block);
+    launch_geometry((a.hi - a.lo) / ve, small_job((a.hi - a.lo) / ve), policy_tree(), grid, block);
     TreeArgs arg = a;
     void* params[] = {&arg};
     return hipLaunchKernel((const void*)kTree[dtype][nsrc - 1], grid, block, params, 0, s);

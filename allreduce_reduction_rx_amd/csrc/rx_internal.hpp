@@ -35,12 +35,13 @@ struct QuantArgs {
 struct DrrArgs {
     const void* codes[kMaxSrc];
     const float* scales[kMaxSrc];
-    void* out_codes;   // REQUANT only
-    float* out_scales; // REQUANT only
-    void* out_hp;      // SUM: required; REQUANT: optional
-    size_t count;
-    int block;         // elements per scale block
-    int hp_bf16;       // out_hp element type: 1 = BF16, 0 = FP32
+    void* out_codes[kMaxSrc];    // REQUANT: nout code buffers (message-indexed)
+    float* out_scales[kMaxSrc];  // REQUANT: nout scale buffers (block-indexed)
+    void* out_hp;                // SUM: required; REQUANT: optional
+    size_t lo, hi;               // element range processed; lo is a block multiple
+    int nout;                    // REQUANT: destinations that receive the result
+    int block;                   // elements per scale block
+    int hp_bf16;                 // out_hp element type: 1 = BF16, 0 = FP32
 };
 
 // Launch geometry helper: number of compute units of the current device
@@ -48,19 +49,21 @@ struct DrrArgs {
 int device_cu_count();
 
 // How a kernel spreads `threads` work items (one per 16-byte vector, or 64
-// per wave tile) over the GPU. Jobs with fewer than `small_per_cu` threads
-// per CU use `wg_small`-thread workgroups, one work item per thread, so that
-// a decode-size message still reaches every CU; larger jobs use `wg_large`
-// threads and at most `max_wgs_per_cu` workgroups per CU with a grid-stride
-// loop (fewer waves in flight keep the HBM access window narrow).
+// per wave tile) over the GPU. Decode-size jobs (`small`) get one work item
+// per thread in `wg_small`-thread workgroups, so that even a 512 KiB message
+// reaches every CU; large jobs use `wg_large` threads and at most
+// `max_wgs_per_cu` workgroups per CU with a grid-stride loop (fewer waves in
+// flight keep the HBM access window narrow).
 struct LaunchPolicy {
     unsigned wg_small;
     unsigned wg_large;
-    unsigned small_per_cu;
     unsigned max_wgs_per_cu;
 };
 
-void launch_geometry(size_t threads, const LaunchPolicy& p, dim3& grid, dim3& block);
+// Jobs below this many threads per CU count as decode-size.
+constexpr size_t kSmallThreadsPerCu = 512;
+
+void launch_geometry(size_t threads, bool small, const LaunchPolicy& p, dim3& grid, dim3& block);
 
 // Launchers (return the hipError_t of the launch). dtype: 0 FP32, 1 BF16.
 // fmt: 0 E4M3, 1 E5M2.

@@ -12,8 +12,10 @@ rank buffers (N = 8 separate HBM allocations):
 The default workload is the decode-size message: 8 x 32x8192 BF16 (512 KiB
 per rank), low-precision leg in E5M2 with 256-element blocks. Inputs are
 resident in HBM before timing starts; the batches rotate over enough copies
-(>= 1 GiB in total) that every step reads its inputs from HBM rather than
-from the 256 MB Infinity Cache.
+(>= 2 GiB in total) that every step reads its inputs from HBM rather than
+from the 256 MB Infinity Cache. The low-precision tree step (one rank's
+share of a low-precision reduce-scatter + all-gather) is timed beside the
+step.
 
 Output: one JSON line (see the fields below). Per-kernel times come from HIP
 events around back-to-back launches of that kernel alone, on the stream the
@@ -40,6 +42,7 @@ KERNEL_SOURCES = {
     "tree_step": ["reduce.hip", "rx_device.hpp"],
     "quant_fp8": ["lowprec.hip", "rx_device.hpp"],
     "dequant_reduce_requant": ["lowprec.hip", "rx_device.hpp"],
+    "lp_tree_step": ["lowprec.hip", "rx_device.hpp"],
 }
 # rocprofv3 kernel names (substrings of the mangled names)
 KERNEL_SYMBOLS = {
@@ -47,6 +50,7 @@ KERNEL_SYMBOLS = {
     "tree_step": "k_tree",
     "quant_fp8": "k_quant",
     "dequant_reduce_requant": "k_drr",
+    "lp_tree_step": "k_drr",
 }
 
 
@@ -111,6 +115,8 @@ class Batch:
         self.out_codes = torch.empty(count, dtype=torch.uint8, device=dev)
         self.out_scales = torch.empty(nb, dtype=torch.float32, device=dev)
         self.out_hp = torch.empty(count, dtype=dt, device=dev)
+        self.lp_dst_codes = [torch.empty(count, dtype=torch.uint8, device=dev) for _ in range(n)]
+        self.lp_dst_scales = [torch.empty(nb, dtype=torch.float32, device=dev) for _ in range(n)]
 
 
 def main():
@@ -153,6 +159,8 @@ def main():
     chunk_lo, chunk_hi = rx.rx_tree_chunk(count, n, w.dtype, 0)
     chunk = chunk_hi - chunk_lo
 
+    lp_lo, lp_hi = rx.rx_lp_tree_chunk(count, n, lp_block, 0)
+    lp_chunk = lp_hi - lp_lo
     bytes_k = {
         "reduce_flat": n * count * e + count * e,
         "tree_step": 2 * n * chunk * e,
@@ -160,15 +168,18 @@ def main():
         "dequant_reduce_requant": n * (count + 4 * nb) + (count + 4 * nb) + count * e,
     }
     step_bytes = sum(bytes_k.values())
+    # measured beside the step, not part of it: the low-precision tree step
+    bytes_k["lp_tree_step"] = 2 * n * (lp_chunk + 4 * (lp_chunk // lp_block))
     per_batch_bytes = (n * count * e            # sources
                        + count * e              # flat out
                        + n * count * e          # tree destinations
                        + n * (count + 4 * nb)   # codes + scales
-                       + count + 4 * nb + count * e)
+                       + count + 4 * nb + count * e
+                       + n * (count + 4 * nb))    # low-precision tree destinations
     if args.warm:
         nsets = 1
     else:
-        nsets = max(1, min(256, -(-(1 << 30) // per_batch_bytes)))
+        nsets = max(1, min(256, -(-(2 << 30) // per_batch_bytes)))
     free, _ = torch.cuda.mem_get_info()
     nsets = max(1, min(nsets, int(0.6 * free // per_batch_bytes)))
     batches = [Batch(w, base, lp_fmt, lp_block, torch)]
@@ -189,6 +200,10 @@ def main():
         rx.rx_dequant_reduce_requant(b.codes, b.scales, lp_fmt, lp_block, rx.RX_DRR_REQUANT,
                                      b.out_codes, b.out_scales, b.out_hp)
 
+    def k_lp_tree(b, i):
+        rx.rx_lp_reduce_scatter_chunk_bcast(b.codes, b.scales, lp_fmt, lp_block, i % n,
+                                            b.lp_dst_codes, b.lp_dst_scales)
+
     kernels = [("reduce_flat", k_flat), ("tree_step", k_tree),
                ("quant_fp8", k_quant), ("dequant_reduce_requant", k_drr)]
 
@@ -196,6 +211,8 @@ def main():
         b = batches[i % nsets]
         for _, fn in kernels:
             fn(b, i)
+
+    kernels_timed = kernels + [("lp_tree_step", k_lp_tree)]
 
     def capture(calls):
         """HIP graph of the given launches (captured on torch's capture
@@ -235,7 +252,7 @@ def main():
 
     # ---- per-kernel timing: back-to-back launches of one kernel ----
     per_kernel = {}
-    for name, fn in kernels:
+    for name, fn in kernels_timed:
         reps = args.kernel_reps or max(50, min(2000, int(0.05 / max(1e-7, bytes_k[name] / 4e12))))
         calls = [lambda i=i: fn(batches[i % nsets], i) for i in range(reps)]
         if args.no_graph:
@@ -263,7 +280,7 @@ def main():
                               b0.flat_out[lo:hi].view(torch.int16 if tdt == torch.bfloat16 else torch.int32))
                   for d in b0.tree_dsts)
 
-    dominant = max(per_kernel, key=lambda k: per_kernel[k]["us"])
+    dominant = max((k for k, _ in kernels), key=lambda k: per_kernel[k]["us"])
     dk = per_kernel[dominant]
     traffic = read_traffic(dominant, args.workload)
     value = step_bytes / (step_ms * 1e-3) / 1e9

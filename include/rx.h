@@ -164,6 +164,43 @@ rx_status_t rx_dequant_reduce_requant(const void* const* codes,
                                       void* out_hp, rx_dtype_t hp_dtype,
                                       hipStream_t stream);
 
+/*
+ * Low-precision tree step: one rank's share of a low-precision
+ * reduce-scatter + all-gather, i.e. the DDA tree split (RCCLX article, "Core
+ * feature 1: Direct Data Access (DDA)", DDA Tree item) applied to the FP8
+ * messages of the low-precision collectives ("Core feature 2: Low-Precision
+ * Collectives", which lists ReduceScatter and AllGather among the supported
+ * operations). This rank dequantizes its chunk of every rank's codes, sums in
+ * FP32, requantizes exactly as rx_dequant_reduce_requant does, and pushes the
+ * FP8 codes and scales of the chunk into every destination.
+ *
+ * Chunks are whole scale blocks (the pages do not fix the split):
+ * c = roundup(ceil(count/nsrc), block); chunk k = [min(k c, count),
+ * min(k c + c, count)); rx_lp_tree_chunk() returns the bounds.
+ *
+ * codes, scales         : nsrc device pointers (count bytes, ceil(count/block)
+ *                         floats), the ranks' quantized messages.
+ * rank                  : 0 .. nsrc-1, the chunk this call reduces.
+ * dst_codes, dst_scales : nsrc device pointers each, message-indexed like the
+ *                         inputs; only chunk `rank` (codes) and its blocks
+ *                         (scales) are written.
+ * out_hp                : optional (NULL): chunk `rank` of the dequantized
+ *                         result, hp_dtype RX_FP32 or RX_BF16, message-indexed.
+ * Destinations must not overlap the inputs.
+ */
+rx_status_t rx_lp_reduce_scatter_chunk_bcast(const void* const* codes,
+                                             const float* const* scales, int nsrc,
+                                             size_t count, rx_dtype_t fp8_dtype,
+                                             int block, int rank,
+                                             void* const* dst_codes,
+                                             float* const* dst_scales,
+                                             void* out_hp, rx_dtype_t hp_dtype,
+                                             hipStream_t stream);
+
+/* Host helper: bounds [*lo, *hi) of low-precision chunk `rank` (no HIP call). */
+rx_status_t rx_lp_tree_chunk(size_t count, int nsrc, int block, int rank,
+                             size_t* lo, size_t* hi);
+
 /* Static description of a status code (never NULL). */
 const char* rx_status_string(rx_status_t s);
 

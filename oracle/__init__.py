@@ -51,6 +51,9 @@ def lib():
             "rxo_quant_fp8": (None, [_P, _I, _SZ, _I, _I, _I, _P, _P]),
             "rxo_dequant_reduce_requant": (None, [_P, _P, _I, _SZ, _I, _I, _I,
                                                   _P, _P, _P, _I]),
+            "rxo_lp_tree_chunk": (None, [_SZ, _I, _I, _I, _P, _P]),
+            "rxo_lp_reduce_scatter_chunk_bcast": (None, [_P, _P, _I, _SZ, _I, _I, _I,
+                                                         _P, _P, _P, _I]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -183,3 +186,33 @@ def dequant_reduce_requant(codes: Sequence[np.ndarray], scales: Sequence[np.ndar
     lib().rxo_dequant_reduce_requant(_ptrs(codes), _ptrs(scales), len(codes), count,
                                      fmt, block, mode, cptr, sptr, hptr, hp_dtype)
     return out_codes, out_scales, out_hp
+
+
+def lp_tree_chunk(count: int, nsrc: int, block: int, rank: int) -> Tuple[int, int]:
+    lo = ctypes.c_size_t()
+    hi = ctypes.c_size_t()
+    lib().rxo_lp_tree_chunk(count, nsrc, block, rank, ctypes.byref(lo), ctypes.byref(hi))
+    return lo.value, hi.value
+
+
+def lp_reduce_scatter_chunk_bcast(codes: Sequence[np.ndarray], scales: Sequence[np.ndarray],
+                                  fmt: int, block: int, rank: int,
+                                  dst_codes: Sequence[np.ndarray], dst_scales: Sequence[np.ndarray],
+                                  out_hp: Optional[np.ndarray] = None, hp_dtype: int = FP32,
+                                  count: Optional[int] = None) -> None:
+    """Writes the requantized chunk `rank` into every dst_codes[j] /
+    dst_scales[j] (and its dequantized values into out_hp when given)."""
+    count = codes[0].size if count is None else count
+    nb = (count + block - 1) // block
+    _check(codes, np.uint8, count)
+    _check(scales, np.float32, nb)
+    _check(dst_codes, np.uint8, count)
+    _check(dst_scales, np.float32, nb)
+    assert len(codes) == len(scales) == len(dst_codes) == len(dst_scales)
+    hptr = None
+    if out_hp is not None:
+        _check([out_hp], _np_of(hp_dtype), count)
+        hptr = out_hp.ctypes.data
+    lib().rxo_lp_reduce_scatter_chunk_bcast(_ptrs(codes), _ptrs(scales), len(codes), count,
+                                            fmt, block, rank, _ptrs(dst_codes),
+                                            _ptrs(dst_scales), hptr, hp_dtype)

@@ -350,3 +350,59 @@ void rxo_dequant_reduce_requant(const uint8_t* const* codes,
     free(cq);
     free(sum);
 }
+
+/* ---------------------------------------------------------------------- */
+/* Low-precision tree step                                                 */
+/* ---------------------------------------------------------------------- */
+
+void rxo_lp_tree_chunk(size_t count, int nsrc, int block, int rank,
+                       size_t* lo, size_t* hi)
+{
+    size_t c = (count + (size_t)nsrc - 1) / (size_t)nsrc;
+    c = (c + (size_t)block - 1) / (size_t)block * (size_t)block;
+    size_t a = (size_t)rank * c;
+    if (a > count) a = count;
+    size_t b = a + c;
+    if (b > count) b = count;
+    *lo = a;
+    *hi = b;
+}
+
+/* The reduce-scatter / all-gather split of the DDA tree item of the RCCLX
+ * article ("Core feature 1") carried out on the FP8 messages of "Core
+ * feature 2": this rank reduces its chunk of every rank's codes in FP32,
+ * requantizes it, and pushes the FP8 chunk to every rank. */
+void rxo_lp_reduce_scatter_chunk_bcast(const uint8_t* const* codes,
+                                       const float* const* scales, int nsrc,
+                                       size_t count, int fmt, int block,
+                                       int rank, uint8_t* const* dst_codes,
+                                       float* const* dst_scales,
+                                       void* out_hp, int hp_dtype)
+{
+    size_t lo, hi;
+    rxo_lp_tree_chunk(count, nsrc, block, rank, &lo, &hi);
+    if (lo >= hi || nsrc > 64)
+        return;
+    size_t len = hi - lo;
+    size_t nb = (len + (size_t)block - 1) / (size_t)block;
+    size_t b0 = lo / (size_t)block;
+    const uint8_t* csub[64];
+    const float* ssub[64];
+    for (int r = 0; r < nsrc; ++r) {
+        csub[r] = codes[r] + lo;
+        ssub[r] = scales[r] + b0;
+    }
+    uint8_t* oc = (uint8_t*)malloc(len);
+    float* os = (float*)malloc(nb * sizeof(float));
+    void* hp = NULL;
+    if (out_hp)
+        hp = (uint8_t*)out_hp + lo * elem_size(hp_dtype);
+    rxo_dequant_reduce_requant(csub, ssub, nsrc, len, fmt, block, RXO_DRR_REQUANT,
+                               oc, os, hp, hp_dtype);
+    for (int j = 0; j < nsrc; ++j) {
+        memcpy(dst_codes[j] + lo, oc, len);
+        memcpy(dst_scales[j] + b0, os, nb * sizeof(float));
+    }
+    free(os);
+    free(oc);
+}

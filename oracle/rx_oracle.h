@@ -99,6 +99,24 @@ void rxo_dequant_reduce_requant(const uint8_t* const* codes,
                                 uint8_t* out_codes, float* out_scales,
                                 void* out_hp, int hp_dtype);
 
+/* Low-precision tree step (one rank's share of a low-precision
+ * reduce-scatter + all-gather). Chunks are whole scale blocks:
+ * c = roundup(ceil(count / nsrc), block); chunk k = [min(k c, count),
+ * min(k c + c, count)). */
+void rxo_lp_tree_chunk(size_t count, int nsrc, int block, int rank,
+                       size_t* lo, size_t* hi);
+
+/* Dequantize + FP32 sum + requantize the blocks of chunk `rank`, and write
+ * the requantized codes and scales of the chunk into every dst_codes[j] /
+ * dst_scales[j] (message-indexed; nothing outside the chunk is written).
+ * When out_hp is not NULL, its chunk receives dequant(requant(sum)). */
+void rxo_lp_reduce_scatter_chunk_bcast(const uint8_t* const* codes,
+                                       const float* const* scales, int nsrc,
+                                       size_t count, int fmt, int block,
+                                       int rank, uint8_t* const* dst_codes,
+                                       float* const* dst_scales,
+                                       void* out_hp, int hp_dtype);
+
 #ifdef __cplusplus
 }
 #endif

@@ -124,3 +124,27 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros(8)
     with pytest.raises(ValueError):
         rx.rx_reduce_flat([x], x)
+
+
+def test_lp_tree_validation_and_chunks():
+    L = rx.lib()
+    f = L.rx_lp_reduce_scatter_chunk_bcast
+    c, s = ptrs(FAKE, FAKE + 4096), ptrs(FAKE + 8192, FAKE + 12288)
+    dc, ds = ptrs(FAKE + 16384, FAKE + 20480), ptrs(FAKE + 24576, FAKE + 28672)
+    E4 = rx.RX_FP8_E4M3
+    assert f(None, s, 2, 1000, E4, 128, 0, dc, ds, None, rx.RX_FP32, None) == NULL
+    assert f(c, s, 2, 1000, E4, 128, 0, None, ds, None, rx.RX_FP32, None) == NULL
+    assert f(c, s, 2, 1000, E4, 128, 2, dc, ds, None, rx.RX_FP32, None) == ARG
+    assert f(c, s, 2, 1000, E4, 96, 0, dc, ds, None, rx.RX_FP32, None) == ARG
+    assert f(c, s, 2, 1000, rx.RX_FP32, 128, 0, dc, ds, None, rx.RX_FP32, None) == DTYPE
+    assert f(c, s, 2, 1000, E4, 128, 0, dc, ds, FAKE, rx.RX_FP8_E5M2, None) == DTYPE
+    assert f(c, s, 2, 1000, E4, 128, 0, ptrs(FAKE + 16384, FAKE + 8), ds, None, rx.RX_FP32, None) == ALIGN
+    assert f(c, s, 2, 1000, E4, 128, 0, dc, ptrs(FAKE, FAKE + 1), None, rx.RX_FP32, None) == ALIGN
+    assert f(c, s, 2, 1000, E4, 128, 0, dc, ds, FAKE + 4, rx.RX_BF16, None) == ALIGN
+    assert f(c, s, 2, 0, E4, 128, 1, dc, ds, None, rx.RX_FP32, None) == OK
+    # 8 ranks over the 64 MiB FP32 low-precision message, blocks of 128
+    for k in range(8):
+        assert rx.rx_lp_tree_chunk(16_777_216, 8, 128, k) == (k * 2_097_152, (k + 1) * 2_097_152)
+    assert [rx.rx_lp_tree_chunk(1000, 3, 128, k) for k in range(3)] == [(0, 384), (384, 768), (768, 1000)]
+    # an empty chunk launches nothing
+    assert f(c, s, 2, 100, E4, 128, 1, dc, ds, None, rx.RX_FP32, None) == OK

@@ -510,3 +510,80 @@ def test_p11_error_bounds(wl, fmt, block, u, uprime):
     assert np.all(np.abs(D64 - T) <= b2)
     # the literal per-element bound N * u * blockabsmax, on these inputs
     assert np.all(np.abs(D64 - T) <= n * u * Ab)
+
+
+# ---------------------------------------------------------------------------
+# Low-precision tree step: chunks are whole blocks; the chunks of all ranks
+# together reproduce the requantized allreduce; nothing outside the chunk
+# is written
+# ---------------------------------------------------------------------------
+
+def test_lp_tree_partition_brute_force():
+    for block in (32, 128, 1024):
+        for n in range(1, 17):
+            for count in list(range(0, 70)) + [block * 5 + 3, block * 16, block * 33 + 1]:
+                bounds = [O.lp_tree_chunk(count, n, block, k) for k in range(n)]
+                covered = np.zeros(count, dtype=np.int64)
+                for lo, hi in bounds:
+                    assert 0 <= lo <= hi <= count
+                    assert lo % block == 0 or lo == count
+                    covered[lo:hi] += 1
+                assert np.all(covered == 1)
+                if count:
+                    lens = [hi - lo for lo, hi in bounds]
+                    c = max(lens)
+                    last = max(k for k in range(n) if lens[k])
+                    assert all(lens[k] == c for k in range(last))
+                    cc = -(-c // block) * block
+                    assert cc * n >= count and (cc - block) * n < count
+
+
+@pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 256), (O.E4M3, 32)])
+def test_lp_tree_union_is_requantized_allreduce(fmt, block):
+    n, count = 5, block * 23 + 9
+    srcs = [G.fill(count, G.FP32, G.NORMAL_OUTLIER, seed=71, rank=r) for r in range(n)]
+    codes, scales = O.quant_fp8(srcs, O.FP32, fmt, block)
+    ref_c, ref_s, ref_h = O.dequant_reduce_requant(codes, scales, fmt, block, O.DRR_REQUANT,
+                                                   O.BF16, True)
+    nb = -(-count // block)
+    union_c = np.full(count, 0xA5, np.uint8)
+    union_s = np.full(nb, -7.0, np.float32)
+    union_h = np.full(count, 0x7FA5, np.uint16)
+    for k in range(n):
+        dc = [np.full(count, 0xA5, np.uint8) for _ in range(n)]
+        ds = [np.full(nb, -7.0, np.float32) for _ in range(n)]
+        hp = np.full(count, 0x7FA5, np.uint16)
+        O.lp_reduce_scatter_chunk_bcast(codes, scales, fmt, block, k, dc, ds, hp, O.BF16)
+        lo, hi = O.lp_tree_chunk(count, n, block, k)
+        b0, b1 = lo // block, -(-hi // block)
+        for j in range(n):
+            assert np.array_equal(dc[j][lo:hi], ref_c[lo:hi])
+            assert np.all(dc[j][:lo] == 0xA5) and np.all(dc[j][hi:] == 0xA5)
+            assert np.array_equal(ds[j][b0:b1], ref_s[b0:b1])
+            assert np.all(ds[j][:b0] == -7.0) and np.all(ds[j][b1:] == -7.0)
+        assert np.array_equal(hp[lo:hi], ref_h[lo:hi])
+        assert np.all(hp[:lo] == 0x7FA5) and np.all(hp[hi:] == 0x7FA5)
+        union_c[lo:hi] = dc[0][lo:hi]
+        union_s[b0:b1] = ds[0][b0:b1]
+        union_h[lo:hi] = hp[lo:hi]
+    assert np.array_equal(union_c, ref_c) and np.array_equal(union_s, ref_s)
+    assert np.array_equal(union_h, ref_h)
+
+
+def test_lp_tree_rank_id_example():
+    # the pages' rank-id example through the low-precision tree: every chunk
+    # requantizes to the max code with scale 28/FMAX and dequantizes to 28
+    n, count = 8, 200
+    for fmt_s, block_s, maxc_s, s2_s, res_s in read_golden("rank_id_lowprec.txt"):
+        fmt, block, maxc = O.FMT[fmt_s], int(block_s), int(maxc_s, 16)
+        srcs = [G.fill(count, G.FP32, G.RANK, rank=r) for r in range(n)]
+        codes, scales = O.quant_fp8(srcs, O.FP32, fmt, block)
+        nb = -(-count // block)
+        dc = [np.zeros(count, np.uint8) for _ in range(n)]
+        ds = [np.zeros(nb, np.float32) for _ in range(n)]
+        hp = np.zeros(count, np.float32)
+        for k in range(n):
+            O.lp_reduce_scatter_chunk_bcast(codes, scales, fmt, block, k, dc, ds, hp, O.FP32)
+        for j in range(n):
+            assert np.all(dc[j] == maxc) and np.all(ds[j] == np.float32(float(s2_s)))
+        assert np.all(hp == np.float32(float(res_s)))

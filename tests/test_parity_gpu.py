@@ -287,6 +287,57 @@ def test_drr_large_variant_ragged(fmt, block):
                 assert bits_equal(g, r), f"{name}: " + first_mismatch(g, r)
 
 
+def _lp_tree_case(codes, scales, fmt, block, rank, count, hp_dtype=None):
+    n = len(codes)
+    nb = -(-count // block)
+    dc = [Guarded(count, torch.uint8) for _ in range(n)]
+    ds = [Guarded(nb, torch.float32) for _ in range(n)]
+    hp = None if hp_dtype is None else Guarded(count, TD[hp_dtype])
+    ref_c = [to_host(g.t).copy() for g in dc]
+    ref_s = [to_host(g.t).copy() for g in ds]
+    ref_h = None if hp is None else to_host(hp.t).copy()
+    rx.rx_lp_reduce_scatter_chunk_bcast([to_gpu(c) for c in codes], [to_gpu(s) for s in scales],
+                                        FMTS[fmt], block, rank, [g.t for g in dc], [g.t for g in ds],
+                                        None if hp is None else hp.t, count=count)
+    sync()
+    O.lp_reduce_scatter_chunk_bcast(codes, scales, fmt, block, rank, ref_c, ref_s,
+                                    ref_h, O.FP32 if hp_dtype is None else hp_dtype)
+    for j in range(n):
+        got_c, got_s = to_host(dc[j].t), to_host(ds[j].t)
+        assert bits_equal(got_c, ref_c[j]), f"rank={rank} dst={j} codes: " + first_mismatch(got_c, ref_c[j])
+        assert bits_equal(got_s, ref_s[j]), f"rank={rank} dst={j} scales: " + first_mismatch(got_s, ref_s[j])
+        assert dc[j].guards_intact() and ds[j].guards_intact()
+    if hp is not None:
+        got_h = to_host(hp.t)
+        assert bits_equal(got_h, ref_h), f"rank={rank} hp: " + first_mismatch(got_h, ref_h)
+        assert hp.guards_intact()
+
+
+@pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 256), (O.E4M3, 32), (O.E5M2, 1024)])
+@pytest.mark.parametrize("n", [1, 3, 8, 16])
+def test_lp_tree_shapes(fmt, block, n):
+    for count in [1, 17, block, 3 * block + 5, 20_000, 300_001]:
+        srcs = [G.fill(count, O.FP32, G.NORMAL_OUTLIER, seed=5000 + count, rank=r) for r in range(n)]
+        codes, scales = O.quant_fp8(srcs, O.FP32, fmt, block)
+        for k in range(n):
+            log(f"lp tree fmt={fmt} block={block} n={n} count={count} rank={k}")
+            _lp_tree_case(codes, scales, fmt, block, k, count,
+                          hp_dtype=(O.BF16, None, O.FP32)[k % 3])
+
+
+def test_lp_tree_fp32_workload_all_ranks():
+    """The low-precision tree step on the 8 x 64 MiB FP32 message (E4M3,
+    blocks of 128): each rank's 2,097,152-element chunk (the large variant)."""
+    w = G.WORKLOADS["lp_fp32"]
+    fmt, block = O.FMT[w.fp8], w.block
+    srcs = w.sources()
+    codes, scales = O.quant_fp8(srcs, w.dtype, fmt, block)
+    del srcs
+    for k in range(w.nsrc):
+        log(f"lp tree lp_fp32 rank={k}")
+        _lp_tree_case(codes, scales, fmt, block, k, w.count, hp_dtype=O.FP32 if k == 0 else None)
+
+
 def test_lp_fp32_workload_full():
     """Low-precision allreduce on 8 x 16,777,216 FP32 (N(0,1), 1% outliers
     x100), E4M3, blocks of 128: quant and DRR-REQUANT (+FP32 output)
