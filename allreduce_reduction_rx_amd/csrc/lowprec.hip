@@ -305,7 +305,9 @@ __device__ __forceinline__ void store_hp(void* out, bool bf16, size_t v, size_t 
     }
 }
 
-template <int F, int N, bool REQUANT, int CPL>
+// MULTI: the requantized result goes to a.nout destinations (the
+// low-precision tree step's push); otherwise to out_codes[0] / out_scales[0].
+template <int F, int N, bool REQUANT, int CPL, bool MULTI>
 __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
 {
     const int lane = lane_id();
@@ -364,11 +366,17 @@ __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
         for (int p = 0; p < CPL / 4; ++p)
             q[p] = f32x4_to_fp8<F>(clamp_fmax<F>(S[4 * p + 0] * r2), clamp_fmax<F>(S[4 * p + 1] * r2),
                                    clamp_fmax<F>(S[4 * p + 2] * r2), clamp_fmax<F>(S[4 * p + 3] * r2));
-        for (int j = 0; j < a.nout; ++j)   // push the chunk to every destination
-            store_codes<CPL>(static_cast<uint8_t*>(a.out_codes[j]), v, e, count, whole, q);
-        if (valid && (lane % lpb) == 0)
-            for (int j = 0; j < a.nout; ++j)
-                a.out_scales[j][b] = s2;
+        if constexpr (MULTI) {
+            for (int j = 0; j < a.nout; ++j)   // push the chunk to every destination
+                store_codes<CPL>(static_cast<uint8_t*>(a.out_codes[j]), v, e, count, whole, q);
+            if (valid && (lane % lpb) == 0)
+                for (int j = 0; j < a.nout; ++j)
+                    a.out_scales[j][b] = s2;
+        } else {
+            store_codes<CPL>(static_cast<uint8_t*>(a.out_codes[0]), v, e, count, whole, q);
+            if (valid && (lane % lpb) == 0)
+                a.out_scales[0][b] = s2;
+        }
 
         if (a.out_hp) {
             float h[CPL];
@@ -403,20 +411,22 @@ struct QuantTable {
 const QuantTable<false> kQuantLarge;
 const QuantTable<true> kQuantSmall;
 
-template <int F, bool R, int CPL, int... I>
+template <int F, bool R, int CPL, bool M, int... I>
 constexpr std::array<DrrFn, sizeof...(I)> drr_row(std::integer_sequence<int, I...>)
 {
-    return {{&k_drr<F, I + 1, R, CPL>...}};
+    return {{&k_drr<F, I + 1, R, CPL, M>...}};
 }
 
 template <int CPL>
 struct DrrTable {
-    // [fmt][requant][nsrc - 1]
-    std::array<DrrFn, kMaxSrc> fn[2][2] = {
-        {drr_row<0, false, CPL>(std::make_integer_sequence<int, kMaxSrc>{}),
-         drr_row<0, true, CPL>(std::make_integer_sequence<int, kMaxSrc>{})},
-        {drr_row<1, false, CPL>(std::make_integer_sequence<int, kMaxSrc>{}),
-         drr_row<1, true, CPL>(std::make_integer_sequence<int, kMaxSrc>{})}};
+    // [fmt][0 sum, 1 requant, 2 requant to every destination][nsrc - 1]
+    std::array<DrrFn, kMaxSrc> fn[2][3] = {
+        {drr_row<0, false, CPL, false>(std::make_integer_sequence<int, kMaxSrc>{}),
+         drr_row<0, true, CPL, false>(std::make_integer_sequence<int, kMaxSrc>{}),
+         drr_row<0, true, CPL, true>(std::make_integer_sequence<int, kMaxSrc>{})},
+        {drr_row<1, false, CPL, false>(std::make_integer_sequence<int, kMaxSrc>{}),
+         drr_row<1, true, CPL, false>(std::make_integer_sequence<int, kMaxSrc>{}),
+         drr_row<1, true, CPL, true>(std::make_integer_sequence<int, kMaxSrc>{})}};
 };
 const DrrTable<16> kDrr16;
 const DrrTable<4> kDrr4;
@@ -465,7 +475,7 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     launch_geometry(tiles * kWave, small, policy_drr(), grid, blk);
     DrrArgs arg = a;
     void* params[] = {&arg};
-    const int r = requant ? 1 : 0;
+    const int r = requant ? (a.nout > 1 ? 2 : 1) : 0;
     DrrFn fn = narrow ? kDrr4.fn[fmt][r][nsrc - 1] : kDrr16.fn[fmt][r][nsrc - 1];
     return hipLaunchKernel((const void*)fn, grid, blk, params, 0, s);
 }

@@ -28,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -81,22 +82,18 @@ def sha_of(files):
 
 
 def read_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or
-    None when absent or when the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary
+    (profiles/traffic_<workload>.md), or None when absent or when the
+    kernel's source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
     if not os.path.exists(path):
         return None
-    kv = {}
+    want = sha_of(KERNEL_SOURCES[kernel])
     for line in open(path):
-        if ":" in line and line.startswith("- "):
-            k, v = line[2:].split(":", 1)
-            kv[k.strip()] = v.strip().strip("`")
-    if kv.get("source_sha256") != sha_of(KERNEL_SOURCES[kernel]):
-        return None
-    try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+        m = re.match(r"- (\w+): source_sha256=(\w+) hbm_bytes_per_launch=(\d+)", line.strip())
+        if m and m.group(1) == kernel:
+            return float(m.group(3)) if m.group(2) == want else None
+    return None
 
 
 class Batch:
