@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void k_tree(TreeArgs a)
         u32x4 y = fold_vec<DT, N, false>(a.src, v);
 #pragma unroll
         for (int j = 0; j < N; ++j)
-            st16(a.dst[j], v, y);
+            st16_stream(a.dst[j], v, y);
     }
     // hi is a multiple of VE unless it is the end of a ragged message
     const size_t i = (v1 > v0 ? v1 : v0) * VE + gid;
@@ -148,11 +148,11 @@ const std::array<TreeFn, kMaxSrc> kTree[2] = {
     tree_table<1>(std::make_integer_sequence<int, kMaxSrc>{})};
 
 // One thread per 16-byte output vector. Large messages run one 256-thread
-// workgroup per CU (flat) or two 128-thread ones (tree) with a grid-stride
+// workgroup per CU with a grid-stride
 // loop: on MI355X a narrow window of in-flight addresses measured up to 20%
 // faster than filling every CU with 8 workgroups.
 LaunchPolicy policy_flat() { return {128u, 256u, 1u}; }
-LaunchPolicy policy_tree() { return {64u, 128u, 2u}; }
+LaunchPolicy policy_tree() { return {64u, 256u, 1u}; }
 
 bool small_job(size_t threads) { return threads < kSmallThreadsPerCu * (size_t)device_cu_count(); }
 
