@@ -202,42 +202,53 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a)
 // Dequantize -> FP32 sum -> (requantize)
 // ---------------------------------------------------------------------------
 
-// Each lane owns CPL consecutive codes per rank: CPL = 16 (one dwordx4 per
-// rank) for large messages, CPL = 4 (one dword) for decode-size messages,
-// which gives 4x the waves and a quarter of the per-wave ALU chain.
-template <int CPL>
-struct Codes {
-    uint32_t w[CPL / 4];
+// Lane layout of a wave tile of 64 * CPC * U codes: lane l owns U chunks of
+// CPC consecutive codes, chunk u at tile offset (u * 64 + l) * CPC. Every
+// load and store instruction then covers one contiguous run (64 lanes x CPC
+// codes, or their 2- or 4-byte outputs). Layouts used:
+//   CPC 16, U 1: dwordx4 code loads (any block size);
+//   CPC  8, U 2: BF16 output, 16-byte stores contiguous across the wave;
+//   CPC  4, U 4: FP32 output, 16-byte stores contiguous across the wave;
+//   CPC  4, U 1: decode-size messages (4x the waves, short serial chains).
+// A block spans block / CPC lanes of one chunk; the launcher only picks
+// layouts with block / CPC <= 64.
+template <int CPC>
+struct Chunk {
+    uint32_t w[CPC / 4];
 };
 
-template <int CPL>
-__device__ __forceinline__ Codes<CPL> load_codes(const uint8_t* p, size_t v, size_t e,
+template <int CPC>
+__device__ __forceinline__ Chunk<CPC> load_chunk(const uint8_t* p, size_t c, size_t e,
                                                  size_t count, bool whole)
 {
-    Codes<CPL> c;
+    Chunk<CPC> x;
     if (whole) {
-        if constexpr (CPL == 16) {
-            u32x4 x = ld16_stream(p, v);
+        if constexpr (CPC == 16) {
+            u32x4 v = ld16_stream(p, c);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) c.w[q] = x[q];
+            for (int q = 0; q < 4; ++q) x.w[q] = v[q];
+        } else if constexpr (CPC == 8) {
+            u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p) + c);
+            x.w[0] = v[0];
+            x.w[1] = v[1];
         } else {
-            c.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p) + v);
+            x.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p) + c);
         }
     } else {  // codes [e, count) byte by byte, the rest code 0 (decodes to +0)
 #pragma unroll
-        for (int q = 0; q < CPL / 4; ++q) c.w[q] = 0u;
+        for (int q = 0; q < CPC / 4; ++q) x.w[q] = 0u;
 #pragma unroll
-        for (int k = 0; k < CPL; ++k)
-            if (e + k < count) c.w[k / 4] |= (uint32_t)p[e + k] << (8 * (k & 3));
+        for (int k = 0; k < CPC; ++k)
+            if (e + k < count) x.w[k / 4] |= (uint32_t)p[e + k] << (8 * (k & 3));
     }
-    return c;
+    return x;
 }
 
-template <int F, int CPL>
+template <int F, int CPC>
 __device__ __forceinline__ void dequant(const uint32_t* w, float sc, float* v)
 {
 #pragma unroll
-    for (int q = 0; q < CPL / 4; ++q) {
+    for (int q = 0; q < CPC / 4; ++q) {
         float d[4];
         fp8x4_to_f32<F>(w[q], d);
 #pragma unroll
@@ -246,59 +257,69 @@ __device__ __forceinline__ void dequant(const uint32_t* w, float sc, float* v)
     }
 }
 
-template <int CPL>
-__device__ __forceinline__ void store_codes(uint8_t* p, size_t v, size_t e, size_t count,
+// Code stores are contiguous across the wave: stream past the caches.
+template <int CPC>
+__device__ __forceinline__ void store_codes(uint8_t* p, size_t c, size_t e, size_t count,
                                             bool whole, const uint32_t* w)
 {
-    if (whole) {  // contiguous across the wave: stream past the caches
-        if constexpr (CPL == 16) {
-            u32x4 x = {w[0], w[1], w[2], w[3]};
-            st16_stream(p, v, x);
+    if (whole) {
+        if constexpr (CPC == 16) {
+            u32x4 v = {w[0], w[1], w[2], w[3]};
+            st16_stream(p, c, v);
+        } else if constexpr (CPC == 8) {
+            u32x2 v = {w[0], w[1]};
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p) + c);
         } else {
-            __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(p) + v);
+            __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(p) + c);
         }
     } else {
 #pragma unroll
-        for (int k = 0; k < CPL; ++k)
+        for (int k = 0; k < CPC; ++k)
             if (e + k < count) p[e + k] = (uint8_t)(w[k / 4] >> (8 * (k & 3)));
     }
 }
 
-// High-precision values of elements e .. e + CPL - 1 (lane vector v).
-template <int CPL>
-__device__ __forceinline__ void store_hp(void* out, bool bf16, size_t v, size_t e, size_t count,
+// High-precision values of elements e .. e + CPC - 1 (chunk c). When a lane's
+// output is one 16-byte (or 8-byte) piece, the store instruction covers a
+// contiguous run and streams past the caches; wider outputs are written as
+// strided 16-byte pieces with cached stores, which merge in L2.
+template <int CPC>
+__device__ __forceinline__ void store_hp(void* out, bool bf16, size_t c, size_t e, size_t count,
                                          bool whole, const float* h)
 {
     if (whole) {
         if (bf16) {
-            uint32_t p[CPL / 2];
+            uint32_t p[CPC / 2];
 #pragma unroll
-            for (int i = 0; i < CPL / 2; ++i) p[i] = pack_bf16(h[2 * i], h[2 * i + 1]);
-            // BF16: nontemporal (measured faster); the FP32 output below keeps
-            // cached stores, which merge its four strided 16-byte pieces in L2
-            // (nontemporal there measured 28% slower)
-            if constexpr (CPL == 16) {
-                u32x4 p0 = {p[0], p[1], p[2], p[3]};
-                u32x4 p1 = {p[4], p[5], p[6], p[7]};
-                st16_stream(out, 2 * v, p0);
-                st16_stream(out, 2 * v + 1, p1);
+            for (int i = 0; i < CPC / 2; ++i) p[i] = pack_bf16(h[2 * i], h[2 * i + 1]);
+            if constexpr (CPC == 4) {
+                u32x2 v = {p[0], p[1]};
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(out) + c);
+            } else if constexpr (CPC == 8) {
+                u32x4 v = {p[0], p[1], p[2], p[3]};
+                st16_stream(out, c, v);
             } else {
-                u32x2 p0 = {p[0], p[1]};
-                __builtin_nontemporal_store(p0, reinterpret_cast<u32x2*>(out) + v);
+                u32x4 v0 = {p[0], p[1], p[2], p[3]};
+                u32x4 v1 = {p[4], p[5], p[6], p[7]};
+                st16(out, 2 * c, v0);
+                st16(out, 2 * c + 1, v1);
             }
         } else {
 #pragma unroll
-            for (int q = 0; q < CPL / 4; ++q) {
-                u32x4 x = {__builtin_bit_cast(uint32_t, h[4 * q]),
+            for (int q = 0; q < CPC / 4; ++q) {
+                u32x4 v = {__builtin_bit_cast(uint32_t, h[4 * q]),
                            __builtin_bit_cast(uint32_t, h[4 * q + 1]),
                            __builtin_bit_cast(uint32_t, h[4 * q + 2]),
                            __builtin_bit_cast(uint32_t, h[4 * q + 3])};
-                st16(out, (CPL / 4) * v + q, x);
+                if constexpr (CPC == 4)
+                    st16_stream(out, c, v);
+                else
+                    st16(out, (CPC / 4) * c + q, v);
             }
         }
     } else {
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) {
+        for (int k = 0; k < CPC; ++k) {
             if (e + k < count) {
                 if (bf16)
                     static_cast<uint16_t*>(out)[e + k] = (uint16_t)(pack_bf16(h[k], 0.0f) & 0xFFFFu);
@@ -311,7 +332,7 @@ __device__ __forceinline__ void store_hp(void* out, bool bf16, size_t v, size_t 
 
 // MULTI: the requantized result goes to a.nout destinations (the
 // low-precision tree step's push); otherwise to out_codes[0] / out_scales[0].
-template <int F, int N, bool REQUANT, int CPL, bool MULTI>
+template <int F, int N, bool REQUANT, int CPC, int U, bool MULTI>
 __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
 {
     const int lane = lane_id();
@@ -320,72 +341,84 @@ __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
     const uint32_t wave = blockIdx.x * waves_per_wg + wave_in_wg;
     const uint32_t nwaves = gridDim.x * waves_per_wg;
     const size_t count = a.hi;                                    // end of the range
-    constexpr size_t kTile = (size_t)kWave * CPL;                 // codes per wave tile
+    constexpr size_t kTile = (size_t)kWave * CPC * U;             // codes per wave tile
     const uint32_t ntiles = (uint32_t)((a.hi - a.lo + kTile - 1) / kTile);
-    const size_t v0 = a.lo / CPL;                                 // lo is a block multiple
-    const int lpb = a.block / CPL;                                // lanes per block: 2..64
+    const size_t c0 = a.lo / CPC;                                 // lo is a block multiple
+    const int lpb = a.block / CPC;                                // lanes per block: <= 64
     const int bshift = __builtin_ctz((unsigned)a.block);
 
     for (uint32_t t = wave; t < ntiles; t += nwaves) {
-        const size_t v = v0 + (size_t)t * kWave + lane;  // this lane's CPL-code vector
-        const size_t e = v * CPL;
-        const bool whole = e + CPL <= count;
-        const bool valid = e < count;
-        const size_t b = e >> bshift;
+        size_t c[U], e[U], b[U];
+        bool whole[U], valid[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            c[u] = c0 + ((size_t)t * U + u) * kWave + lane;  // this lane's chunk u
+            e[u] = c[u] * CPC;
+            whole[u] = e[u] + CPC <= count;
+            valid[u] = e[u] < count;
+            b[u] = e[u] >> bshift;
+        }
 
-        Codes<CPL> c[N];
-        float sc[N];
+        Chunk<CPC> x[N][U];
+        float sc[N][U];
 #pragma unroll
         for (int r = 0; r < N; ++r) {
-            c[r] = load_codes<CPL>(static_cast<const uint8_t*>(a.codes[r]), v, e, count, whole);
-            sc[r] = valid ? a.scales[r][b] : 0.0f;
+            const uint8_t* cp = static_cast<const uint8_t*>(a.codes[r]);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                x[r][u] = load_chunk<CPC>(cp, c[u], e[u], count, whole[u]);
+                sc[r][u] = valid[u] ? a.scales[r][b[u]] : 0.0f;
+            }
         }
 
-        float S[CPL];
-        dequant<F, CPL>(c[0].w, sc[0], S);
 #pragma unroll
-        for (int r = 1; r < N; ++r) {
-            float d[CPL];
-            dequant<F, CPL>(c[r].w, sc[r], d);
+        for (int u = 0; u < U; ++u) {
+            float S[CPC];
+            dequant<F, CPC>(x[0][u].w, sc[0][u], S);
 #pragma unroll
-            for (int k = 0; k < CPL; ++k)
-                S[k] = S[k] + d[k];
-        }
+            for (int r = 1; r < N; ++r) {
+                float d[CPC];
+                dequant<F, CPC>(x[r][u].w, sc[r][u], d);
+#pragma unroll
+                for (int k = 0; k < CPC; ++k)
+                    S[k] = S[k] + d[k];
+            }
 
-        if constexpr (!REQUANT) {
-            store_hp<CPL>(a.out_hp, a.hp_bf16 != 0, v, e, count, whole, S);
-            continue;
-        }
+            if constexpr (!REQUANT) {
+                store_hp<CPC>(a.out_hp, a.hp_bf16 != 0, c[u], e[u], count, whole[u], S);
+                continue;
+            }
 
-        // Requantize the FP32 sum with the same block size and format.
-        float m = __builtin_fabsf(S[0]);
+            // Requantize the FP32 sum with the same block size and format.
+            float m = __builtin_fabsf(S[0]);
 #pragma unroll
-        for (int k = 1; k < CPL; ++k)
-            m = __builtin_fmaxf(m, __builtin_fabsf(S[k]));
-        const float A = bits_f32(group_max_rt(__builtin_bit_cast(uint32_t, m), lpb));
-        float s2, r2;
-        block_scale<F>(A, s2, r2);
-        uint32_t q[CPL / 4];
+            for (int k = 1; k < CPC; ++k)
+                m = __builtin_fmaxf(m, __builtin_fabsf(S[k]));
+            const float A = bits_f32(group_max_rt(__builtin_bit_cast(uint32_t, m), lpb));
+            float s2, r2;
+            block_scale<F>(A, s2, r2);
+            uint32_t q[CPC / 4];
 #pragma unroll
-        for (int p = 0; p < CPL / 4; ++p)
-            q[p] = f32x4_to_fp8<F>(clamp_fmax<F>(S[4 * p + 0] * r2), clamp_fmax<F>(S[4 * p + 1] * r2),
-                                   clamp_fmax<F>(S[4 * p + 2] * r2), clamp_fmax<F>(S[4 * p + 3] * r2));
-        if constexpr (MULTI) {
-            for (int j = 0; j < a.nout; ++j)   // push the chunk to every destination
-                store_codes<CPL>(static_cast<uint8_t*>(a.out_codes[j]), v, e, count, whole, q);
-            if (valid && (lane % lpb) == 0)
-                for (int j = 0; j < a.nout; ++j)
-                    a.out_scales[j][b] = s2;
-        } else {
-            store_codes<CPL>(static_cast<uint8_t*>(a.out_codes[0]), v, e, count, whole, q);
-            if (valid && (lane % lpb) == 0)
-                a.out_scales[0][b] = s2;
-        }
+            for (int p = 0; p < CPC / 4; ++p)
+                q[p] = f32x4_to_fp8<F>(clamp_fmax<F>(S[4 * p + 0] * r2), clamp_fmax<F>(S[4 * p + 1] * r2),
+                                       clamp_fmax<F>(S[4 * p + 2] * r2), clamp_fmax<F>(S[4 * p + 3] * r2));
+            if constexpr (MULTI) {
+                for (int j = 0; j < a.nout; ++j)   // push the chunk to every destination
+                    store_codes<CPC>(static_cast<uint8_t*>(a.out_codes[j]), c[u], e[u], count, whole[u], q);
+                if (valid[u] && (lane % lpb) == 0)
+                    for (int j = 0; j < a.nout; ++j)
+                        a.out_scales[j][b[u]] = s2;
+            } else {
+                store_codes<CPC>(static_cast<uint8_t*>(a.out_codes[0]), c[u], e[u], count, whole[u], q);
+                if (valid[u] && (lane % lpb) == 0)
+                    a.out_scales[0][b[u]] = s2;
+            }
 
-        if (a.out_hp) {
-            float h[CPL];
-            dequant<F, CPL>(q, s2, h);
-            store_hp<CPL>(a.out_hp, a.hp_bf16 != 0, v, e, count, whole, h);
+            if (a.out_hp) {
+                float h[CPC];
+                dequant<F, CPC>(q, s2, h);
+                store_hp<CPC>(a.out_hp, a.hp_bf16 != 0, c[u], e[u], count, whole[u], h);
+            }
         }
     }
 }
@@ -415,25 +448,27 @@ struct QuantTable {
 const QuantTable<false> kQuantLarge;
 const QuantTable<true> kQuantSmall;
 
-template <int F, bool R, int CPL, bool M, int... I>
+template <int F, bool R, int CPC, int U, bool M, int... I>
 constexpr std::array<DrrFn, sizeof...(I)> drr_row(std::integer_sequence<int, I...>)
 {
-    return {{&k_drr<F, I + 1, R, CPL, M>...}};
+    return {{&k_drr<F, I + 1, R, CPC, U, M>...}};
 }
 
-template <int CPL>
+template <int CPC, int U>
 struct DrrTable {
     // [fmt][0 sum, 1 requant, 2 requant to every destination][nsrc - 1]
     std::array<DrrFn, kMaxSrc> fn[2][3] = {
-        {drr_row<0, false, CPL, false>(std::make_integer_sequence<int, kMaxSrc>{}),
-         drr_row<0, true, CPL, false>(std::make_integer_sequence<int, kMaxSrc>{}),
-         drr_row<0, true, CPL, true>(std::make_integer_sequence<int, kMaxSrc>{})},
-        {drr_row<1, false, CPL, false>(std::make_integer_sequence<int, kMaxSrc>{}),
-         drr_row<1, true, CPL, false>(std::make_integer_sequence<int, kMaxSrc>{}),
-         drr_row<1, true, CPL, true>(std::make_integer_sequence<int, kMaxSrc>{})}};
+        {drr_row<0, false, CPC, U, false>(std::make_integer_sequence<int, kMaxSrc>{}),
+         drr_row<0, true, CPC, U, false>(std::make_integer_sequence<int, kMaxSrc>{}),
+         drr_row<0, true, CPC, U, true>(std::make_integer_sequence<int, kMaxSrc>{})},
+        {drr_row<1, false, CPC, U, false>(std::make_integer_sequence<int, kMaxSrc>{}),
+         drr_row<1, true, CPC, U, false>(std::make_integer_sequence<int, kMaxSrc>{}),
+         drr_row<1, true, CPC, U, true>(std::make_integer_sequence<int, kMaxSrc>{})}};
 };
-const DrrTable<16> kDrr16;
-const DrrTable<4> kDrr4;
+const DrrTable<16, 1> kDrr16x1;
+const DrrTable<8, 2> kDrr8x2;
+const DrrTable<4, 4> kDrr4x4;
+const DrrTable<4, 1> kDrr4x1;
 
 // One wave per tile (64 threads per work item). Large messages: 256-thread
 // workgroups, at most 2 per CU (a narrow HBM access window measured best on
@@ -472,15 +507,26 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     const size_t cus = (size_t)device_cu_count();
     const size_t len = a.hi - a.lo;
     const bool small = (len + 1023) / 1024 < kSmallTilesPerCu * cus / 2;
-    const bool narrow = small && a.block <= 256;   // 4 codes per lane
-    const size_t tile = narrow ? 256 : 1024;
+    const bool fp32_out = a.out_hp != nullptr && !a.hp_bf16;
+    // chunk layout (codes per lane per chunk, chunks per lane); block / CPC <= 64
+    int cpc = 16, u = 1;
+    if (small) {
+        if (a.block <= 256) cpc = 4;
+    } else if (fp32_out) {
+        if (a.block <= 256) { cpc = 4; u = 4; }
+    } else if (a.block <= 512) {
+        cpc = 8;
+        u = 2;
+    }
+    const size_t tile = (size_t)kWave * cpc * u;
     const size_t tiles = (len + tile - 1) / tile;
     dim3 grid, blk;
     launch_geometry(tiles * kWave, small, policy_drr(), grid, blk);
     DrrArgs arg = a;
     void* params[] = {&arg};
     const int r = requant ? (a.nout > 1 ? 2 : 1) : 0;
-    DrrFn fn = narrow ? kDrr4.fn[fmt][r][nsrc - 1] : kDrr16.fn[fmt][r][nsrc - 1];
+    const DrrFn fn = cpc == 4 ? (u == 4 ? kDrr4x4.fn[fmt][r][nsrc - 1] : kDrr4x1.fn[fmt][r][nsrc - 1])
+                   : cpc == 8 ? kDrr8x2.fn[fmt][r][nsrc - 1] : kDrr16x1.fn[fmt][r][nsrc - 1];
     return hipLaunchKernel((const void*)fn, grid, blk, params, 0, s);
 }
 

@@ -270,21 +270,37 @@ def test_drr_shapes(fmt, block, n):
                     assert bits_equal(g, r), f"{name} count={count}: " + first_mismatch(g, r)
 
 
-@pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 256), (O.E4M3, 32)])
+@pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 256), (O.E4M3, 32),
+                                       (O.E5M2, 512), (O.E4M3, 1024)])
 def test_drr_large_variant_ragged(fmt, block):
-    # > 1024 tiles of 1024 codes: the 16-codes-per-lane kernel, grid-stride,
-    # ragged tail and partial last block
+    # > 1024 tiles of 1024 codes: the grid-stride kernels in every chunk
+    # layout (16 codes x 1, 8 x 2 for BF16 / code-only output, 4 x 4 for FP32
+    # output), ragged tail and partial last block
     n, count = 4, (1 << 21) + 7
     srcs = [G.fill(count, O.FP32, G.LAPLACE, seed=4500 + block, rank=r) for r in range(n)]
     codes, scales = O.quant_fp8(srcs, O.FP32, fmt, block)
-    for mode, hp_dtype, want_hp in ((O.DRR_SUM, O.BF16, True), (O.DRR_REQUANT, O.FP32, True)):
-        log(f"drr large variant fmt={fmt} block={block} mode={mode}")
+    for mode, hp_dtype, want_hp in ((O.DRR_SUM, O.BF16, True), (O.DRR_SUM, O.FP32, True),
+                                    (O.DRR_REQUANT, O.FP32, False), (O.DRR_REQUANT, O.BF16, True),
+                                    (O.DRR_REQUANT, O.FP32, True)):
+        log(f"drr large variant fmt={fmt} block={block} mode={mode} hp={hp_dtype}/{want_hp}")
         got = _drr_gpu(codes, scales, fmt, block, mode, hp_dtype, want_hp, count)
         ref = O.dequant_reduce_requant(codes, scales, fmt, block, mode, hp_dtype, want_hp)
         for name, g, r in zip(("codes", "scales", "hp"), got, ref):
             assert (g is None) == (r is None)
             if g is not None:
                 assert bits_equal(g, r), f"{name}: " + first_mismatch(g, r)
+
+
+@pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 512)])
+def test_lp_tree_large_variant_ragged(fmt, block):
+    # chunks above the decode-size threshold, ragged message end
+    n, count = 3, 3 * (1 << 21) + 5
+    srcs = [G.fill(count, O.FP32, G.NORMAL_OUTLIER, seed=5500 + block, rank=r) for r in range(n)]
+    codes, scales = O.quant_fp8(srcs, O.FP32, fmt, block)
+    for k in range(n):
+        log(f"lp tree large variant fmt={fmt} block={block} rank={k}")
+        _lp_tree_case(codes, scales, fmt, block, k, count,
+                      hp_dtype=(O.BF16, None, O.FP32)[k % 3])
 
 
 def _lp_tree_case(codes, scales, fmt, block, rank, count, hp_dtype=None):
