@@ -1,0 +1,46 @@
+// drr.hip -- launch of the dequantize-reduce-requantize kernel (drr.hpp):
+// lane layout and launch geometry by message size and output type.
+#include "drr.hpp"
+
+namespace rx {
+namespace {
+
+// One wave per tile (64 threads per work item). Large messages: 256-thread
+// workgroups, at most 2 per CU (a narrow HBM access window measured best on
+// MI355X); decode-size messages: one tile per wave over every CU.
+LaunchPolicy policy_drr() { return {64u, 256u, 2u}; }
+
+}  // namespace
+
+hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStream_t s)
+{
+    const size_t cus = (size_t)device_cu_count();
+    const size_t len = a.hi - a.lo;
+    const bool small = (len + 1023) / 1024 < kSmallTilesPerCu * cus / 2;
+    const bool fp32_out = a.out_hp != nullptr && !a.hp_bf16;
+    // chunk layout (codes per lane per chunk, chunks per lane); block / CPC <= 64
+    int cpc = 16, u = 1;
+    if (small) {
+        if (a.block <= 256) cpc = 4;
+    } else if (fp32_out) {
+        if (a.block <= 256) { cpc = 4; u = 4; }
+    } else if (a.block <= 512) {
+        cpc = 8;
+        u = 2;
+    }
+    const size_t tile = (size_t)kWave * cpc * u;
+    const size_t tiles = (len + tile - 1) / tile;
+    dim3 grid, blk;
+    launch_geometry(tiles * kWave, small, policy_drr(), grid, blk);
+    DrrArgs arg = a;
+    // decode-size: one tile per wave, and the waves sharing a scale line on
+    // one XCD (measured 8% faster); large messages keep the plain order
+    arg.xcd_ranges = small ? 1 : 0;
+    void* params[] = {&arg};
+    const int r = requant ? (a.nout > 1 ? 2 : 1) : 0;
+    const DrrFn fn = cpc == 4 ? (u == 4 ? drr_fns_4x4().fn[fmt][r][nsrc - 1] : drr_fns_4x1().fn[fmt][r][nsrc - 1])
+                   : cpc == 8 ? drr_fns_8x2().fn[fmt][r][nsrc - 1] : drr_fns_16x1().fn[fmt][r][nsrc - 1];
+    return hipLaunchKernel((const void*)fn, grid, blk, params, 0, s);
+}
+
+}  // namespace rx

@@ -1,0 +1,278 @@
+// drr.hpp -- the fused dequantize -> FP32 sum -> requantize kernel of the
+// low-precision collectives on gfx950 (RCCLX article, code-journey.com,
+// "Core feature 2: Low-Precision Collectives": FP8 on the wire, "Compute
+// precision" FP32). One kernel template serves rx_dequant_reduce_requant
+// (one destination) and rx_lp_reduce_scatter_chunk_bcast (the requantized
+// chunk pushed to every destination). Each lane layout is instantiated in a
+// translation unit of its own (drr_<CPC>x<U>.hip) so the build compiles them
+// in parallel.
+#pragma once
+
+#include <array>
+#include <utility>
+
+#include "rx_device.hpp"
+#include "rx_internal.hpp"
+
+namespace rx {
+
+using DrrFn = void (*)(DrrArgs);
+
+// [fmt][0 sum, 1 requant, 2 requant to every destination][nsrc - 1]
+struct DrrFns {
+    DrrFn fn[2][3][kMaxSrc];
+};
+
+const DrrFns& drr_fns_16x1();
+const DrrFns& drr_fns_8x2();
+const DrrFns& drr_fns_4x4();
+const DrrFns& drr_fns_4x1();
+
+namespace drr_detail {
+
+
+// Lane layout of a wave tile of 64 * CPC * U codes: lane l owns U chunks of
+// CPC consecutive codes, chunk u at tile offset (u * 64 + l) * CPC. Every
+// load and store instruction then covers one contiguous run (64 lanes x CPC
+// codes, or their 2- or 4-byte outputs). Layouts used:
+//   CPC 16, U 1: dwordx4 code loads (any block size);
+//   CPC  8, U 2: BF16 output, 16-byte stores contiguous across the wave;
+//   CPC  4, U 4: FP32 output, 16-byte stores contiguous across the wave;
+//   CPC  4, U 1: decode-size messages (4x the waves, short serial chains).
+// A block spans block / CPC lanes of one chunk; the launcher only picks
+// layouts with block / CPC <= 64.
+template <int CPC>
+struct Chunk {
+    uint32_t w[CPC / 4];
+};
+
+template <int CPC>
+__device__ __forceinline__ Chunk<CPC> load_chunk(const uint8_t* p, size_t c, size_t e,
+                                                 size_t count, bool whole)
+{
+    Chunk<CPC> x;
+    if (whole) {
+        if constexpr (CPC == 16) {
+            u32x4 v = ld16_stream(p, c);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x.w[q] = v[q];
+        } else if constexpr (CPC == 8) {
+            u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p) + c);
+            x.w[0] = v[0];
+            x.w[1] = v[1];
+        } else {
+            x.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p) + c);
+        }
+    } else {  // codes [e, count) byte by byte, the rest code 0 (decodes to +0)
+#pragma unroll
+        for (int q = 0; q < CPC / 4; ++q) x.w[q] = 0u;
+#pragma unroll
+        for (int k = 0; k < CPC; ++k)
+            if (e + k < count) x.w[k / 4] |= (uint32_t)p[e + k] << (8 * (k & 3));
+    }
+    return x;
+}
+
+template <int F, int CPC>
+__device__ __forceinline__ void dequant(const uint32_t* w, float sc, float* v)
+{
+#pragma unroll
+    for (int q = 0; q < CPC / 4; ++q) {
+        float d[4];
+        fp8x4_to_f32<F>(w[q], d);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            v[4 * q + k] = d[k] * sc;
+    }
+}
+
+// Code stores are contiguous across the wave: stream past the caches.
+template <int CPC>
+__device__ __forceinline__ void store_codes(uint8_t* p, size_t c, size_t e, size_t count,
+                                            bool whole, const uint32_t* w)
+{
+    if (whole) {
+        if constexpr (CPC == 16) {
+            u32x4 v = {w[0], w[1], w[2], w[3]};
+            st16_stream(p, c, v);
+        } else if constexpr (CPC == 8) {
+            u32x2 v = {w[0], w[1]};
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p) + c);
+        } else {
+            __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(p) + c);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < CPC; ++k)
+            if (e + k < count) p[e + k] = (uint8_t)(w[k / 4] >> (8 * (k & 3)));
+    }
+}
+
+// High-precision values of elements e .. e + CPC - 1 (chunk c). When a lane's
+// output is one 16-byte (or 8-byte) piece, the store instruction covers a
+// contiguous run and streams past the caches; wider outputs are written as
+// strided 16-byte pieces with cached stores, which merge in L2.
+template <int CPC>
+__device__ __forceinline__ void store_hp(void* out, bool bf16, size_t c, size_t e, size_t count,
+                                         bool whole, const float* h)
+{
+    if (whole) {
+        if (bf16) {
+            uint32_t p[CPC / 2];
+#pragma unroll
+            for (int i = 0; i < CPC / 2; ++i) p[i] = pack_bf16(h[2 * i], h[2 * i + 1]);
+            if constexpr (CPC == 4) {
+                u32x2 v = {p[0], p[1]};
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(out) + c);
+            } else if constexpr (CPC == 8) {
+                u32x4 v = {p[0], p[1], p[2], p[3]};
+                st16_stream(out, c, v);
+            } else {
+                u32x4 v0 = {p[0], p[1], p[2], p[3]};
+                u32x4 v1 = {p[4], p[5], p[6], p[7]};
+                st16(out, 2 * c, v0);
+                st16(out, 2 * c + 1, v1);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < CPC / 4; ++q) {
+                u32x4 v = {__builtin_bit_cast(uint32_t, h[4 * q]),
+                           __builtin_bit_cast(uint32_t, h[4 * q + 1]),
+                           __builtin_bit_cast(uint32_t, h[4 * q + 2]),
+                           __builtin_bit_cast(uint32_t, h[4 * q + 3])};
+                if constexpr (CPC == 4)
+                    st16_stream(out, c, v);
+                else
+                    st16(out, (CPC / 4) * c + q, v);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < CPC; ++k) {
+            if (e + k < count) {
+                if (bf16)
+                    static_cast<uint16_t*>(out)[e + k] = (uint16_t)(pack_bf16(h[k], 0.0f) & 0xFFFFu);
+                else
+                    static_cast<float*>(out)[e + k] = h[k];
+            }
+        }
+    }
+}
+
+// MULTI: the requantized result goes to a.nout destinations (the
+// low-precision tree step's push); otherwise to out_codes[0] / out_scales[0].
+template <int F, int N, bool REQUANT, int CPC, int U, bool MULTI>
+__global__ __launch_bounds__(256) void k_drr(DrrArgs a)
+{
+    const int lane = lane_id();
+    const uint32_t wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t waves_per_wg = blockDim.x / kWave;
+    const uint32_t wg = a.xcd_ranges ? xcd_contiguous(blockIdx.x, gridDim.x) : blockIdx.x;
+    const uint32_t wave = wg * waves_per_wg + wave_in_wg;
+    const uint32_t nwaves = gridDim.x * waves_per_wg;
+    const size_t count = a.hi;                                    // end of the range
+    constexpr size_t kTile = (size_t)kWave * CPC * U;             // codes per wave tile
+    const uint32_t ntiles = (uint32_t)((a.hi - a.lo + kTile - 1) / kTile);
+    const size_t c0 = a.lo / CPC;                                 // lo is a block multiple
+    const int lpb = a.block / CPC;                                // lanes per block: <= 64
+    const int bshift = __builtin_ctz((unsigned)a.block);
+
+    for (uint32_t t = wave; t < ntiles; t += nwaves) {
+        size_t c[U], e[U], b[U];
+        bool whole[U], valid[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            c[u] = c0 + ((size_t)t * U + u) * kWave + lane;  // this lane's chunk u
+            e[u] = c[u] * CPC;
+            whole[u] = e[u] + CPC <= count;
+            valid[u] = e[u] < count;
+            b[u] = e[u] >> bshift;
+        }
+
+        Chunk<CPC> x[N][U];
+        float sc[N][U];
+#pragma unroll
+        for (int r = 0; r < N; ++r) {
+            const uint8_t* cp = static_cast<const uint8_t*>(a.codes[r]);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                x[r][u] = load_chunk<CPC>(cp, c[u], e[u], count, whole[u]);
+                sc[r][u] = valid[u] ? a.scales[r][b[u]] : 0.0f;
+            }
+        }
+
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float S[CPC];
+            dequant<F, CPC>(x[0][u].w, sc[0][u], S);
+#pragma unroll
+            for (int r = 1; r < N; ++r) {
+                float d[CPC];
+                dequant<F, CPC>(x[r][u].w, sc[r][u], d);
+#pragma unroll
+                for (int k = 0; k < CPC; ++k)
+                    S[k] = S[k] + d[k];
+            }
+
+            if constexpr (!REQUANT) {
+                store_hp<CPC>(a.out_hp, a.hp_bf16 != 0, c[u], e[u], count, whole[u], S);
+                continue;
+            }
+
+            // Requantize the FP32 sum with the same block size and format.
+            float m = __builtin_fabsf(S[0]);
+#pragma unroll
+            for (int k = 1; k < CPC; ++k)
+                m = __builtin_fmaxf(m, __builtin_fabsf(S[k]));
+            const float A = bits_f32(group_max_rt(__builtin_bit_cast(uint32_t, m), lpb));
+            float s2, r2;
+            block_scale<F>(A, s2, r2);
+            uint32_t q[CPC / 4];
+#pragma unroll
+            for (int p = 0; p < CPC / 4; ++p)
+                q[p] = f32x4_to_fp8<F>(clamp_fmax<F>(S[4 * p + 0] * r2), clamp_fmax<F>(S[4 * p + 1] * r2),
+                                       clamp_fmax<F>(S[4 * p + 2] * r2), clamp_fmax<F>(S[4 * p + 3] * r2));
+            if constexpr (MULTI) {
+                for (int j = 0; j < a.nout; ++j)   // push the chunk to every destination
+                    store_codes<CPC>(static_cast<uint8_t*>(a.out_codes[j]), c[u], e[u], count, whole[u], q);
+                if (valid[u] && (lane % lpb) == 0)
+                    for (int j = 0; j < a.nout; ++j)
+                        a.out_scales[j][b[u]] = s2;
+            } else {
+                store_codes<CPC>(static_cast<uint8_t*>(a.out_codes[0]), c[u], e[u], count, whole[u], q);
+                if (valid[u] && (lane % lpb) == 0)
+                    a.out_scales[0][b[u]] = s2;
+            }
+
+            if (a.out_hp) {
+                float h[CPC];
+                dequant<F, CPC>(q, s2, h);
+                store_hp<CPC>(a.out_hp, a.hp_bf16 != 0, c[u], e[u], count, whole[u], h);
+            }
+        }
+    }
+}
+
+
+template <int F, bool R, int CPC, int U, bool M, int... I>
+void fill_row(DrrFn* row, std::integer_sequence<int, I...>)
+{
+    ((row[I] = &k_drr<F, I + 1, R, CPC, U, M>), ...);
+}
+
+template <int CPC, int U>
+DrrFns make_fns()
+{
+    DrrFns t{};
+    const auto seq = std::make_integer_sequence<int, kMaxSrc>{};
+    fill_row<0, false, CPC, U, false>(t.fn[0][0], seq);
+    fill_row<0, true, CPC, U, false>(t.fn[0][1], seq);
+    fill_row<0, true, CPC, U, true>(t.fn[0][2], seq);
+    fill_row<1, false, CPC, U, false>(t.fn[1][0], seq);
+    fill_row<1, true, CPC, U, false>(t.fn[1][1], seq);
+    fill_row<1, true, CPC, U, true>(t.fn[1][2], seq);
+    return t;
+}
+
+}  // namespace drr_detail
+}  // namespace rx

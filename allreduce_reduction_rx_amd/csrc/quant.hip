@@ -1,0 +1,248 @@
+// quant.hip -- FP32/BF16 -> OCP FP8 block quantizer on gfx950, the sender
+// side of the low-precision collectives (RCCLX article, code-journey.com,
+// "Core feature 2: Low-Precision Collectives": FP8 quantization with up to
+// 4:1 compression; table row "Data types").
+//
+// Encoding (a reading; the pages give only "FP8"): one FP32 scale per block
+// of B elements, s = A / FMAX with A the block absmax; elements multiplied
+// by r = FMAX / A, clamped to +-FMAX and converted with round-to-nearest-even
+// on the hardware converters (v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32).
+//
+// One streaming pass with no LDS: every load is a coalesced 16-byte load
+// (lane l of a wave reads vector base + l), the block absmax is reduced
+// across the lanes that hold the block with DPP and permlane swaps, and each
+// lane stores its own codes.
+#include <array>
+#include <utility>
+
+#include "rx_device.hpp"
+#include "rx_internal.hpp"
+
+namespace rx {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Quantizer
+// ---------------------------------------------------------------------------
+
+// A wave processes tiles of U loads per lane (U x 1 KiB per tile): U = 4 for
+// large messages (more bytes in flight per wave), U = the loads per block
+// (usually 1) for decode-size messages (4x the waves, shorter serial chains).
+template <int DT, int F, int BLOCK, int U>
+struct QuantShape {
+    static constexpr int kVE = DT == 0 ? 4 : 8;          // elements per 16-B vector
+    static constexpr int kLanesRaw = BLOCK / kVE;        // vectors per block
+    static constexpr int kLPB = kLanesRaw < 64 ? kLanesRaw : 64;  // lanes per block
+    static constexpr int kUPB = kLanesRaw / kLPB;        // loads per block (1, 2, 4)
+    static constexpr int kU = U;                         // loads per lane per tile
+    static constexpr int kTileVec = kWave * kU;
+    static constexpr int kTileElems = kTileVec * kVE;
+    static_assert(kU % kUPB == 0, "a tile holds whole blocks");
+    static_assert(kLanesRaw >= 1, "block of at least one vector");
+};
+
+template <int DT, int BLOCK>
+constexpr int loads_per_block()
+{
+    constexpr int lanes = BLOCK / (DT == 0 ? 4 : 8);
+    return lanes <= 64 ? 1 : lanes / 64;
+}
+
+// Widen vector x (16 bytes) to kVE floats.
+template <int DT>
+__device__ __forceinline__ void widen(const u32x4& x, float* f)
+{
+    if constexpr (DT == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) f[k] = bits_f32(x[k]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            f[2 * k] = bf16_lo(x[k]);
+            f[2 * k + 1] = bf16_hi(x[k]);
+        }
+    }
+}
+
+// Partial vector at the end of a ragged source: elements [e, count) loaded
+// one by one, the rest zero (zero is neutral for the absmax).
+template <int DT>
+__device__ __forceinline__ u32x4 load_partial(const void* src, size_t e, size_t count)
+{
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if constexpr (DT == 0) {
+        const uint32_t* p = static_cast<const uint32_t*>(src);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (e + k < count) x[k] = p[e + k];
+    } else {
+        const uint16_t* p = static_cast<const uint16_t*>(src);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (e + k < count) x[k / 2] |= (uint32_t)p[e + k] << (16 * (k & 1));
+    }
+    return x;
+}
+
+template <int DT, int F, int BLOCK, int UL>
+__global__ __launch_bounds__(256) void k_quant(QuantArgs a)
+{
+    using Sh = QuantShape<DT, F, BLOCK, UL>;
+    constexpr int VE = Sh::kVE, U = Sh::kU, LPB = Sh::kLPB, UPB = Sh::kUPB;
+    const int lane = lane_id();
+    const uint32_t wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t waves_per_wg = blockDim.x / kWave;
+    const uint32_t wave = blockIdx.x * waves_per_wg + wave_in_wg;
+    const uint32_t nwaves = gridDim.x * waves_per_wg;
+    const uint32_t tiles_per_src = (uint32_t)((a.count + Sh::kTileElems - 1) / Sh::kTileElems);
+    const uint32_t total = tiles_per_src * (uint32_t)a.nsrc;
+
+    for (uint32_t t = wave; t < total; t += nwaves) {
+        const uint32_t j = t / tiles_per_src;
+        const uint32_t tile = t - j * tiles_per_src;
+        const void* src = a.src[j];
+        uint8_t* codes = static_cast<uint8_t*>(a.codes[j]);
+        float* scales = a.scales[j];
+        const size_t e0 = (size_t)tile * Sh::kTileElems;   // first element of the tile
+        const size_t v0 = e0 / VE;
+        const bool full = e0 + Sh::kTileElems <= a.count;
+
+        u32x4 x[U];
+        if (full) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                x[u] = ld16_stream(src, v0 + u * kWave + lane);
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const size_t e = (v0 + u * kWave + lane) * VE;
+                if (e + VE <= a.count)
+                    x[u] = ld16(src, v0 + u * kWave + lane);
+                else
+                    x[u] = load_partial<DT>(src, e, a.count);
+            }
+        }
+
+        float f[U][VE];
+        float amax[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            widen<DT>(x[u], f[u]);
+            float m = __builtin_fabsf(f[u][0]);
+#pragma unroll
+            for (int k = 1; k < VE; ++k)
+                m = __builtin_fmaxf(m, __builtin_fabsf(f[u][k]));
+            amax[u] = m;
+        }
+
+        // Block absmax across the lanes (and loads) that hold the block.
+        float s[U], r[U];
+        if constexpr (UPB == 1) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float A = bits_f32(group_max<LPB>(__builtin_bit_cast(uint32_t, amax[u])));
+                block_scale<F>(A, s[u], r[u]);
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < U / UPB; ++g) {
+                float m = amax[g * UPB];
+#pragma unroll
+                for (int q = 1; q < UPB; ++q)
+                    m = __builtin_fmaxf(m, amax[g * UPB + q]);
+                float A = bits_f32(group_max<64>(__builtin_bit_cast(uint32_t, m)));
+                float sg, rg;
+                block_scale<F>(A, sg, rg);
+#pragma unroll
+                for (int q = 0; q < UPB; ++q) {
+                    s[g * UPB + q] = sg;
+                    r[g * UPB + q] = rg;
+                }
+            }
+        }
+
+        // Encode and store: VE codes per lane per load (4 or 8 bytes).
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            uint32_t w[VE / 4];
+#pragma unroll
+            for (int q = 0; q < VE / 4; ++q) {
+                float y0 = clamp_fmax<F>(f[u][4 * q + 0] * r[u]);
+                float y1 = clamp_fmax<F>(f[u][4 * q + 1] * r[u]);
+                float y2 = clamp_fmax<F>(f[u][4 * q + 2] * r[u]);
+                float y3 = clamp_fmax<F>(f[u][4 * q + 3] * r[u]);
+                w[q] = f32x4_to_fp8<F>(y0, y1, y2, y3);
+            }
+            const size_t vi = v0 + u * kWave + lane;
+            const size_t e = vi * VE;
+            if (full || e + VE <= a.count) {
+                // contiguous across the wave: stream past the caches
+                if constexpr (VE == 4) {
+                    __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(codes) + vi);
+                } else {
+                    u32x2 p = {w[0], w[1]};
+                    __builtin_nontemporal_store(p, reinterpret_cast<u32x2*>(codes) + vi);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < VE; ++k)
+                    if (e + k < a.count)
+                        codes[e + k] = (uint8_t)(w[k / 4] >> (8 * (k & 3)));
+            }
+            // one lane per block writes the scale
+            const bool leader = UPB == 1 ? (lane % LPB) == 0 : (lane == 0 && u % UPB == 0);
+            if (leader && e < a.count)
+                scales[e / BLOCK] = s[u];
+        }
+    }
+}
+
+
+using QuantFn = void (*)(QuantArgs);
+
+template <int DT, int F, bool SMALL, int... L>
+constexpr std::array<QuantFn, sizeof...(L)> quant_row(std::integer_sequence<int, L...>)
+{
+    return {{&k_quant<DT, F, (32 << L), SMALL ? loads_per_block<DT, (32 << L)>() : 4>...}};
+}
+
+template <bool SMALL>
+struct QuantTable {
+    // [src dtype][fmt][log2(block) - 5]
+    std::array<QuantFn, 6> fn[2][2] = {
+        {quant_row<0, 0, SMALL>(std::make_integer_sequence<int, 6>{}),
+         quant_row<0, 1, SMALL>(std::make_integer_sequence<int, 6>{})},
+        {quant_row<1, 0, SMALL>(std::make_integer_sequence<int, 6>{}),
+         quant_row<1, 1, SMALL>(std::make_integer_sequence<int, 6>{})}};
+};
+const QuantTable<false> kQuantLarge;
+const QuantTable<true> kQuantSmall;
+
+// One wave per tile (64 threads per work item). Large messages: 256-thread
+// workgroups, at most 2 per CU (a narrow HBM access window measured best on
+// MI355X); decode-size messages: one tile per wave over every CU.
+LaunchPolicy policy_quant() { return {256u, 256u, 2u}; }
+
+}  // namespace
+
+hipError_t launch_quant(const QuantArgs& a, int src_dtype, int fmt, int block, hipStream_t s)
+{
+    const int lb = __builtin_ctz((unsigned)block) - 5;
+    const size_t vec_elems = src_dtype == 0 ? 4 : 8;
+    const size_t cus = (size_t)device_cu_count();
+    const size_t large_tiles = (a.count + 4 * 64 * vec_elems - 1) / (4 * 64 * vec_elems) * (size_t)a.nsrc;
+    const bool small = large_tiles < kSmallTilesPerCu * cus;
+    // loads per tile of the chosen variant
+    size_t lanes_per_block = (size_t)block / vec_elems;
+    size_t u = small ? (lanes_per_block <= 64 ? 1 : lanes_per_block / 64) : 4;
+    const size_t tile_elems = u * 64 * vec_elems;
+    const size_t tiles = (a.count + tile_elems - 1) / tile_elems * (size_t)a.nsrc;
+    dim3 grid, blk;
+    launch_geometry(tiles * kWave, small, policy_quant(), grid, blk);
+    QuantArgs arg = a;
+    void* params[] = {&arg};
+    QuantFn fn = small ? kQuantSmall.fn[src_dtype][fmt][lb] : kQuantLarge.fn[src_dtype][fmt][lb];
+    return hipLaunchKernel((const void*)fn, grid, blk, params, 0, s);
+}
+
+}  // namespace rx

@@ -179,4 +179,17 @@ __device__ __forceinline__ float bits_f32(uint32_t u) { return __builtin_bit_cas
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
+// MI355X dispatches workgroup b to XCD b % 8, and each XCD has its own L2.
+// Renumber workgroups so that each XCD owns one contiguous range of the g
+// workgroup ids (a bijection on [0, g)); data shared by neighbouring tiles
+// (a cache line of block scales) is then fetched once per XCD range instead
+// of once per XCD.
+constexpr uint32_t kXcds = 8;
+
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t g)
+{
+    const uint32_t q = g / kXcds, r = g % kXcds, x = b % kXcds, i = b / kXcds;
+    return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
 }  // namespace rx

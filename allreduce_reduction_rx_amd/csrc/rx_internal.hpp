@@ -42,6 +42,7 @@ struct DrrArgs {
     int nout;                    // REQUANT: destinations that receive the result
     int block;                   // elements per scale block
     int hp_bf16;                 // out_hp element type: 1 = BF16, 0 = FP32
+    int xcd_ranges;              // 1: each XCD takes a contiguous range of tiles
 };
 
 // Launch geometry helper: number of compute units of the current device
@@ -62,6 +63,10 @@ struct LaunchPolicy {
 
 // Jobs below this many threads per CU count as decode-size.
 constexpr size_t kSmallThreadsPerCu = 512;
+
+// Quantizer and dequant-reduce-requant: below this many large-variant wave
+// tiles per CU a message counts as decode-size and takes the narrow variant.
+constexpr size_t kSmallTilesPerCu = 8;
 
 void launch_geometry(size_t threads, bool small, const LaunchPolicy& p, dim3& grid, dim3& block);
 

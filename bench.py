@@ -41,9 +41,9 @@ METRIC = "effective HBM GB/s (% of MI355X peak) per reduce kernel; µs at 512 KB
 KERNEL_SOURCES = {
     "reduce_flat": ["reduce.hip", "rx_device.hpp"],
     "tree_step": ["reduce.hip", "rx_device.hpp"],
-    "quant_fp8": ["lowprec.hip", "rx_device.hpp"],
-    "dequant_reduce_requant": ["lowprec.hip", "rx_device.hpp"],
-    "lp_tree_step": ["lowprec.hip", "rx_device.hpp"],
+    "quant_fp8": ["quant.hip", "rx_device.hpp"],
+    "dequant_reduce_requant": ["drr.hpp", "drr.hip", "rx_device.hpp"],
+    "lp_tree_step": ["drr.hpp", "drr.hip", "rx_device.hpp"],
 }
 # rocprofv3 kernel names (substrings of the mangled names)
 KERNEL_SYMBOLS = {
