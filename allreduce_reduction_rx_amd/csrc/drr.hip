@@ -7,8 +7,11 @@ namespace {
 
 // One wave per tile (64 threads per work item). Large messages: 256-thread
 // workgroups, at most 2 per CU (a narrow HBM access window measured best on
-// MI355X); decode-size messages: one tile per wave over every CU.
+// MI355X), 4 for the FP32-output layout, whose 4 chunks per lane keep fewer
+// bytes in flight per wave; decode-size messages: one tile per wave over
+// every CU.
 LaunchPolicy policy_drr() { return {64u, 256u, 2u}; }
+LaunchPolicy policy_drr_fp32_out() { return {64u, 256u, 4u}; }
 
 }  // namespace
 
@@ -31,7 +34,8 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     const size_t tile = (size_t)kWave * cpc * u;
     const size_t tiles = (len + tile - 1) / tile;
     dim3 grid, blk;
-    launch_geometry(tiles * kWave, small, policy_drr(), grid, blk);
+    launch_geometry(tiles * kWave, small,
+                    (cpc == 4 && u == 4) ? policy_drr_fp32_out() : policy_drr(), grid, blk);
     DrrArgs arg = a;
     // decode-size: one tile per wave, and the waves sharing a scale line on
     // one XCD (measured 8% faster); large messages keep the plain order

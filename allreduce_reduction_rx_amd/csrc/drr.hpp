@@ -159,7 +159,7 @@ __device__ __forceinline__ void store_hp(void* out, bool bf16, size_t c, size_t 
     }
 }
 
-// MULTI: the requantized result goes to a.nout destinations (the
+// MULTI: the requantized result goes to N destinations, one per rank (the
 // low-precision tree step's push); otherwise to out_codes[0] / out_scales[0].
 template <int F, int N, bool REQUANT, int CPC, int U, bool MULTI>
 __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
@@ -233,11 +233,16 @@ __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
                 q[p] = f32x4_to_fp8<F>(clamp_fmax<F>(S[4 * p + 0] * r2), clamp_fmax<F>(S[4 * p + 1] * r2),
                                        clamp_fmax<F>(S[4 * p + 2] * r2), clamp_fmax<F>(S[4 * p + 3] * r2));
             if constexpr (MULTI) {
-                for (int j = 0; j < a.nout; ++j)   // push the chunk to every destination
+                // push the chunk to every destination (one per rank: nout == N,
+                // so the loop unrolls and the pointers load once)
+#pragma unroll
+                for (int j = 0; j < N; ++j)
                     store_codes<CPC>(static_cast<uint8_t*>(a.out_codes[j]), c[u], e[u], count, whole[u], q);
-                if (valid[u] && (lane % lpb) == 0)
-                    for (int j = 0; j < a.nout; ++j)
+                if (valid[u] && (lane % lpb) == 0) {
+#pragma unroll
+                    for (int j = 0; j < N; ++j)
                         a.out_scales[j][b[u]] = s2;
+                }
             } else {
                 store_codes<CPC>(static_cast<uint8_t*>(a.out_codes[0]), c[u], e[u], count, whole[u], q);
                 if (valid[u] && (lane % lpb) == 0)

@@ -519,3 +519,103 @@ def test_group_max_lane_layout():
         got = out.cpu().numpy().view(np.uint32)
         ref = np.repeat(vals.reshape(-1, g).max(axis=1), g)
         assert np.array_equal(got, ref), f"g={g}"
+
+
+# ---------------------------------------------------------------------------
+# HIP graphs and concurrent streams
+# ---------------------------------------------------------------------------
+
+def _lp_all(ts, fmt, block, n, count):
+    nb = -(-count // block)
+    dt = ts[0].dtype
+    out = dict(
+        flat=torch.empty(count, dtype=dt, device=DEV),
+        tree=[torch.empty(count, dtype=dt, device=DEV) for _ in range(n)],
+        codes=[torch.empty(count, dtype=torch.uint8, device=DEV) for _ in range(n)],
+        scales=[torch.empty(nb, dtype=torch.float32, device=DEV) for _ in range(n)],
+        oc=torch.empty(count, dtype=torch.uint8, device=DEV),
+        osc=torch.empty(nb, dtype=torch.float32, device=DEV),
+        hp=torch.empty(count, dtype=dt, device=DEV),
+        lpc=[torch.empty(count, dtype=torch.uint8, device=DEV) for _ in range(n)],
+        lps=[torch.empty(nb, dtype=torch.float32, device=DEV) for _ in range(n)],
+    )
+
+    def run():
+        rx.rx_reduce_flat(ts, out["flat"])
+        rx.rx_reduce_scatter_chunk_bcast(ts, 1, out["tree"])
+        rx.rx_quant_fp8(ts, fmt, block, out["codes"], out["scales"])
+        rx.rx_dequant_reduce_requant(out["codes"], out["scales"], fmt, block, rx.RX_DRR_REQUANT,
+                                     out["oc"], out["osc"], out["hp"])
+        rx.rx_lp_reduce_scatter_chunk_bcast(out["codes"], out["scales"], fmt, block, 2,
+                                            out["lpc"], out["lps"])
+    return out, run
+
+
+def _snapshot(out):
+    flat = lambda v: [v] if torch.is_tensor(v) else list(v)
+    return {k: [to_host(t).copy() for t in flat(v)] for k, v in out.items()}
+
+
+@pytest.mark.parametrize("count", [262_144, 3 * (1 << 20) + 77])
+def test_graph_replays_match_eager(count):
+    """All five entry points captured in one HIP graph (no memset nodes: the
+    library enqueues kernels only), replayed three times with new inputs
+    written eagerly between replays; every replay must equal an eager run on
+    the same inputs."""
+    n, fmt, block = 8, "e5m2", 256
+    inputs = [[to_gpu(G.fill(count, G.BF16, G.NORMAL, seed=6000 + 10 * k + count % 7, rank=r))
+               for r in range(n)] for k in range(3)]
+    ts = [torch.empty(count, dtype=torch.bfloat16, device=DEV) for _ in range(n)]
+    out, run = _lp_all(ts, fmt, block, n, count)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    def clear():   # the chunk steps leave everything outside their chunk as it was
+        for v in out.values():
+            for t in ([v] if torch.is_tensor(v) else v):
+                t.zero_()
+
+    for k in range(3):
+        log(f"graph replay {k} count={count}")
+        for t, x in zip(ts, inputs[k]):
+            t.copy_(x)
+        clear()
+        sync()
+        g.replay()
+        sync()
+        got = _snapshot(out)
+        clear()
+        run()
+        sync()
+        ref = _snapshot(out)
+        for key in got:
+            for a, b in zip(got[key], ref[key]):
+                assert bits_equal(a, b), f"replay {k} {key}: " + first_mismatch(a, b)
+
+
+def test_concurrent_streams_are_independent():
+    """Calls on two streams at once (the library keeps no state) give the
+    same results as the same calls one after the other."""
+    n, fmt, block, count = 8, "e4m3", 128, 2 * (1 << 20) + 3
+    ins = [[to_gpu(G.fill(count, G.FP32, G.NORMAL_OUTLIER, seed=7000 + s, rank=r)) for r in range(n)]
+           for s in range(2)]
+    outs, runs = zip(*[_lp_all(ins[s], fmt, block, n, count) for s in range(2)])
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    cur = torch.cuda.current_stream()
+    for s in range(2):
+        streams[s].wait_stream(cur)
+    for _ in range(3):
+        for s in range(2):
+            with torch.cuda.stream(streams[s]):
+                runs[s]()
+    for s in range(2):
+        cur.wait_stream(streams[s])
+    sync()
+    got = [_snapshot(o) for o in outs]
+    for s in range(2):
+        runs[s]()
+        sync()
+        ref = _snapshot(outs[s])
+        for key in ref:
+            for a, b in zip(got[s][key], ref[key]):
+                assert bits_equal(a, b), f"stream {s} {key}: " + first_mismatch(a, b)
