@@ -21,17 +21,21 @@ __all__ = [
     "RX_DRR_REQUANT", "RX_MAX_SRC", "RxError", "lib", "lib_path",
     "rx_reduce_flat", "rx_reduce_scatter_chunk_bcast", "rx_tree_chunk",
     "rx_quant_fp8", "rx_dequant_reduce_requant", "rx_status_string",
-    "rx_lp_reduce_scatter_chunk_bcast", "rx_lp_tree_chunk", "EXPORTED_SYMBOLS",
+    "rx_lp_reduce_scatter_chunk_bcast", "rx_lp_tree_chunk", "rx_allreduce_local",
+    "rx_allreduce_local_workspace", "RX_ALGO_AUTO", "RX_ALGO_FLAT", "RX_ALGO_TREE",
+    "RX_ALGO_LOWPREC", "EXPORTED_SYMBOLS",
 ]
 
 RX_FP32, RX_BF16, RX_FP8_E4M3, RX_FP8_E5M2 = 0, 1, 2, 3
 RX_DRR_SUM, RX_DRR_REQUANT = 0, 1
+RX_ALGO_AUTO, RX_ALGO_FLAT, RX_ALGO_TREE, RX_ALGO_LOWPREC = 0, 1, 2, 3
 RX_MAX_SRC = 16
 
 EXPORTED_SYMBOLS = (
     "rx_reduce_flat", "rx_reduce_scatter_chunk_bcast", "rx_tree_chunk",
     "rx_quant_fp8", "rx_dequant_reduce_requant", "rx_status_string",
-    "rx_lp_reduce_scatter_chunk_bcast", "rx_lp_tree_chunk", "rxtest_fp8_encode_bits", "rxtest_fp8_decode", "rxtest_bf16_round_bits",
+    "rx_lp_reduce_scatter_chunk_bcast", "rx_lp_tree_chunk", "rx_allreduce_local",
+    "rx_allreduce_local_workspace", "rxtest_fp8_encode_bits", "rxtest_fp8_decode", "rxtest_bf16_round_bits",
     "rxtest_group_max",
 )
 
@@ -73,6 +77,7 @@ def lib() -> ctypes.CDLL:
             "rx_lp_reduce_scatter_chunk_bcast": [_PP, _PP, _I, _SZ, _I, _I, _I, _PP, _PP, _P,
                                                  _I, _P],
             "rx_lp_tree_chunk": [_SZ, _I, _I, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)],
+            "rx_allreduce_local": [_PP, _I, _SZ, _I, _I, _I, _I, _P, _SZ, _P],
             "rxtest_fp8_encode_bits": [ctypes.c_uint32, _SZ, _I, _P, _P],
             "rxtest_fp8_decode": [_P, _SZ, _I, _P, _P],
             "rxtest_bf16_round_bits": [ctypes.c_uint32, _SZ, _P, _P],
@@ -82,6 +87,8 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        L.rx_allreduce_local_workspace.argtypes = [_I, _SZ, _I]
+        L.rx_allreduce_local_workspace.restype = ctypes.c_size_t
         L.rx_status_string.argtypes = [_I]
         L.rx_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -277,6 +284,35 @@ def rx_lp_reduce_scatter_chunk_bcast(codes: Sequence, scales: Sequence, fmt, blo
         arr(codes), arr(scales), n, count, _fp8_code(fmt), block, rank, arr(dst_codes),
         arr(dst_scales), None if out_hp is None else out_hp.data_ptr(), hp_dt, _stream(stream)),
         "rx_lp_reduce_scatter_chunk_bcast")
+
+
+def rx_allreduce_local_workspace(nsrc: int, count: int, block: int) -> int:
+    """Workspace bytes rx_allreduce_local needs for the low-precision algorithm."""
+    return int(lib().rx_allreduce_local_workspace(nsrc, count, block))
+
+
+def rx_allreduce_local(bufs: Sequence, algo: int = RX_ALGO_AUTO, fmt="e4m3", block: int = 128,
+                       workspace=None, count: Optional[int] = None, stream=None) -> None:
+    """In-place SUM allreduce of the rank buffers `bufs` (all on this GPU):
+    afterwards every buffer holds the result. `workspace` (a uint8 GPU tensor
+    of rx_allreduce_local_workspace() bytes) is needed by the low-precision
+    algorithm only."""
+    import torch
+    count = bufs[0].numel() if count is None else count
+    dt = _rx_dtype(bufs[0])
+    for k, t in enumerate(bufs):
+        _gpu(t, f"bufs[{k}]")
+        if t.dtype != bufs[0].dtype or t.numel() < count:
+            raise ValueError(f"bufs[{k}] must be {bufs[0].dtype} with >= {count} elements")
+    wptr, wbytes = None, 0
+    if workspace is not None:
+        _gpu(workspace, "workspace")
+        if workspace.dtype != torch.uint8:
+            raise ValueError("workspace must be a uint8 tensor")
+        wptr, wbytes = workspace.data_ptr(), workspace.numel()
+    _check(lib().rx_allreduce_local(_ptr_array([t.data_ptr() for t in bufs]), len(bufs), count,
+                                    dt, int(algo), _fp8_code(fmt), block, wptr, wbytes,
+                                    _stream(stream)), "rx_allreduce_local")
 
 
 # ---- test hooks (rx_testhooks.h) -------------------------------------------

@@ -79,6 +79,8 @@ rx_status_t check_ptrs(const void* const* p, int n, bool align16)
     return RX_OK;
 }
 
+size_t round256(size_t n) { return (n + 255u) / 256u * 256u; }
+
 size_t lp_chunk_len(size_t count, int nsrc, int block)
 {
     size_t c = (count + (size_t)nsrc - 1) / (size_t)nsrc;
@@ -333,6 +335,130 @@ rx_status_t rx_lp_reduce_scatter_chunk_bcast(const void* const* codes,
     a.block = block;
     a.hp_bf16 = hp_dtype == RX_BF16 ? 1 : 0;
     return launched(rx::launch_drr(a, nsrc, fp8_dtype == RX_FP8_E5M2 ? 1 : 0, true, stream));
+}
+
+size_t rx_allreduce_local_workspace(int nsrc, size_t count, int block)
+{
+    if (nsrc < 1 || nsrc > RX_MAX_SRC || !valid_block(block) || count > kMaxCount)
+        return 0;
+    const size_t nb = (count + (size_t)block - 1) / (size_t)block;
+    return (size_t)nsrc * (round256(count) + round256(nb * sizeof(float)));
+}
+
+rx_status_t rx_allreduce_local(void* const* bufs, int nsrc, size_t count,
+                               rx_dtype_t dtype, rx_algo_t algo,
+                               rx_dtype_t fp8_dtype, int block, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream)
+{
+    if (!bufs)
+        return RX_ERR_NULL;
+    if (nsrc < 1 || nsrc > RX_MAX_SRC || count > kMaxCount || algo < RX_ALGO_AUTO ||
+        algo > RX_ALGO_LOWPREC)
+        return RX_ERR_ARG;
+    if (!hp_type(dtype))
+        return RX_ERR_DTYPE;
+    rx_status_t st = check_ptrs(reinterpret_cast<const void* const*>(bufs), nsrc, true);
+    if (st != RX_OK)
+        return st;
+    const size_t esz = dtype == RX_BF16 ? 2 : 4;
+    if (algo == RX_ALGO_AUTO) {
+        const char* en = getenv("RX_LOW_PRECISION_ENABLE");
+        const bool lp = en && en[0] == '1' && en[1] == '\0' && count * esz >= ((size_t)16 << 20);
+        algo = lp ? RX_ALGO_LOWPREC : RX_ALGO_FLAT;
+    }
+    size_t need = 0;
+    if (algo == RX_ALGO_LOWPREC) {
+        if (!valid_block(block))
+            return RX_ERR_ARG;
+        if (!fp8_type(fp8_dtype))
+            return RX_ERR_DTYPE;
+        if (!workspace)
+            return RX_ERR_NULL;
+        if (((uintptr_t)workspace & 255u) != 0)
+            return RX_ERR_ALIGN;
+        need = rx_allreduce_local_workspace(nsrc, count, block);
+        if (workspace_bytes < need)
+            return RX_ERR_ARG;
+    }
+    if (count == 0)
+        return RX_OK;
+    const int dt = dtype == RX_BF16 ? 1 : 0;
+
+    if (algo == RX_ALGO_FLAT || algo == RX_ALGO_TREE) {
+        rx::TreeArgs a = {};
+        for (int j = 0; j < nsrc; ++j) {
+            a.src[j] = bufs[j];
+            a.dst[j] = bufs[j];
+        }
+        if (algo == RX_ALGO_FLAT) {
+            a.lo = 0;
+            a.hi = count;
+            return launched(rx::launch_tree(a, nsrc, dt, stream));
+        }
+        for (int k = 0; k < nsrc; ++k) {
+            rx_tree_chunk(count, nsrc, dtype, k, &a.lo, &a.hi);
+            if (a.lo >= a.hi)
+                continue;
+            rx_status_t r = launched(rx::launch_tree(a, nsrc, dt, stream));
+            if (r != RX_OK)
+                return r;
+        }
+        return RX_OK;
+    }
+
+    // low precision: codes and scales of every rank in the workspace
+    const size_t nb = (count + (size_t)block - 1) / (size_t)block;
+    const int fmt = fp8_dtype == RX_FP8_E5M2 ? 1 : 0;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    void* codes[RX_MAX_SRC];
+    float* scales[RX_MAX_SRC];
+    for (int j = 0; j < nsrc; ++j) {
+        codes[j] = ws + (size_t)j * round256(count);
+        scales[j] = reinterpret_cast<float*>(ws + (size_t)nsrc * round256(count) +
+                                             (size_t)j * round256(nb * sizeof(float)));
+    }
+    rx::QuantArgs q = {};
+    for (int j = 0; j < nsrc; ++j) {
+        q.src[j] = bufs[j];
+        q.codes[j] = codes[j];
+        q.scales[j] = scales[j];
+    }
+    q.count = count;
+    q.nsrc = nsrc;
+    rx_status_t r = launched(rx::launch_quant(q, dt, fmt, block, stream));
+    if (r != RX_OK)
+        return r;
+    rx::DrrArgs d = {};
+    for (int j = 0; j < nsrc; ++j) {
+        d.codes[j] = codes[j];
+        d.scales[j] = scales[j];
+        d.out_codes[j] = codes[j];     // in place: see rx_lp_reduce_scatter_chunk_bcast
+        d.out_scales[j] = scales[j];
+    }
+    d.nout = nsrc;
+    d.block = block;
+    for (int k = 0; k < nsrc; ++k) {
+        rx_lp_tree_chunk(count, nsrc, block, k, &d.lo, &d.hi);
+        if (d.lo >= d.hi)
+            continue;
+        r = launched(rx::launch_drr(d, nsrc, fmt, true, stream));
+        if (r != RX_OK)
+            return r;
+    }
+    for (int j = 0; j < nsrc; ++j) {   // every rank dequantizes the gathered message
+        rx::DrrArgs x = {};
+        x.codes[0] = codes[j];
+        x.scales[0] = scales[j];
+        x.out_hp = bufs[j];
+        x.lo = 0;
+        x.hi = count;
+        x.block = block;
+        x.hp_bf16 = dt;
+        r = launched(rx::launch_drr(x, 1, fmt, false, stream));
+        if (r != RX_OK)
+            return r;
+    }
+    return RX_OK;
 }
 
 }  // extern "C"

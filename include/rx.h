@@ -186,7 +186,9 @@ rx_status_t rx_dequant_reduce_requant(const void* const* codes,
  *                         (scales) are written.
  * out_hp                : optional (NULL): chunk `rank` of the dequantized
  *                         result, hp_dtype RX_FP32 or RX_BF16, message-indexed.
- * Destinations must not overlap the inputs.
+ * Exact aliasing dst_codes[j] == codes[j] with dst_scales[j] == scales[j] is
+ * allowed (in-place all-gather: every block is read completely by one wave
+ * before that wave writes it); any other overlap is undefined.
  */
 rx_status_t rx_lp_reduce_scatter_chunk_bcast(const void* const* codes,
                                              const float* const* scales, int nsrc,
@@ -200,6 +202,57 @@ rx_status_t rx_lp_reduce_scatter_chunk_bcast(const void* const* codes,
 /* Host helper: bounds [*lo, *hi) of low-precision chunk `rank` (no HIP call). */
 rx_status_t rx_lp_tree_chunk(size_t count, int nsrc, int block, int rank,
                              size_t* lo, size_t* hi);
+
+typedef enum {
+    RX_ALGO_AUTO = 0,    /* LOWPREC when enabled and >= 16 MiB, else FLAT   */
+    RX_ALGO_FLAT = 1,    /* one fused sum-and-broadcast pass                */
+    RX_ALGO_TREE = 2,    /* nsrc tree steps, one per rank's chunk           */
+    RX_ALGO_LOWPREC = 3  /* quantize, nsrc low-precision tree steps, dequant */
+} rx_algo_t;
+
+/*
+ * Allreduce (SUM) of nsrc rank buffers held on this device, in place:
+ * afterwards every bufs[j] holds the result (RCCLX article, "Practical
+ * guide": allreduce with ReduceOp.SUM, in place). It runs one of the
+ * algorithms of the article on the local buffers:
+ *   RX_ALGO_FLAT    each rank's result is the full reduce ("Core feature 1",
+ *                   DDA Flat); on one device the nsrc identical reductions
+ *                   are one pass that reads every buffer once and writes the
+ *                   FP32 left fold into all of them.
+ *   RX_ALGO_TREE    rx_reduce_scatter_chunk_bcast for every rank k in turn
+ *                   ("Core feature 1", DDA Tree); same result as FLAT.
+ *   RX_ALGO_LOWPREC rx_quant_fp8 of every buffer, rx_lp_reduce_scatter_chunk_
+ *                   bcast for every rank k (in place on the workspace), then
+ *                   every rank dequantizes the gathered FP8 message into its
+ *                   buffer ("Core feature 2"); every buffer receives
+ *                   dequant(requant(FP32 sum of the dequantized inputs)).
+ *   RX_ALGO_AUTO    RX_ALGO_LOWPREC when the environment variable
+ *                   RX_LOW_PRECISION_ENABLE is "1" and a buffer is >= 16 MiB
+ *                   (the article's activation switch and threshold),
+ *                   otherwise RX_ALGO_FLAT (on one device the flat pass is
+ *                   never slower than nsrc tree steps).
+ *
+ * bufs            : nsrc device pointers, `count` elements of dtype each
+ *                   (RX_FP32 or RX_BF16), 16-B aligned, distinct.
+ * fp8_dtype, block: low-precision format and block size (as rx_quant_fp8);
+ *                   checked only when the low-precision algorithm runs.
+ * workspace       : device memory of at least rx_allreduce_local_workspace()
+ *                   bytes, 256-B aligned; needed only by the low-precision
+ *                   algorithm (NULL otherwise); its contents on return are
+ *                   unspecified.
+ * Errors: RX_ERR_NULL when the low-precision algorithm runs without a
+ * workspace, RX_ERR_ARG when it is too small, as well as the errors of the
+ * entry points above.
+ */
+rx_status_t rx_allreduce_local(void* const* bufs, int nsrc, size_t count,
+                               rx_dtype_t dtype, rx_algo_t algo,
+                               rx_dtype_t fp8_dtype, int block, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes rx_allreduce_local needs for the low-precision algorithm
+ * (codes and scales of every rank, each array 256-B aligned); 0 on invalid
+ * arguments. No HIP call. */
+size_t rx_allreduce_local_workspace(int nsrc, size_t count, int block);
 
 /* Static description of a status code (never NULL). */
 const char* rx_status_string(rx_status_t s);

@@ -16,6 +16,7 @@ import numpy as np
 
 FP32, BF16, E4M3, E5M2 = 0, 1, 2, 3
 DRR_SUM, DRR_REQUANT = 0, 1
+ALGO_FLAT, ALGO_TREE, ALGO_LOWPREC = 1, 2, 3
 FMT = {"e4m3": E4M3, "e5m2": E5M2}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -52,6 +53,7 @@ def lib():
             "rxo_dequant_reduce_requant": (None, [_P, _P, _I, _SZ, _I, _I, _I,
                                                   _P, _P, _P, _I]),
             "rxo_lp_tree_chunk": (None, [_SZ, _I, _I, _I, _P, _P]),
+            "rxo_allreduce_local": (None, [_P, _I, _SZ, _I, _I, _I, _I]),
             "rxo_lp_reduce_scatter_chunk_bcast": (None, [_P, _P, _I, _SZ, _I, _I, _I,
                                                          _P, _P, _P, _I]),
         }
@@ -216,3 +218,11 @@ def lp_reduce_scatter_chunk_bcast(codes: Sequence[np.ndarray], scales: Sequence[
     lib().rxo_lp_reduce_scatter_chunk_bcast(_ptrs(codes), _ptrs(scales), len(codes), count,
                                             fmt, block, rank, _ptrs(dst_codes),
                                             _ptrs(dst_scales), hptr, hp_dtype)
+
+
+def allreduce_local(bufs: Sequence[np.ndarray], dtype: int, algo: int, fmt: int = E4M3,
+                    block: int = 128, count: Optional[int] = None) -> None:
+    """In place: every array of ``bufs`` receives the allreduce result."""
+    count = bufs[0].size if count is None else count
+    _check(bufs, _np_of(dtype), count)
+    lib().rxo_allreduce_local(_ptrs(bufs), len(bufs), count, dtype, algo, fmt, block)

@@ -406,3 +406,53 @@ void rxo_lp_reduce_scatter_chunk_bcast(const uint8_t* const* codes,
     free(os);
     free(oc);
 }
+
+/* ---------------------------------------------------------------------- */
+/* Local allreduce (all ranks' buffers on one device)                      */
+/* ---------------------------------------------------------------------- */
+
+/* The usage example of the RCCLX article ("Practical guide": allreduce with
+ * ReduceOp.SUM, in place) carried out with each of the algorithms of "Core
+ * feature 1" (DDA flat, DDA tree) and "Core feature 2" (low precision). */
+void rxo_allreduce_local(void* const* bufs, int nsrc, size_t count, int dtype,
+                         int algo, int fmt, int block)
+{
+    if (count == 0 || nsrc < 1 || nsrc > 64)
+        return;
+    size_t es = elem_size(dtype);
+    if (algo == RXO_ALGO_FLAT || algo == RXO_ALGO_TREE) {
+        void* y = malloc(count * es);
+        rxo_reduce_flat((const void* const*)bufs, nsrc, count, dtype, y);
+        for (int j = 0; j < nsrc; ++j)
+            memcpy(bufs[j], y, count * es);
+        free(y);
+        return;
+    }
+    /* low precision */
+    size_t nb = (count + (size_t)block - 1) / (size_t)block;
+    uint8_t* codes[64];
+    float* scales[64];
+    for (int j = 0; j < nsrc; ++j) {
+        codes[j] = (uint8_t*)malloc(count);
+        scales[j] = (float*)malloc(nb * sizeof(float));
+    }
+    rxo_quant_fp8((const void* const*)bufs, nsrc, count, dtype, fmt, block, codes, scales);
+    uint8_t* rc[64];
+    float* rs[64];
+    for (int j = 0; j < nsrc; ++j) {
+        rc[j] = (uint8_t*)malloc(count);
+        rs[j] = (float*)malloc(nb * sizeof(float));
+    }
+    for (int k = 0; k < nsrc; ++k)
+        rxo_lp_reduce_scatter_chunk_bcast((const uint8_t* const*)codes, (const float* const*)scales,
+                                          nsrc, count, fmt, block, k, rc, rs, NULL, RXO_FP32);
+    for (int j = 0; j < nsrc; ++j) {
+        const uint8_t* cj[1] = {rc[j]};
+        const float* sj[1] = {rs[j]};
+        rxo_dequant_reduce_requant(cj, sj, 1, count, fmt, block, RXO_DRR_SUM, NULL, NULL,
+                                   bufs[j], dtype);
+    }
+    for (int j = 0; j < nsrc; ++j) {
+        free(codes[j]); free(scales[j]); free(rc[j]); free(rs[j]);
+    }
+}

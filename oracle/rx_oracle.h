@@ -117,6 +117,16 @@ void rxo_lp_reduce_scatter_chunk_bcast(const uint8_t* const* codes,
                                        float* const* dst_scales,
                                        void* out_hp, int hp_dtype);
 
+/* Whole allreduce of nsrc rank buffers on one GPU, in place: afterwards
+ * every bufs[j] holds the result. algo 1 (flat) and 2 (tree) give the FP32
+ * left fold cast to dtype; algo 3 (low precision) gives, for every rank,
+ * the dequantization of the requantized FP32 sum of the quantized inputs
+ * (quantize each rank, reduce-scatter + all-gather of the FP8 chunks,
+ * dequantize). */
+enum { RXO_ALGO_FLAT = 1, RXO_ALGO_TREE = 2, RXO_ALGO_LOWPREC = 3 };
+void rxo_allreduce_local(void* const* bufs, int nsrc, size_t count, int dtype,
+                         int algo, int fmt, int block);
+
 #ifdef __cplusplus
 }
 #endif

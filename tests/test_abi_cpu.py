@@ -148,3 +148,29 @@ def test_lp_tree_validation_and_chunks():
     assert [rx.rx_lp_tree_chunk(1000, 3, 128, k) for k in range(3)] == [(0, 384), (384, 768), (768, 1000)]
     # an empty chunk launches nothing
     assert f(c, s, 2, 100, E4, 128, 1, dc, ds, None, rx.RX_FP32, None) == OK
+
+
+def test_allreduce_local_validation():
+    L = rx.lib()
+    f = L.rx_allreduce_local
+    bufs = ptrs(FAKE, FAKE + 4096)
+    ws = FAKE + (1 << 20)
+    F32, E4 = rx.RX_FP32, rx.RX_FP8_E4M3
+    FLAT, LP, AUTO = rx.RX_ALGO_FLAT, rx.RX_ALGO_LOWPREC, rx.RX_ALGO_AUTO
+    need = rx.rx_allreduce_local_workspace(2, 1000, 128)
+    assert need == 2 * (1024 + 256)
+    assert rx.rx_allreduce_local_workspace(0, 1000, 128) == 0
+    assert rx.rx_allreduce_local_workspace(2, 1000, 100) == 0
+    assert f(None, 2, 1000, F32, FLAT, E4, 128, None, 0, None) == NULL
+    assert f(bufs, 0, 1000, F32, FLAT, E4, 128, None, 0, None) == ARG
+    assert f(bufs, 2, 1000, F32, 9, E4, 128, None, 0, None) == ARG
+    assert f(bufs, 2, 1000, rx.RX_FP8_E5M2, FLAT, E4, 128, None, 0, None) == DTYPE
+    assert f(ptrs(FAKE, FAKE + 2), 2, 1000, F32, FLAT, E4, 128, None, 0, None) == ALIGN
+    assert f(bufs, 2, 1000, F32, LP, E4, 128, None, 0, None) == NULL
+    assert f(bufs, 2, 1000, F32, LP, E4, 128, ws, need - 1, None) == ARG
+    assert f(bufs, 2, 1000, F32, LP, E4, 128, ws + 16, need, None) == ALIGN
+    assert f(bufs, 2, 1000, F32, LP, E4, 96, ws, need, None) == ARG
+    assert f(bufs, 2, 1000, F32, LP, rx.RX_BF16, 128, ws, need, None) == DTYPE
+    # nothing to do: no launch
+    assert f(bufs, 2, 0, F32, LP, E4, 128, ws, need, None) == OK
+    assert f(bufs, 2, 0, F32, AUTO, E4, 128, None, 0, None) == OK

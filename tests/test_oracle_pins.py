@@ -587,3 +587,44 @@ def test_lp_tree_rank_id_example():
         for j in range(n):
             assert np.all(dc[j] == maxc) and np.all(ds[j] == np.float32(float(s2_s)))
         assert np.all(hp == np.float32(float(res_s)))
+
+
+# ---------------------------------------------------------------------------
+# Local allreduce (all ranks' buffers on one device), in place
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("algo", [O.ALGO_FLAT, O.ALGO_TREE, O.ALGO_LOWPREC])
+def test_allreduce_local_rank_id_example(algo):
+    # the pages' usage example: 8 ranks, 10x20 FP32 filled with the rank id,
+    # SUM in place -> 28 in every rank's tensor, whatever the algorithm
+    for fmt, block in ((O.E4M3, 128), (O.E5M2, 256)):
+        bufs = [G.fill(200, G.FP32, G.RANK, rank=r) for r in range(8)]
+        O.allreduce_local(bufs, O.FP32, algo, fmt, block)
+        for b in bufs:
+            assert np.all(b == 28.0)
+
+
+@pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
+def test_allreduce_local_flat_and_tree_broadcast_the_reduce(dtype):
+    n, count = 6, 3001
+    srcs = [G.fill(count, dtype, G.NORMAL, seed=81, rank=r) for r in range(n)]
+    ref = O.reduce_flat(srcs, dtype)
+    for algo in (O.ALGO_FLAT, O.ALGO_TREE):
+        bufs = [s.copy() for s in srcs]
+        O.allreduce_local(bufs, dtype, algo)
+        for b in bufs:
+            assert np.array_equal(b, ref)
+
+
+@pytest.mark.parametrize("dtype,fmt,block", [(O.FP32, O.E4M3, 128), (O.BF16, O.E5M2, 256)])
+def test_allreduce_local_lowprec_is_requantized_allreduce(dtype, fmt, block):
+    # every rank ends with dequant(requant(sum)): the high-precision output of
+    # the dequant-reduce-requant step on the quantized inputs
+    n, count = 5, block * 13 + 7
+    srcs = [G.fill(count, dtype, G.LAPLACE, seed=82, rank=r) for r in range(n)]
+    codes, scales = O.quant_fp8(srcs, dtype, fmt, block)
+    _, _, ref = O.dequant_reduce_requant(codes, scales, fmt, block, O.DRR_REQUANT, dtype, True)
+    bufs = [s.copy() for s in srcs]
+    O.allreduce_local(bufs, dtype, O.ALGO_LOWPREC, fmt, block)
+    for b in bufs:
+        assert np.array_equal(b, ref)

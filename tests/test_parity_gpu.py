@@ -619,3 +619,83 @@ def test_concurrent_streams_are_independent():
         for key in ref:
             for a, b in zip(got[s][key], ref[key]):
                 assert bits_equal(a, b), f"stream {s} {key}: " + first_mismatch(a, b)
+
+
+# ---------------------------------------------------------------------------
+# Local allreduce dispatcher and in-place low-precision tree step
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
+@pytest.mark.parametrize("algo", [rx.RX_ALGO_FLAT, rx.RX_ALGO_TREE, rx.RX_ALGO_LOWPREC])
+def test_allreduce_local(dtype, algo):
+    n = 8
+    fmt, block = (O.E4M3, 128) if dtype == O.FP32 else (O.E5M2, 256)
+    for count in [1, 1000, 262_144, 3 * (1 << 20) + 5]:
+        log(f"allreduce_local algo={algo} dtype={dtype} count={count}")
+        srcs = [G.fill(count, dtype, G.NORMAL_OUTLIER, seed=8000 + count % 97, rank=r) for r in range(n)]
+        ts = [to_gpu(s) for s in srcs]
+        ws = torch.empty(rx.rx_allreduce_local_workspace(n, count, block), dtype=torch.uint8, device=DEV)
+        rx.rx_allreduce_local(ts, algo, FMTS[fmt], block, ws)
+        sync()
+        ref = [s.copy() for s in srcs]
+        O.allreduce_local(ref, dtype, {rx.RX_ALGO_FLAT: O.ALGO_FLAT, rx.RX_ALGO_TREE: O.ALGO_TREE,
+                                       rx.RX_ALGO_LOWPREC: O.ALGO_LOWPREC}[algo], fmt, block)
+        for j in range(n):
+            got = to_host(ts[j])
+            assert bits_equal(got, ref[j]), f"count={count} rank={j}: " + first_mismatch(got, ref[j])
+
+
+def test_allreduce_local_rank_id_example():
+    for algo in (rx.RX_ALGO_FLAT, rx.RX_ALGO_TREE, rx.RX_ALGO_LOWPREC, rx.RX_ALGO_AUTO):
+        ts = [torch.full((10, 20), float(r), dtype=torch.float32, device=DEV) for r in range(8)]
+        ws = torch.empty(rx.rx_allreduce_local_workspace(8, 200, 128), dtype=torch.uint8, device=DEV)
+        rx.rx_allreduce_local(ts, algo, "e4m3", 128, ws)
+        sync()
+        assert all(torch.all(t == 28.0).item() for t in ts), f"algo {algo}"
+
+
+def test_allreduce_local_auto_switch(monkeypatch):
+    """AUTO takes the low-precision path only with RX_LOW_PRECISION_ENABLE=1
+    and messages of at least 16 MiB; otherwise the flat pass."""
+    n, count, fmt, block = 8, 8 * (1 << 20) + 3, "e5m2", 256   # BF16: 16 MiB + 6 bytes
+    srcs = [G.fill(count, G.BF16, G.LAPLACE, seed=8500, rank=r) for r in range(n)]
+    ws = torch.empty(rx.rx_allreduce_local_workspace(n, count, block), dtype=torch.uint8, device=DEV)
+    for env, algo in (("0", O.ALGO_FLAT), ("1", O.ALGO_LOWPREC)):
+        monkeypatch.setenv("RX_LOW_PRECISION_ENABLE", env)
+        log(f"allreduce_local auto env={env}")
+        ts = [to_gpu(s) for s in srcs]
+        rx.rx_allreduce_local(ts, rx.RX_ALGO_AUTO, fmt, block, ws)
+        sync()
+        ref = [s.copy() for s in srcs]
+        O.allreduce_local(ref, O.BF16, algo, O.E5M2, block)
+        for j in (0, n - 1):
+            got = to_host(ts[j])
+            assert bits_equal(got, ref[j]), f"env={env} rank={j}: " + first_mismatch(got, ref[j])
+    # below 16 MiB the switch does not apply
+    monkeypatch.setenv("RX_LOW_PRECISION_ENABLE", "1")
+    small = [s[:1000].copy() for s in srcs]
+    ts = [to_gpu(s) for s in small]
+    rx.rx_allreduce_local(ts, rx.RX_ALGO_AUTO, fmt, block, None)
+    sync()
+    ref = [s.copy() for s in small]
+    O.allreduce_local(ref, O.BF16, O.ALGO_FLAT)
+    assert bits_equal(to_host(ts[0]), ref[0])
+
+
+@pytest.mark.parametrize("count", [20_000, 3 * (1 << 20) + 5])
+def test_lp_tree_in_place(count):
+    n, fmt, block = 8, O.E4M3, 128
+    srcs = [G.fill(count, O.FP32, G.NORMAL, seed=9000 + count % 13, rank=r) for r in range(n)]
+    codes, scales = O.quant_fp8(srcs, O.FP32, fmt, block)
+    tc = [to_gpu(c) for c in codes]
+    tsc = [to_gpu(s) for s in scales]
+    ref_c = [c.copy() for c in codes]
+    ref_s = [s.copy() for s in scales]
+    for k in range(n):
+        log(f"lp tree in place count={count} rank={k}")
+        rx.rx_lp_reduce_scatter_chunk_bcast(tc, tsc, FMTS[fmt], block, k, tc, tsc)
+        sync()
+        O.lp_reduce_scatter_chunk_bcast([c.copy() for c in ref_c], [s.copy() for s in ref_s],
+                                        fmt, block, k, ref_c, ref_s)
+    for j in range(n):
+        assert bits_equal(to_host(tc[j]), ref_c[j]) and bits_equal(to_host(tsc[j]), ref_s[j])
