@@ -194,6 +194,8 @@ rx_status_t rx_quant_fp8(const void* const* srcs, int nsrc, size_t count,
         return RX_ERR_NULL;
     if (nsrc < 1 || nsrc > RX_MAX_SRC || !valid_block(block) || count > kMaxCount)
         return RX_ERR_ARG;
+    if ((count / 256 + 1) * (size_t)nsrc >= ((size_t)1 << 32))   // 32-bit tile indices
+        return RX_ERR_ARG;
     if (!hp_type(src_dtype) || !fp8_type(fp8_dtype))
         return RX_ERR_DTYPE;
     rx_status_t st = check_ptrs(srcs, nsrc, true);

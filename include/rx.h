@@ -128,6 +128,8 @@ rx_status_t rx_tree_chunk(size_t count, int nsrc, rx_dtype_t dtype, int rank,
  * codes     : nsrc device pointers, `count` bytes each (16-B aligned).
  * scales    : nsrc device pointers, ceil(count/block) floats each.
  * Codes and scales must not overlap the sources.
+ * RX_ERR_ARG also when (count / 256 + 1) * nsrc >= 2^32 (far beyond the
+ * device memory of one GPU).
  */
 rx_status_t rx_quant_fp8(const void* const* srcs, int nsrc, size_t count,
                          rx_dtype_t src_dtype, rx_dtype_t fp8_dtype, int block,

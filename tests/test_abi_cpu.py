@@ -96,6 +96,9 @@ def test_quant_validation():
     assert f(src, 1, 100, rx.RX_FP32, rx.RX_FP8_E4M3, 128, ptrs(FAKE + 1), sc, None) == ALIGN
     assert f(src, 1, 100, rx.RX_FP32, rx.RX_FP8_E4M3, 128, codes, ptrs(FAKE + 2), None) == ALIGN
     assert f(src, 1, 0, rx.RX_BF16, rx.RX_FP8_E5M2, 256, codes, sc, None) == OK
+    src16 = ptrs(*([FAKE] * 16))
+    c16, s16 = ptrs(*([FAKE + 4096] * 16)), ptrs(*([FAKE + 8192] * 16))
+    assert f(src16, 16, (1 << 36), rx.RX_FP32, rx.RX_FP8_E4M3, 128, c16, s16, None) == ARG
 
 
 def test_drr_validation():
