@@ -35,7 +35,7 @@ EXPORTED_SYMBOLS = (
     "rx_reduce_flat", "rx_reduce_scatter_chunk_bcast", "rx_tree_chunk",
     "rx_quant_fp8", "rx_dequant_reduce_requant", "rx_status_string",
     "rx_lp_reduce_scatter_chunk_bcast", "rx_lp_tree_chunk", "rx_allreduce_local",
-    "rx_allreduce_local_workspace", "rxtest_fp8_encode_bits", "rxtest_fp8_decode", "rxtest_bf16_round_bits",
+    "rx_allreduce_local_workspace", "rxtest_block_scale_bits", "rxtest_fp8_encode_bits", "rxtest_fp8_decode", "rxtest_bf16_round_bits",
     "rxtest_group_max",
 )
 
@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "rx_lp_tree_chunk": [_SZ, _I, _I, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)],
             "rx_allreduce_local": [_PP, _I, _SZ, _I, _I, _I, _I, _P, _SZ, _P],
             "rxtest_fp8_encode_bits": [ctypes.c_uint32, _SZ, _I, _P, _P],
+            "rxtest_block_scale_bits": [ctypes.c_uint32, _SZ, _I, _P, _P, _P],
             "rxtest_fp8_decode": [_P, _SZ, _I, _P, _P],
             "rxtest_bf16_round_bits": [ctypes.c_uint32, _SZ, _P, _P],
             "rxtest_group_max": [_P, _SZ, _I, _P, _P],
@@ -320,6 +321,11 @@ def rx_allreduce_local(bufs: Sequence, algo: int = RX_ALGO_AUTO, fmt="e4m3", blo
 def rxtest_fp8_encode_bits(first: int, n: int, fmt, out, stream=None) -> None:
     _check(lib().rxtest_fp8_encode_bits(first, n, _fp8_code(fmt), out.data_ptr(), _stream(stream)),
            "rxtest_fp8_encode_bits")
+
+
+def rxtest_block_scale_bits(first: int, n: int, fmt, s, r, stream=None) -> None:
+    _check(lib().rxtest_block_scale_bits(first, n, _fp8_code(fmt), s.data_ptr(), r.data_ptr(),
+                                         _stream(stream)), "rxtest_block_scale_bits")
 
 
 def rxtest_fp8_decode(codes, fmt, out, stream=None) -> None:

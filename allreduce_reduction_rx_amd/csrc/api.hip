@@ -430,36 +430,23 @@ rx_status_t rx_allreduce_local(void* const* bufs, int nsrc, size_t count,
     rx_status_t r = launched(rx::launch_quant(q, dt, fmt, block, stream));
     if (r != RX_OK)
         return r;
+    // On one device the nsrc ranks' low-precision tree steps (each reducing
+    // and requantizing its chunk) and their dequantizations of the gathered
+    // FP8 message collapse into one pass: reduce, requantize, dequantize, and
+    // write the result into every rank's buffer.
     rx::DrrArgs d = {};
     for (int j = 0; j < nsrc; ++j) {
         d.codes[j] = codes[j];
         d.scales[j] = scales[j];
-        d.out_codes[j] = codes[j];     // in place: see rx_lp_reduce_scatter_chunk_bcast
-        d.out_scales[j] = scales[j];
+        d.out_hps[j] = bufs[j];
     }
-    d.nout = nsrc;
+    d.lo = 0;
+    d.hi = count;
     d.block = block;
-    for (int k = 0; k < nsrc; ++k) {
-        rx_lp_tree_chunk(count, nsrc, block, k, &d.lo, &d.hi);
-        if (d.lo >= d.hi)
-            continue;
-        r = launched(rx::launch_drr(d, nsrc, fmt, true, stream));
-        if (r != RX_OK)
-            return r;
-    }
-    for (int j = 0; j < nsrc; ++j) {   // every rank dequantizes the gathered message
-        rx::DrrArgs x = {};
-        x.codes[0] = codes[j];
-        x.scales[0] = scales[j];
-        x.out_hp = bufs[j];
-        x.lo = 0;
-        x.hi = count;
-        x.block = block;
-        x.hp_bf16 = dt;
-        r = launched(rx::launch_drr(x, 1, fmt, false, stream));
-        if (r != RX_OK)
-            return r;
-    }
+    d.hp_bf16 = dt;
+    r = launched(rx::launch_drr(d, nsrc, fmt, true, stream));
+    if (r != RX_OK)
+        return r;
     return RX_OK;
 }
 

@@ -20,7 +20,8 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     const size_t cus = (size_t)device_cu_count();
     const size_t len = a.hi - a.lo;
     const bool small = (len + 1023) / 1024 < kSmallTilesPerCu * cus / 2;
-    const bool fp32_out = a.out_hp != nullptr && !a.hp_bf16;
+    const bool all = requant && a.out_hps[0] != nullptr;   // every rank's buffer
+    const bool fp32_out = (a.out_hp != nullptr || all) && !a.hp_bf16;
     // chunk layout (codes per lane per chunk, chunks per lane); block / CPC <= 64
     int cpc = 16, u = 1;
     if (small) {
@@ -41,7 +42,7 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     // one XCD (measured 8% faster); large messages keep the plain order
     arg.xcd_ranges = small ? 1 : 0;
     void* params[] = {&arg};
-    const int r = requant ? (a.nout > 1 ? 2 : 1) : 0;
+    const int r = !requant ? kDrrSum : all ? kDrrRequantAll : a.nout > 1 ? kDrrRequantPush : kDrrRequant;
     const DrrFn fn = cpc == 4 ? (u == 4 ? drr_fns_4x4().fn[fmt][r][nsrc - 1] : drr_fns_4x1().fn[fmt][r][nsrc - 1])
                    : cpc == 8 ? drr_fns_8x2().fn[fmt][r][nsrc - 1] : drr_fns_16x1().fn[fmt][r][nsrc - 1];
     return hipLaunchKernel((const void*)fn, grid, blk, params, 0, s);

@@ -18,9 +18,12 @@ namespace rx {
 
 using DrrFn = void (*)(DrrArgs);
 
-// [fmt][0 sum, 1 requant, 2 requant to every destination][nsrc - 1]
+// [fmt][mode][nsrc - 1]; modes: 0 sum, 1 requant, 2 requant with the codes
+// pushed to every destination, 3 requant with the dequantized result written
+// to every rank's buffer
+enum { kDrrSum = 0, kDrrRequant = 1, kDrrRequantPush = 2, kDrrRequantAll = 3 };
 struct DrrFns {
-    DrrFn fn[2][3][kMaxSrc];
+    DrrFn fn[2][4][kMaxSrc];
 };
 
 const DrrFns& drr_fns_16x1();
@@ -159,9 +162,12 @@ __device__ __forceinline__ void store_hp(void* out, bool bf16, size_t c, size_t 
     }
 }
 
-// MULTI: the requantized result goes to N destinations, one per rank (the
-// low-precision tree step's push); otherwise to out_codes[0] / out_scales[0].
-template <int F, int N, bool REQUANT, int CPC, int U, bool MULTI>
+// OUT (requantization only): kDrrRequant -> out_codes[0] / out_scales[0]
+// (+ out_hp); kDrrRequantPush -> the codes and scales to N destinations, one
+// per rank (the low-precision tree step's push); kDrrRequantAll -> only the
+// dequantized result, into N buffers out_hps[j] (every rank's final values
+// in a one-device allreduce).
+template <int F, int N, bool REQUANT, int CPC, int U, int OUT>
 __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
 {
     const int lane = lane_id();
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
             for (int p = 0; p < CPC / 4; ++p)
                 q[p] = f32x4_to_fp8<F>(clamp_fmax<F>(S[4 * p + 0] * r2), clamp_fmax<F>(S[4 * p + 1] * r2),
                                        clamp_fmax<F>(S[4 * p + 2] * r2), clamp_fmax<F>(S[4 * p + 3] * r2));
-            if constexpr (MULTI) {
+            if constexpr (OUT == kDrrRequantPush) {
                 // push the chunk to every destination (one per rank: nout == N,
                 // so the loop unrolls and the pointers load once)
 #pragma unroll
@@ -243,13 +249,19 @@ __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
                     for (int j = 0; j < N; ++j)
                         a.out_scales[j][b[u]] = s2;
                 }
-            } else {
+            } else if constexpr (OUT == kDrrRequant) {
                 store_codes<CPC>(static_cast<uint8_t*>(a.out_codes[0]), c[u], e[u], count, whole[u], q);
                 if (valid[u] && (lane % lpb) == 0)
                     a.out_scales[0][b[u]] = s2;
             }
 
-            if (a.out_hp) {
+            if constexpr (OUT == kDrrRequantAll) {
+                float h[CPC];
+                dequant<F, CPC>(q, s2, h);
+#pragma unroll
+                for (int j = 0; j < N; ++j)
+                    store_hp<CPC>(a.out_hps[j], a.hp_bf16 != 0, c[u], e[u], count, whole[u], h);
+            } else if (a.out_hp) {
                 float h[CPC];
                 dequant<F, CPC>(q, s2, h);
                 store_hp<CPC>(a.out_hp, a.hp_bf16 != 0, c[u], e[u], count, whole[u], h);
@@ -259,10 +271,10 @@ __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
 }
 
 
-template <int F, bool R, int CPC, int U, bool M, int... I>
+template <int F, bool R, int CPC, int U, int OUT, int... I>
 void fill_row(DrrFn* row, std::integer_sequence<int, I...>)
 {
-    ((row[I] = &k_drr<F, I + 1, R, CPC, U, M>), ...);
+    ((row[I] = &k_drr<F, I + 1, R, CPC, U, OUT>), ...);
 }
 
 template <int CPC, int U>
@@ -270,12 +282,14 @@ DrrFns make_fns()
 {
     DrrFns t{};
     const auto seq = std::make_integer_sequence<int, kMaxSrc>{};
-    fill_row<0, false, CPC, U, false>(t.fn[0][0], seq);
-    fill_row<0, true, CPC, U, false>(t.fn[0][1], seq);
-    fill_row<0, true, CPC, U, true>(t.fn[0][2], seq);
-    fill_row<1, false, CPC, U, false>(t.fn[1][0], seq);
-    fill_row<1, true, CPC, U, false>(t.fn[1][1], seq);
-    fill_row<1, true, CPC, U, true>(t.fn[1][2], seq);
+    fill_row<0, false, CPC, U, kDrrSum>(t.fn[0][kDrrSum], seq);
+    fill_row<0, true, CPC, U, kDrrRequant>(t.fn[0][kDrrRequant], seq);
+    fill_row<0, true, CPC, U, kDrrRequantPush>(t.fn[0][kDrrRequantPush], seq);
+    fill_row<0, true, CPC, U, kDrrRequantAll>(t.fn[0][kDrrRequantAll], seq);
+    fill_row<1, false, CPC, U, kDrrSum>(t.fn[1][kDrrSum], seq);
+    fill_row<1, true, CPC, U, kDrrRequant>(t.fn[1][kDrrRequant], seq);
+    fill_row<1, true, CPC, U, kDrrRequantPush>(t.fn[1][kDrrRequantPush], seq);
+    fill_row<1, true, CPC, U, kDrrRequantAll>(t.fn[1][kDrrRequantAll], seq);
     return t;
 }
 

@@ -38,6 +38,7 @@ struct DrrArgs {
     void* out_codes[kMaxSrc];    // REQUANT: nout code buffers (message-indexed)
     float* out_scales[kMaxSrc];  // REQUANT: nout scale buffers (block-indexed)
     void* out_hp;                // SUM: required; REQUANT: optional
+    void* out_hps[kMaxSrc];      // REQUANT to every rank's buffer: N outputs
     size_t lo, hi;               // element range processed; lo is a block multiple
     int nout;                    // REQUANT: destinations that receive the result
     int block;                   // elements per scale block

@@ -36,6 +36,17 @@ __global__ void k_dec(const uint8_t* in, size_t n, float* out)
         if (i4 + k < n) out[i4 + k] = d[k];
 }
 
+template <int F>
+__global__ void k_scale_bits(uint32_t first, size_t n, float* s, float* r)
+{
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float sv, rv;
+    block_scale<F>(bits_f32(first + (uint32_t)i), sv, rv);
+    s[i] = sv;
+    r[i] = rv;
+}
+
 __global__ void k_bf16_bits(uint32_t first, size_t n, uint16_t* out)
 {
     const size_t i2 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 2;
@@ -84,6 +95,20 @@ rx_status_t rxtest_fp8_decode(const uint8_t* in, size_t n, rx_dtype_t fmt,
         hipLaunchKernelGGL(rx::k_dec<rx::kE4M3>, dim3(rx::blocks_for(th)), dim3(256), 0, stream, in, n, out);
     else
         hipLaunchKernelGGL(rx::k_dec<rx::kE5M2>, dim3(rx::blocks_for(th)), dim3(256), 0, stream, in, n, out);
+    return hipGetLastError() == hipSuccess ? RX_OK : RX_ERR_HIP;
+}
+
+rx_status_t rxtest_block_scale_bits(uint32_t first, size_t n, rx_dtype_t fmt,
+                                    float* s, float* r, hipStream_t stream)
+{
+    if (!s || !r) return RX_ERR_NULL;
+    if (fmt != RX_FP8_E4M3 && fmt != RX_FP8_E5M2) return RX_ERR_DTYPE;
+    if ((size_t)first + n > 0x7F800000u) return RX_ERR_ARG;
+    if (n == 0) return RX_OK;
+    if (fmt == RX_FP8_E4M3)
+        hipLaunchKernelGGL(rx::k_scale_bits<rx::kE4M3>, dim3(rx::blocks_for(n)), dim3(256), 0, stream, first, n, s, r);
+    else
+        hipLaunchKernelGGL(rx::k_scale_bits<rx::kE5M2>, dim3(rx::blocks_for(n)), dim3(256), 0, stream, first, n, s, r);
     return hipGetLastError() == hipSuccess ? RX_OK : RX_ERR_HIP;
 }
 

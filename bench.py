@@ -44,6 +44,8 @@ KERNEL_SOURCES = {
     "quant_fp8": ["quant.hip", "rx_device.hpp"],
     "dequant_reduce_requant": ["drr.hpp", "drr.hip", "rx_device.hpp"],
     "lp_tree_step": ["drr.hpp", "drr.hip", "rx_device.hpp"],
+    "allreduce_local_flat": ["reduce.hip", "rx_device.hpp"],
+    "allreduce_local_lowprec": ["quant.hip", "drr.hpp", "drr.hip", "rx_device.hpp"],
 }
 # rocprofv3 kernel names (substrings of the mangled names)
 KERNEL_SYMBOLS = {
@@ -52,6 +54,8 @@ KERNEL_SYMBOLS = {
     "quant_fp8": "k_quant",
     "dequant_reduce_requant": "k_drr",
     "lp_tree_step": "k_drr",
+    "allreduce_local_flat": "k_tree",
+    "allreduce_local_lowprec": "k_quant, k_drr",
 }
 
 
@@ -166,7 +170,13 @@ def main():
     }
     step_bytes = sum(bytes_k.values())
     # measured beside the step, not part of it: the low-precision tree step
+    # and the whole local allreduce (every buffer read once and written once;
+    # low precision: quantize every buffer, then one pass that reduces,
+    # requantizes, dequantizes and writes every buffer)
     bytes_k["lp_tree_step"] = 2 * n * (lp_chunk + 4 * (lp_chunk // lp_block))
+    bytes_k["allreduce_local_flat"] = 2 * n * count * e
+    bytes_k["allreduce_local_lowprec"] = (n * (count * e + count + 4 * nb)   # quantize
+                                          + n * (count + 4 * nb) + n * count * e)  # reduce + write all
     per_batch_bytes = (n * count * e            # sources
                        + count * e              # flat out
                        + n * count * e          # tree destinations
@@ -209,7 +219,22 @@ def main():
         for _, fn in kernels:
             fn(b, i)
 
-    kernels_timed = kernels + [("lp_tree_step", k_lp_tree)]
+    # whole in-place local allreduce (rx_allreduce_local), on buffers of
+    # zeros so that repeated in-place sums stay finite (kernel time does not
+    # depend on the values)
+    ar_bufs = [[torch.zeros(count, dtype=tdt, device=dev) for _ in range(n)]
+               for _ in range(max(1, min(nsets, 32)))]
+    ws_bytes = rx.rx_allreduce_local_workspace(n, count, lp_block)
+    ar_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def k_ar_flat(b, i):
+        rx.rx_allreduce_local(ar_bufs[i % len(ar_bufs)], rx.RX_ALGO_FLAT, lp_fmt, lp_block)
+
+    def k_ar_lp(b, i):
+        rx.rx_allreduce_local(ar_bufs[i % len(ar_bufs)], rx.RX_ALGO_LOWPREC, lp_fmt, lp_block, ar_ws)
+
+    kernels_timed = kernels + [("lp_tree_step", k_lp_tree), ("allreduce_local_flat", k_ar_flat),
+                               ("allreduce_local_lowprec", k_ar_lp)]
 
     def capture(calls):
         """HIP graph of the given launches (captured on torch's capture

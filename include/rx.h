@@ -223,11 +223,12 @@ typedef enum {
  *                   FP32 left fold into all of them.
  *   RX_ALGO_TREE    rx_reduce_scatter_chunk_bcast for every rank k in turn
  *                   ("Core feature 1", DDA Tree); same result as FLAT.
- *   RX_ALGO_LOWPREC rx_quant_fp8 of every buffer, rx_lp_reduce_scatter_chunk_
- *                   bcast for every rank k (in place on the workspace), then
- *                   every rank dequantizes the gathered FP8 message into its
- *                   buffer ("Core feature 2"); every buffer receives
- *                   dequant(requant(FP32 sum of the dequantized inputs)).
+ *   RX_ALGO_LOWPREC rx_quant_fp8 of every buffer into the workspace, then
+ *                   what every rank's rx_lp_reduce_scatter_chunk_bcast and
+ *                   its dequantization of the gathered FP8 message compute
+ *                   ("Core feature 2"), which on one device is one pass:
+ *                   every buffer receives dequant(requant(FP32 sum of the
+ *                   dequantized inputs)).
  *   RX_ALGO_AUTO    RX_ALGO_LOWPREC when the environment variable
  *                   RX_LOW_PRECISION_ENABLE is "1" and a buffer is >= 16 MiB
  *                   (the article's activation switch and threshold),

@@ -29,6 +29,13 @@ rx_status_t rxtest_fp8_decode(const uint8_t* in, size_t n, rx_dtype_t fmt,
 rx_status_t rxtest_bf16_round_bits(uint32_t first, size_t n, uint16_t* out,
                                    hipStream_t stream);
 
+/* s[i], r[i] = the kernels' block scale and reciprocal for the block absmax
+ * A = FP32 pattern (first + i): s = A / FMAX, r = FMAX / A (correctly rounded
+ * divisions), s = r = 1 for A == 0, s == 0 or r not finite. Patterns must be
+ * finite and non-negative: first + n <= 0x7F800000. */
+rx_status_t rxtest_block_scale_bits(uint32_t first, size_t n, rx_dtype_t fmt,
+                                    float* s, float* r, hipStream_t stream);
+
 /* For each wave of 64 values in in[0 .. 64*nwaves): out[l] = max of in over
  * the aligned group of g lanes that holds lane l (g = 1, 2, 4, ..., 64),
  * computed with the kernels' DPP / permlane group maximum. */

@@ -46,6 +46,7 @@ def lib():
             "rxo_f32_to_bf16_array": (None, [_P, _SZ, _P]),
             "rxo_fp8_decode_array": (None, [_P, _SZ, _I, _P]),
             "rxo_block_scale": (None, [_P, _SZ, _I, _P, _P]),
+            "rxo_block_scale_bits_range": (None, [ctypes.c_uint32, ctypes.c_uint32, _I, _P, _P]),
             "rxo_reduce_flat": (None, [_P, _I, _SZ, _I, _P]),
             "rxo_tree_chunk": (None, [_SZ, _I, _I, _I, _P, _P]),
             "rxo_reduce_scatter_chunk_bcast": (None, [_P, _I, _SZ, _I, _I, _P]),
@@ -124,6 +125,13 @@ def block_scale(x: np.ndarray, fmt: int) -> Tuple[float, float]:
     r = ctypes.c_float()
     lib().rxo_block_scale(x.ctypes.data, x.size, fmt, ctypes.byref(s), ctypes.byref(r))
     return s.value, r.value
+
+
+def block_scale_bits(first: int, n: int, fmt: int) -> Tuple[np.ndarray, np.ndarray]:
+    s = np.empty(n, dtype=np.float32)
+    r = np.empty(n, dtype=np.float32)
+    lib().rxo_block_scale_bits_range(first, n, fmt, s.ctypes.data, r.ctypes.data)
+    return s, r
 
 
 # ---- hot-path operations -------------------------------------------------

@@ -276,6 +276,16 @@ void rxo_block_scale(const float* x, size_t len, int fmt, float* s, float* r)
     *r = rv;
 }
 
+void rxo_block_scale_bits_range(uint32_t first, uint32_t n, int fmt, float* s, float* r)
+{
+    for (uint32_t i = 0; i < n; ++i) {
+        uint32_t u = first + i;
+        float a;
+        memcpy(&a, &u, sizeof a);
+        rxo_block_scale(&a, 1, fmt, s + i, r + i);
+    }
+}
+
 /* Quantize one block of FP32 values into codes and return its scale. */
 static float quant_block(const float* x, size_t len, int fmt, uint8_t* codes)
 {

@@ -70,6 +70,9 @@ void rxo_fp8_decode_array(const uint8_t* in, size_t n, int fmt, float* out);
 /* ---- block scale ------------------------------------------------------ */
 /* Scale and reciprocal of one block of FP32 values (already widened). */
 void rxo_block_scale(const float* x, size_t len, int fmt, float* s, float* r);
+/* Test helper: s[i], r[i] of the one-element block {A}, A = FP32 pattern
+ * (first + i). */
+void rxo_block_scale_bits_range(uint32_t first, uint32_t n, int fmt, float* s, float* r);
 
 /* ---- hot-path operations ---------------------------------------------- */
 /* y[i] = cast(fold_r x_r[i]); dtype FP32 or BF16 for sources and dst. */

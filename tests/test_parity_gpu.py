@@ -475,6 +475,37 @@ def test_fp8_encode_exhaustive(fmt):
 
 
 @pytest.mark.parametrize("fmt", [O.E4M3, O.E5M2])
+def test_block_scale_exhaustive(fmt):
+    """The kernels' block scale and reciprocal (two correctly rounded FP32
+    divisions, degenerate blocks -> 1) for every finite non-negative FP32
+    block absmax A, including zero, subnormals and the thresholds where
+    A / FMAX underflows or FMAX / A overflows, against the oracle."""
+    from concurrent.futures import ThreadPoolExecutor
+    end = 0x7F800000
+    s_d = torch.empty(CHUNK, dtype=torch.float32, device=DEV)
+    r_d = torch.empty(CHUNK, dtype=torch.float32, device=DEV)
+    for first in range(0, end, CHUNK):
+        n = min(CHUNK, end - first)
+        log(f"block scale sweep fmt={fmt} first={first:#x}")
+        rx.rxtest_block_scale_bits(first, n, FMTS[fmt], s_d, r_d)
+        sync()
+        gs, gr = s_d[:n].cpu().numpy(), r_d[:n].cpu().numpy()
+        rs, rr = np.empty(n, np.float32), np.empty(n, np.float32)
+        per = -(-n // 16)
+
+        def job(t):
+            lo, hi = t * per, min(n, (t + 1) * per)
+            if lo < hi:
+                rs[lo:hi], rr[lo:hi] = O.block_scale_bits(first + lo, hi - lo, fmt)
+        with ThreadPoolExecutor(16) as ex:
+            list(ex.map(job, range(16)))
+        for name, g, r in (("s", gs, rs), ("r", gr, rr)):
+            bad = np.nonzero(g.view(np.uint32) != r.view(np.uint32))[0]
+            assert bad.size == 0, (f"{name}: {bad.size} mismatches, first A pattern "
+                                   f"{first + bad[0]:#010x}: got {g[bad[0]]!r} want {r[bad[0]]!r}")
+
+
+@pytest.mark.parametrize("fmt", [O.E4M3, O.E5M2])
 def test_fp8_decode_all_codes(fmt):
     codes = torch.arange(256, dtype=torch.int32, device=DEV).to(torch.uint8)
     out = torch.empty(256, dtype=torch.float32, device=DEV)
