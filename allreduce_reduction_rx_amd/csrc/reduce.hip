@@ -62,7 +62,7 @@ __device__ __forceinline__ u32x4 fold_vec(const void* const* src, size_t v)
 
 // One element i (tail of a count that is not a multiple of 16 bytes).
 template <int DT, int N>
-__device__ __forceinline__ float fold_elem(const void* const* src, size_t i)
+__device__ __forceinline__ float fold_vec_tail(const void* const* src, size_t i)
 {
     float acc;
     if constexpr (DT == 0) {
@@ -88,6 +88,7 @@ __device__ __forceinline__ void store_elem(void* dst, size_t i, float v)
         static_cast<uint16_t*>(dst)[i] = (uint16_t)(pack_bf16(v, 0.0f) & 0xFFFFu);
 }
 
+// Decode-size messages: one 16-byte output vector per thread.
 template <int DT, int N>
 __global__ __launch_bounds__(256) void k_reduce_flat(FlatArgs a)
 {
@@ -99,7 +100,40 @@ __global__ __launch_bounds__(256) void k_reduce_flat(FlatArgs a)
         st16(a.dst, v, fold_vec<DT, N, true>(a.src, v));
     const size_t i = nvec * VE + gid;
     if (i < a.count)
-        store_elem<DT>(a.dst, i, fold_elem<DT, N>(a.src, i));
+        store_elem<DT>(a.dst, i, fold_vec_tail<DT, N>(a.src, i));
+}
+
+// Large messages: each wave takes tiles of U x 64 vectors (vector u * 64 +
+// lane of the tile), loads all sources of all U vectors, then issues its U
+// nontemporal stores back to back. Batching the writes of a wave measured
+// ~5% faster on MI355X than one store after every fold.
+template <int DT, int N>
+__global__ __launch_bounds__(256) void k_reduce_flat_tiles(FlatArgs a)
+{
+    constexpr int VE = Elem<DT>::kVE;
+    constexpr int U = N <= 8 ? 4 : 2;
+    const int lane = lane_id();
+    const uint32_t wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const size_t wave = (size_t)blockIdx.x * (blockDim.x / kWave) + wave_in_wg;
+    const size_t nwaves = (size_t)gridDim.x * (blockDim.x / kWave);
+    const size_t nvec = a.count / VE;
+    const size_t ntiles = (nvec + (size_t)U * kWave - 1) / ((size_t)U * kWave);
+    for (size_t t = wave; t < ntiles; t += nwaves) {
+        const size_t base = t * U * kWave + lane;
+        u32x4 y[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (base + u * kWave < nvec)
+                y[u] = fold_vec<DT, N, true>(a.src, base + u * kWave);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (base + u * kWave < nvec)
+                st16_stream(a.dst, base + u * kWave, y[u]);
+    }
+    const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t i = nvec * VE + gid;
+    if (i < a.count)
+        store_elem<DT>(a.dst, i, fold_vec_tail<DT, N>(a.src, i));
 }
 
 template <int DT, int N>
@@ -119,7 +153,7 @@ __global__ __launch_bounds__(256) void k_tree(TreeArgs a)
     // hi is a multiple of VE unless it is the end of a ragged message
     const size_t i = (v1 > v0 ? v1 : v0) * VE + gid;
     if (i >= a.lo && i < a.hi) {
-        float z = fold_elem<DT, N>(a.src, i);
+        float z = fold_vec_tail<DT, N>(a.src, i);
 #pragma unroll
         for (int j = 0; j < N; ++j)
             store_elem<DT>(a.dst[j], i, z);
@@ -135,6 +169,11 @@ constexpr std::array<FlatFn, sizeof...(I)> flat_table(std::integer_sequence<int,
     return {{&k_reduce_flat<DT, I + 1>...}};
 }
 template <int DT, int... I>
+constexpr std::array<FlatFn, sizeof...(I)> flat_tiles_table(std::integer_sequence<int, I...>)
+{
+    return {{&k_reduce_flat_tiles<DT, I + 1>...}};
+}
+template <int DT, int... I>
 constexpr std::array<TreeFn, sizeof...(I)> tree_table(std::integer_sequence<int, I...>)
 {
     return {{&k_tree<DT, I + 1>...}};
@@ -143,6 +182,9 @@ constexpr std::array<TreeFn, sizeof...(I)> tree_table(std::integer_sequence<int,
 const std::array<FlatFn, kMaxSrc> kFlat[2] = {
     flat_table<0>(std::make_integer_sequence<int, kMaxSrc>{}),
     flat_table<1>(std::make_integer_sequence<int, kMaxSrc>{})};
+const std::array<FlatFn, kMaxSrc> kFlatTiles[2] = {
+    flat_tiles_table<0>(std::make_integer_sequence<int, kMaxSrc>{}),
+    flat_tiles_table<1>(std::make_integer_sequence<int, kMaxSrc>{})};
 const std::array<TreeFn, kMaxSrc> kTree[2] = {
     tree_table<0>(std::make_integer_sequence<int, kMaxSrc>{}),
     tree_table<1>(std::make_integer_sequence<int, kMaxSrc>{})};
@@ -161,11 +203,14 @@ bool small_job(size_t threads) { return threads < kSmallThreadsPerCu * (size_t)d
 hipError_t launch_reduce_flat(const FlatArgs& a, int nsrc, int dtype, hipStream_t s)
 {
     const int ve = dtype == 0 ? 4 : 8;
+    const size_t nvec = a.count / ve;
+    const bool small = small_job(nvec);
     dim3 grid, block;
-    launch_geometry(a.count / ve, small_job(a.count / ve), policy_flat(), grid, block);
+    launch_geometry(nvec, small, policy_flat(), grid, block);
     FlatArgs arg = a;
     void* params[] = {&arg};
-    return hipLaunchKernel((const void*)kFlat[dtype][nsrc - 1], grid, block, params, 0, s);
+    const FlatFn fn = small ? kFlat[dtype][nsrc - 1] : kFlatTiles[dtype][nsrc - 1];
+    return hipLaunchKernel((const void*)fn, grid, block, params, 0, s);
 }
 
 hipError_t launch_tree(const TreeArgs& a, int nsrc, int dtype, hipStream_t s)

@@ -86,6 +86,28 @@ def test_flat_in_place(dtype):
         assert bits_equal(got, ref), f"alias {j}: " + first_mismatch(got, ref)
 
 
+@pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
+@pytest.mark.parametrize("n", [2, 8, 16])
+def test_flat_large_variant_ragged(n, dtype):
+    # above the decode-size threshold: wave tiles with deferred stores and a
+    # grid-stride loop; ragged element tail; also in place
+    count = 3 * (1 << 20) + 5
+    srcs = [G.fill(count, dtype, G.NORMAL_OUTLIER, seed=1500 + n, rank=r) for r in range(n)]
+    ref = O.reduce_flat(srcs, dtype)
+    g = Guarded(count, TD[dtype])
+    ts = [to_gpu(s) for s in srcs]
+    log(f"flat large n={n} dtype={dtype}")
+    rx.rx_reduce_flat(ts, g.t)
+    sync()
+    got = to_host(g.t)
+    assert bits_equal(got, ref), first_mismatch(got, ref)
+    assert g.guards_intact()
+    rx.rx_reduce_flat(ts, ts[n - 1])
+    sync()
+    got = to_host(ts[n - 1])
+    assert bits_equal(got, ref), "in place: " + first_mismatch(got, ref)
+
+
 def test_flat_order_and_accumulation():
     # FP32 left fold in source order: ((1e8 + 1) - 1e8) == 0 but
     # ((1e8 - 1e8) + 1) == 1; BF16 {256, 1 x 7} -> 264 needs FP32 accumulation.
