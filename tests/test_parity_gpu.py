@@ -174,6 +174,18 @@ def test_tree_shapes(n, dtype):
             _tree_case(srcs, dtype, count, k)
 
 
+@pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
+@pytest.mark.parametrize("n", [3, 8, 16])
+def test_tree_large_variant_ragged(n, dtype):
+    # chunks above the decode-size threshold (the tiled kernel for BF16),
+    # ragged message end, first and last rank
+    count = n * (1 << 20) + 9
+    srcs = [G.fill(count, dtype, G.NORMAL, seed=2500 + n, rank=r) for r in range(n)]
+    for k in (0, n - 1):
+        log(f"tree large n={n} dtype={dtype} rank={k}")
+        _tree_case(srcs, dtype, count, k)
+
+
 def test_tree_in_place():
     n, count, dtype = 8, 65536 + 24, O.BF16
     srcs = [G.fill(count, dtype, G.NORMAL, seed=99, rank=r) for r in range(n)]
