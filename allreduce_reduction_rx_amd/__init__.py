@@ -36,7 +36,7 @@ EXPORTED_SYMBOLS = (
     "rx_quant_fp8", "rx_dequant_reduce_requant", "rx_status_string",
     "rx_lp_reduce_scatter_chunk_bcast", "rx_lp_tree_chunk", "rx_allreduce_local",
     "rx_allreduce_local_workspace", "rxtest_block_scale_bits", "rxtest_fp8_encode_bits", "rxtest_fp8_decode", "rxtest_bf16_round_bits",
-    "rxtest_group_max",
+    "rxtest_group_max", "rxtest_stream", "rxtest_stream_sink_bytes",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -83,11 +83,14 @@ def lib() -> ctypes.CDLL:
             "rxtest_fp8_decode": [_P, _SZ, _I, _P, _P],
             "rxtest_bf16_round_bits": [ctypes.c_uint32, _SZ, _P, _P],
             "rxtest_group_max": [_P, _SZ, _I, _P, _P],
+            "rxtest_stream": [_I, _P, _P, _SZ, _I, _I, _P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        L.rxtest_stream_sink_bytes.argtypes = [_I]
+        L.rxtest_stream_sink_bytes.restype = ctypes.c_size_t
         L.rx_allreduce_local_workspace.argtypes = [_I, _SZ, _I]
         L.rx_allreduce_local_workspace.restype = ctypes.c_size_t
         L.rx_status_string.argtypes = [_I]
@@ -341,3 +344,19 @@ def rxtest_bf16_round_bits(first: int, n: int, out, stream=None) -> None:
 def rxtest_group_max(values, g: int, out, stream=None) -> None:
     _check(lib().rxtest_group_max(values.data_ptr(), values.numel() // 64, g, out.data_ptr(),
                                   _stream(stream)), "rxtest_group_max")
+
+
+RXTEST_READ, RXTEST_WRITE, RXTEST_COPY = 0, 1, 2
+
+
+def rxtest_stream_sink_bytes(wgs_per_cu: int) -> int:
+    return int(lib().rxtest_stream_sink_bytes(wgs_per_cu))
+
+
+def rxtest_stream(kind: int, src, dst, nbytes: int, wgs_per_cu: int = 1, nontemporal: bool = False,
+                  stream=None) -> None:
+    """Streaming ceiling kernel (read / write / copy) over nbytes; for a read,
+    dst is the per-thread XOR sink of rxtest_stream_sink_bytes(wgs_per_cu)."""
+    _check(lib().rxtest_stream(kind, src.data_ptr() if src is not None else None, dst.data_ptr(),
+                               nbytes, wgs_per_cu, int(bool(nontemporal)), _stream(stream)),
+           "rxtest_stream")

@@ -1,0 +1,111 @@
+// ceiling.hip -- plain streaming kernels (read, write, copy; 16 bytes per
+// lane per access) that measure the HBM ceilings the hot-path kernels are
+// compared against on the same GPU in the same run.
+#include <stdint.h>
+
+#include "rx_device.hpp"
+#include "rx_internal.hpp"
+#include "rx_testhooks.h"
+
+namespace rx {
+namespace {
+
+constexpr int kCeilU = 4;                               // vectors per lane per tile
+constexpr size_t kCeilTile = (size_t)kWave * kCeilU;    // vectors per wave tile
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld(const void* p, size_t v)
+{
+    if constexpr (NT) return ld16_stream(p, v);
+    else return ld16(p, v);
+}
+
+template <bool NT>
+__device__ __forceinline__ void st(void* p, size_t v, u32x4 x)
+{
+    if constexpr (NT) st16_stream(p, v, x);
+    else st16(p, v, x);
+}
+
+// Wave tiles of kCeilU contiguous 64-vector rows, grid-stride over the waves
+// of the launch. KIND 0: read, XOR into a per-thread sum written once at the
+// end (16 bytes per thread); 1: write a constant pattern; 2: copy.
+template <int KIND, bool NT>
+__global__ __launch_bounds__(256) void k_stream(const void* __restrict__ src, void* __restrict__ dst,
+                                                size_t nvec, u32x4 pattern)
+{
+    const size_t waves = (size_t)gridDim.x * (blockDim.x / kWave);
+    const size_t wave = (size_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const size_t lane = threadIdx.x % kWave;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (size_t t = wave; t * kCeilTile < nvec; t += waves) {
+        const size_t base = t * kCeilTile + lane;
+        if ((t + 1) * kCeilTile <= nvec) {
+            if constexpr (KIND == 0) {
+                u32x4 x[kCeilU];
+#pragma unroll
+                for (int u = 0; u < kCeilU; ++u) x[u] = ld<NT>(src, base + (size_t)u * kWave);
+#pragma unroll
+                for (int u = 0; u < kCeilU; ++u) acc ^= x[u];
+            } else if constexpr (KIND == 1) {
+#pragma unroll
+                for (int u = 0; u < kCeilU; ++u) st<NT>(dst, base + (size_t)u * kWave, pattern);
+            } else {
+                u32x4 x[kCeilU];
+#pragma unroll
+                for (int u = 0; u < kCeilU; ++u) x[u] = ld<NT>(src, base + (size_t)u * kWave);
+#pragma unroll
+                for (int u = 0; u < kCeilU; ++u) st<NT>(dst, base + (size_t)u * kWave, x[u]);
+            }
+        } else {
+            for (int u = 0; u < kCeilU; ++u) {
+                const size_t v = base + (size_t)u * kWave;
+                if (v >= nvec) break;
+                if constexpr (KIND == 0) acc ^= ld16(src, v);
+                else if constexpr (KIND == 1) st16(dst, v, pattern);
+                else st16(dst, v, ld16(src, v));
+            }
+        }
+    }
+    if constexpr (KIND == 0)
+        st16(dst, (size_t)blockIdx.x * blockDim.x + threadIdx.x, acc);
+}
+
+typedef void (*StreamFn)(const void*, void*, size_t, u32x4);
+const StreamFn kStream[3][2] = {
+    {k_stream<0, false>, k_stream<0, true>},
+    {k_stream<1, false>, k_stream<1, true>},
+    {k_stream<2, false>, k_stream<2, true>},
+};
+
+}  // namespace
+}  // namespace rx
+
+extern "C" {
+
+size_t rxtest_stream_sink_bytes(int wgs_per_cu)
+{
+    if (wgs_per_cu < 1 || wgs_per_cu > 8) return 0;
+    return (size_t)rx::device_cu_count() * (size_t)wgs_per_cu * 256u * 16u;
+}
+
+rx_status_t rxtest_stream(int kind, const void* src, void* dst, size_t bytes, int wgs_per_cu,
+                          int nontemporal, hipStream_t stream)
+{
+    if (kind < 0 || kind > 2 || wgs_per_cu < 1 || wgs_per_cu > 8) return RX_ERR_ARG;
+    if (!dst || (kind != 1 && !src)) return RX_ERR_NULL;
+    if (bytes % 16 || (uintptr_t)dst % 16 || (uintptr_t)src % 16) return RX_ERR_ALIGN;
+    if (bytes == 0) return RX_OK;
+    const unsigned grid = (unsigned)(rx::device_cu_count() * wgs_per_cu);
+    const rx::u32x4 pattern = {0x3F800000u, 0x40000000u, 0x40400000u, 0x40800000u};
+    void* args_dst = dst;
+    const void* args_src = src;
+    size_t nvec = bytes / 16;
+    rx::u32x4 pat = pattern;
+    void* params[] = {&args_src, &args_dst, &nvec, &pat};
+    const hipError_t e = hipLaunchKernel((const void*)rx::kStream[kind][nontemporal ? 1 : 0],
+                                         dim3(grid), dim3(256), params, 0, stream);
+    return e == hipSuccess && hipGetLastError() == hipSuccess ? RX_OK : RX_ERR_HIP;
+}
+
+}  // extern "C"

@@ -307,7 +307,11 @@ def main():
     traffic = read_traffic(dominant, args.workload)
     value = step_bytes / (step_ms * 1e-3) / 1e9
 
+    us_single, us_events = single_launch_us(torch, rx, k_flat, batches, stream)
     copy = copy_ceiling(torch, stream)
+    ceil = stream_ceilings(torch, rx, stream)
+    for k in per_kernel.values():
+        k["frac_of_copy_ceiling"] = round(k["GB/s"] / ceil["copy"]["GB/s"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -346,8 +350,11 @@ def main():
         },
         "kernels": per_kernel,
         "us_reduce_flat": per_kernel["reduce_flat"]["us"],
+        "us_reduce_flat_single_launch": us_single,
+        "us_event_pair_alone": us_events,
         "tree_matches_flat": bool(tree_ok),
         "copy_ceiling": copy,
+        "stream_ceilings": ceil,
         "wall_s": round(wall_s, 4),
         "launch": "python loop" if args.no_graph else "HIP graph replay",
         "cpu_baseline": cpu,
@@ -377,6 +384,75 @@ def copy_ceiling(torch, stream):
     torch.cuda.empty_cache()
     return {"GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
             "bytes": 2 * nbytes, "us": round(us, 1)}
+
+
+def stream_ceilings(torch, rx, stream):
+    """Read, write and copy rates of the library's plain 16-byte-per-lane
+    streaming kernels over 1 GiB (4x the Infinity Cache), best over 1, 2, 4
+    and 8 workgroups per CU with and without nontemporal hints: the HBM
+    ceilings a streaming kernel reaches on this GPU. Bytes counted: read +
+    written."""
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    sink = torch.empty(rx.rxtest_stream_sink_bytes(8) // 4, dtype=torch.float32, device="cuda:0")
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for kind, name, moved in ((rx.RXTEST_READ, "read", nbytes), (rx.RXTEST_WRITE, "write", nbytes),
+                              (rx.RXTEST_COPY, "copy", 2 * nbytes)):
+        best = None
+        for wgs in (1, 2, 4, 8):
+            for nt in (False, True):
+                d = sink if kind == rx.RXTEST_READ else dst
+                run = lambda: rx.rxtest_stream(kind, src, d, nbytes, wgs, nt, stream)
+                run(); run()
+                reps = 10
+                torch.cuda.synchronize()
+                a.record(stream)
+                for _ in range(reps):
+                    run()
+                z.record(stream)
+                torch.cuda.synchronize()
+                us = a.elapsed_time(z) * 1000.0 / reps
+                gbs = moved / (us * 1e-6) / 1e9
+                if best is None or gbs > best["GB/s"]:
+                    best = {"GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+                            "wgs_per_cu": wgs, "nontemporal": nt}
+        out[name] = best
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return out
+
+
+def single_launch_us(torch, rx, fn, batches, stream, reps=200):
+    """Median µs of one launch on its own (the GPU-side dispatch included),
+    bracketed by its own HIP events. Each launch is queued behind a 512 MiB
+    streaming read, so the host has enqueued the events and the launch before
+    the GPU reaches them and no host-side call overhead is timed; the read
+    also leaves the caches cold. Rotates over the cold batches."""
+    nbytes = 512 << 20
+    busy = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(0.0)
+    sink = torch.empty(rx.rxtest_stream_sink_bytes(2) // 4, dtype=torch.float32, device="cuda:0")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps + 10)]
+    torch.cuda.synchronize()
+    for i, (a, z) in enumerate(evs):
+        rx.rxtest_stream(rx.RXTEST_READ, busy, sink, nbytes, 2, True, stream)
+        a.record(stream)
+        fn(batches[i % len(batches)], i)
+        z.record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(z) * 1000.0 for a, z in evs[10:])
+    # the same pair of events with nothing between them
+    for a, z in evs:
+        rx.rxtest_stream(rx.RXTEST_READ, busy, sink, nbytes, 2, True, stream)
+        a.record(stream)
+        z.record(stream)
+    torch.cuda.synchronize()
+    t0 = sorted(a.elapsed_time(z) * 1000.0 for a, z in evs[10:])
+    del busy, sink
+    torch.cuda.empty_cache()
+    return round(ts[len(ts) // 2], 3), round(t0[len(t0) // 2], 3)
 
 
 def cpu_baseline(w, host, lp_fmt, lp_block, seconds, step_bytes):

@@ -42,6 +42,26 @@ rx_status_t rxtest_block_scale_bits(uint32_t first, size_t n, rx_dtype_t fmt,
 rx_status_t rxtest_group_max(const uint32_t* in, size_t nwaves, int g,
                              uint32_t* out, hipStream_t stream);
 
+/* Streaming ceiling kernels: the HBM rates that plain 16-byte-per-lane
+ * streams reach on this GPU, measured beside the hot-path kernels.
+ *   kind 0 (read):  reads `bytes` of src; every thread XORs what it read
+ *                   and stores its 16-byte sum into dst[thread], so the XOR
+ *                   of dst over rxtest_stream_sink_bytes(wgs_per_cu) bytes
+ *                   equals the XOR of the 16-byte words of src.
+ *   kind 1 (write): fills dst[0 .. bytes) with the FP32 pattern 1, 2, 3, 4
+ *                   repeated; src is ignored (may be NULL).
+ *   kind 2 (copy):  dst[0 .. bytes) = src[0 .. bytes).
+ * Launch: wgs_per_cu (1..8) workgroups of 256 threads per compute unit,
+ * grid-stride over wave tiles of 4 vectors per lane; nontemporal != 0 uses
+ * nontemporal loads and stores. bytes, src and dst must be multiples of 16
+ * (RX_ERR_ALIGN); src and dst must not overlap. */
+rx_status_t rxtest_stream(int kind, const void* src, void* dst, size_t bytes,
+                          int wgs_per_cu, int nontemporal, hipStream_t stream);
+
+/* Size in bytes of the read kernel's dst for this wgs_per_cu (0 if out of
+ * range). */
+size_t rxtest_stream_sink_bytes(int wgs_per_cu);
+
 #ifdef __cplusplus
 }
 #endif

@@ -177,3 +177,20 @@ def test_allreduce_local_validation():
     # nothing to do: no launch
     assert f(bufs, 2, 0, F32, LP, E4, 128, ws, need, None) == OK
     assert f(bufs, 2, 0, F32, AUTO, E4, 128, None, 0, None) == OK
+
+
+def test_stream_ceiling_validation():
+    L = rx.lib()
+    f = L.rxtest_stream
+    assert f(3, FAKE, FAKE, 1024, 1, 0, None) == ARG        # kind
+    assert f(-1, FAKE, FAKE, 1024, 1, 0, None) == ARG
+    assert f(0, FAKE, FAKE, 1024, 0, 0, None) == ARG        # workgroups per CU
+    assert f(0, FAKE, FAKE, 1024, 9, 0, None) == ARG
+    assert f(0, None, FAKE, 1024, 1, 0, None) == NULL       # read needs src
+    assert f(2, FAKE, None, 1024, 1, 0, None) == NULL
+    assert f(2, FAKE, FAKE, 1000, 1, 0, None) == ALIGN      # bytes % 16
+    assert f(2, FAKE + 8, FAKE, 1024, 1, 0, None) == ALIGN
+    assert f(1, None, FAKE + 4, 1024, 1, 0, None) == ALIGN
+    assert f(1, None, FAKE, 0, 1, 0, None) == OK            # nothing to do
+    assert L.rxtest_stream_sink_bytes(0) == 0
+    assert L.rxtest_stream_sink_bytes(9) == 0

@@ -1,0 +1,47 @@
+"""GPU checks of the streaming ceiling kernels the benchmark measures the HBM
+ceilings with: the read kernel really reads every byte (its XOR sink equals
+the XOR of the input), the write kernel writes exactly the pattern over
+exactly the range, and the copy kernel copies exactly the range. Ragged
+sizes leave a partial wave tile at the end."""
+import numpy as np
+import pytest
+import torch
+
+import allreduce_reduction_rx_amd as rx
+from gpu_util import DEV, Guarded, log
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [16, 4096, 4096 + 16, 65536 * 16 + 48, (3 << 20) + 1024 + 16]
+PATTERN = np.array([1.0, 2.0, 3.0, 4.0], dtype=np.float32).view(np.uint8)
+
+
+def random_bytes(nbytes, seed):
+    g = np.random.default_rng(seed)
+    return g.integers(0, 256, nbytes, dtype=np.uint8)
+
+
+@pytest.mark.parametrize("nbytes", SIZES)
+@pytest.mark.parametrize("wgs,nt", [(1, False), (8, True), (2, True)])
+def test_stream_read_copy_write(nbytes, wgs, nt):
+    log(f"ceiling kernels bytes={nbytes} wgs={wgs} nt={nt}")
+    host = random_bytes(nbytes, nbytes + wgs)
+    src = torch.from_numpy(host).to(DEV)
+
+    # read: XOR of the per-thread sinks == XOR of the input's 16-byte words
+    sink_bytes = rx.rxtest_stream_sink_bytes(wgs)
+    sink = torch.zeros(sink_bytes, dtype=torch.uint8, device=DEV)
+    rx.rxtest_stream(rx.RXTEST_READ, src, sink, nbytes, wgs, nt)
+    # copy
+    cp = Guarded(nbytes, torch.uint8)
+    rx.rxtest_stream(rx.RXTEST_COPY, src, cp.t, nbytes, wgs, nt)
+    # write
+    wr = Guarded(nbytes, torch.uint8)
+    rx.rxtest_stream(rx.RXTEST_WRITE, None, wr.t, nbytes, wgs, nt)
+    torch.cuda.synchronize()
+
+    want = np.bitwise_xor.reduce(host.view(np.uint32).reshape(-1, 4), axis=0)
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32).reshape(-1, 4), axis=0)
+    assert np.array_equal(got, want)
+    assert np.array_equal(cp.t.cpu().numpy(), host) and cp.guards_intact()
+    assert np.array_equal(wr.t.cpu().numpy(), np.tile(PATTERN, nbytes // 16)) and wr.guards_intact()
