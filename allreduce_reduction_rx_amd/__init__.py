@@ -346,7 +346,7 @@ def rxtest_group_max(values, g: int, out, stream=None) -> None:
                                   _stream(stream)), "rxtest_group_max")
 
 
-RXTEST_READ, RXTEST_WRITE, RXTEST_COPY = 0, 1, 2
+RXTEST_READ, RXTEST_WRITE, RXTEST_COPY, RXTEST_EMPTY = 0, 1, 2, 3
 
 
 def rxtest_stream_sink_bytes(wgs_per_cu: int) -> int:
@@ -355,8 +355,9 @@ def rxtest_stream_sink_bytes(wgs_per_cu: int) -> int:
 
 def rxtest_stream(kind: int, src, dst, nbytes: int, wgs_per_cu: int = 1, nontemporal: bool = False,
                   stream=None) -> None:
-    """Streaming ceiling kernel (read / write / copy) over nbytes; for a read,
-    dst is the per-thread XOR sink of rxtest_stream_sink_bytes(wgs_per_cu)."""
-    _check(lib().rxtest_stream(kind, src.data_ptr() if src is not None else None, dst.data_ptr(),
+    """Streaming ceiling kernel (read / write / copy / empty) over nbytes; for
+    a read, dst is the per-wave XOR sink of rxtest_stream_sink_bytes(wgs_per_cu)."""
+    _check(lib().rxtest_stream(kind, src.data_ptr() if src is not None else None,
+                               dst.data_ptr() if dst is not None else None,
                                nbytes, wgs_per_cu, int(bool(nontemporal)), _stream(stream)),
            "rxtest_stream")

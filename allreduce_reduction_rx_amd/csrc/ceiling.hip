@@ -27,9 +27,22 @@ __device__ __forceinline__ void st(void* p, size_t v, u32x4 x)
     else st16(p, v, x);
 }
 
+// XOR of a 16-byte value over the 64 lanes of the wave.
+__device__ __forceinline__ u32x4 wave_xor(u32x4 v)
+{
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            v[q] ^= (uint32_t)__shfl_xor((int)v[q], m, kWave);
+    }
+    return v;
+}
+
 // Wave tiles of kCeilU contiguous 64-vector rows, grid-stride over the waves
-// of the launch. KIND 0: read, XOR into a per-thread sum written once at the
-// end (16 bytes per thread); 1: write a constant pattern; 2: copy.
+// of the launch. KIND 0: read, XOR into a per-wave sum written once at the
+// end (16 bytes per wave); 1: write a constant pattern; 2: copy; 3: no
+// memory access at all (the launch alone).
 template <int KIND, bool NT>
 __global__ __launch_bounds__(256) void k_stream(const void* __restrict__ src, void* __restrict__ dst,
                                                 size_t nvec, u32x4 pattern)
@@ -38,6 +51,7 @@ __global__ __launch_bounds__(256) void k_stream(const void* __restrict__ src, vo
     const size_t wave = (size_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     const size_t lane = threadIdx.x % kWave;
     u32x4 acc = {0u, 0u, 0u, 0u};
+    if constexpr (KIND == 3) return;
     for (size_t t = wave; t * kCeilTile < nvec; t += waves) {
         const size_t base = t * kCeilTile + lane;
         if ((t + 1) * kCeilTile <= nvec) {
@@ -67,15 +81,18 @@ __global__ __launch_bounds__(256) void k_stream(const void* __restrict__ src, vo
             }
         }
     }
-    if constexpr (KIND == 0)
-        st16(dst, (size_t)blockIdx.x * blockDim.x + threadIdx.x, acc);
+    if constexpr (KIND == 0) {
+        acc = wave_xor(acc);
+        if (lane == 0) st16(dst, wave, acc);
+    }
 }
 
 typedef void (*StreamFn)(const void*, void*, size_t, u32x4);
-const StreamFn kStream[3][2] = {
+const StreamFn kStream[4][2] = {
     {k_stream<0, false>, k_stream<0, true>},
     {k_stream<1, false>, k_stream<1, true>},
     {k_stream<2, false>, k_stream<2, true>},
+    {k_stream<3, false>, k_stream<3, false>},
 };
 
 }  // namespace
@@ -86,16 +103,16 @@ extern "C" {
 size_t rxtest_stream_sink_bytes(int wgs_per_cu)
 {
     if (wgs_per_cu < 1 || wgs_per_cu > 8) return 0;
-    return (size_t)rx::device_cu_count() * (size_t)wgs_per_cu * 256u * 16u;
+    return (size_t)rx::device_cu_count() * (size_t)wgs_per_cu * (256u / rx::kWave) * 16u;
 }
 
 rx_status_t rxtest_stream(int kind, const void* src, void* dst, size_t bytes, int wgs_per_cu,
                           int nontemporal, hipStream_t stream)
 {
-    if (kind < 0 || kind > 2 || wgs_per_cu < 1 || wgs_per_cu > 8) return RX_ERR_ARG;
-    if (!dst || (kind != 1 && !src)) return RX_ERR_NULL;
+    if (kind < 0 || kind > 3 || wgs_per_cu < 1 || wgs_per_cu > 8) return RX_ERR_ARG;
+    if (kind != 3 && (!dst || (kind != 1 && !src))) return RX_ERR_NULL;
     if (bytes % 16 || (uintptr_t)dst % 16 || (uintptr_t)src % 16) return RX_ERR_ALIGN;
-    if (bytes == 0) return RX_OK;
+    if (bytes == 0 && kind != 3) return RX_OK;
     const unsigned grid = (unsigned)(rx::device_cu_count() * wgs_per_cu);
     const rx::u32x4 pattern = {0x3F800000u, 0x40000000u, 0x40400000u, 0x40800000u};
     void* args_dst = dst;

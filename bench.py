@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "dequant_reduce_requant": ["drr.hpp", "drr.hip", "rx_device.hpp"],
     "lp_tree_step": ["drr.hpp", "drr.hip", "rx_device.hpp"],
     "allreduce_local_flat": ["reduce.hip", "rx_device.hpp"],
+    "allreduce_local_tree": ["reduce.hip", "rx_device.hpp"],
     "allreduce_local_lowprec": ["quant.hip", "drr.hpp", "drr.hip", "rx_device.hpp"],
 }
 # rocprofv3 kernel names (substrings of the mangled names)
@@ -55,6 +56,7 @@ KERNEL_SYMBOLS = {
     "dequant_reduce_requant": "k_drr",
     "lp_tree_step": "k_drr",
     "allreduce_local_flat": "k_tree",
+    "allreduce_local_tree": "k_tree (N launches)",
     "allreduce_local_lowprec": "k_quant, k_drr",
 }
 
@@ -175,6 +177,7 @@ def main():
     # requantizes, dequantizes and writes every buffer)
     bytes_k["lp_tree_step"] = 2 * n * (lp_chunk + 4 * (lp_chunk // lp_block))
     bytes_k["allreduce_local_flat"] = 2 * n * count * e
+    bytes_k["allreduce_local_tree"] = 2 * n * count * e
     bytes_k["allreduce_local_lowprec"] = (n * (count * e + count + 4 * nb)   # quantize
                                           + n * (count + 4 * nb) + n * count * e)  # reduce + write all
     per_batch_bytes = (n * count * e            # sources
@@ -230,10 +233,14 @@ def main():
     def k_ar_flat(b, i):
         rx.rx_allreduce_local(ar_bufs[i % len(ar_bufs)], rx.RX_ALGO_FLAT, lp_fmt, lp_block)
 
+    def k_ar_tree(b, i):
+        rx.rx_allreduce_local(ar_bufs[i % len(ar_bufs)], rx.RX_ALGO_TREE, lp_fmt, lp_block)
+
     def k_ar_lp(b, i):
         rx.rx_allreduce_local(ar_bufs[i % len(ar_bufs)], rx.RX_ALGO_LOWPREC, lp_fmt, lp_block, ar_ws)
 
     kernels_timed = kernels + [("lp_tree_step", k_lp_tree), ("allreduce_local_flat", k_ar_flat),
+                               ("allreduce_local_tree", k_ar_tree),
                                ("allreduce_local_lowprec", k_ar_lp)]
 
     def capture(calls):
@@ -308,6 +315,7 @@ def main():
     value = step_bytes / (step_ms * 1e-3) / 1e9
 
     us_single, us_events = single_launch_us(torch, rx, k_flat, batches, stream)
+    floors = launch_floors(torch, rx, n * count * e) if n * count * e <= (64 << 20) else None
     copy = copy_ceiling(torch, stream)
     ceil = stream_ceilings(torch, rx, stream)
     for k in per_kernel.values():
@@ -352,6 +360,7 @@ def main():
         "us_reduce_flat": per_kernel["reduce_flat"]["us"],
         "us_reduce_flat_single_launch": us_single,
         "us_event_pair_alone": us_events,
+        "launch_floors": floors,
         "tree_matches_flat": bool(tree_ok),
         "copy_ceiling": copy,
         "stream_ceilings": ceil,
@@ -424,6 +433,57 @@ def stream_ceilings(torch, rx, stream):
     return out
 
 
+def launch_floors(torch, rx, in_bytes, reps=256):
+    """What a plain streaming kernel costs per back-to-back launch at this
+    message size, cold (graph replay, each launch on its own slice of a
+    1 GiB rotation): a launch with no memory access, a read of in_bytes, and
+    a copy of in_bytes (best of 1/2/4 workgroups per CU, with and without
+    nontemporal hints)."""
+    total = 1 << 30
+    slices = total // in_bytes
+    src = torch.zeros(total // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.zeros_like(src)
+    sink = torch.empty(rx.rxtest_stream_sink_bytes(8) // 4, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = in_bytes // 4
+
+    def timed(calls):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in calls:
+                c()
+        g.replay()
+        torch.cuda.synchronize()
+        a.record(stream)
+        g.replay()
+        z.record(stream)
+        torch.cuda.synchronize()
+        del g
+        return a.elapsed_time(z) * 1000.0 / len(calls)
+
+    out = {"bytes": in_bytes}
+    out["empty_us"] = round(timed([lambda: rx.rxtest_stream(rx.RXTEST_EMPTY, None, None, 0, 1)
+                                   for _ in range(reps)]), 3)
+    for kind, name in ((rx.RXTEST_READ, "read_us"), (rx.RXTEST_COPY, "copy_us")):
+        best = None
+        for wgs in (1, 2, 4):
+            for nt in (False, True):
+                calls = []
+                for i in range(reps):
+                    k = i % slices
+                    s_ = src[k * per:(k + 1) * per]
+                    d_ = sink if kind == rx.RXTEST_READ else dst[k * per:(k + 1) * per]
+                    calls.append(lambda s_=s_, d_=d_, wgs=wgs, nt=nt:
+                                 rx.rxtest_stream(kind, s_, d_, in_bytes, wgs, nt))
+                us = timed(calls)
+                best = us if best is None else min(best, us)
+        out[name] = round(best, 3)
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return out
+
+
 def single_launch_us(torch, rx, fn, batches, stream, reps=200):
     """Median µs of one launch on its own (the GPU-side dispatch included),
     bracketed by its own HIP events. Each launch is queued behind a 512 MiB
@@ -491,9 +551,18 @@ def cpu_baseline(w, host, lp_fmt, lp_block, seconds, step_bytes):
         if el >= seconds:
             break
     gbs = sbytes * reps / el / 1e9
+    cpu = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} oracle step(s) over the {sample} ({sbytes} algorithmic bytes "
-                      f"per step), {el:.1f} s on one host core"}
+                      f"per step), {el:.1f} s on one host core ({cpu}, "
+                      f"{os.cpu_count()} logical CPUs visible)"}
 
 
 if __name__ == "__main__":

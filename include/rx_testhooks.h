@@ -44,13 +44,16 @@ rx_status_t rxtest_group_max(const uint32_t* in, size_t nwaves, int g,
 
 /* Streaming ceiling kernels: the HBM rates that plain 16-byte-per-lane
  * streams reach on this GPU, measured beside the hot-path kernels.
- *   kind 0 (read):  reads `bytes` of src; every thread XORs what it read
- *                   and stores its 16-byte sum into dst[thread], so the XOR
- *                   of dst over rxtest_stream_sink_bytes(wgs_per_cu) bytes
- *                   equals the XOR of the 16-byte words of src.
+ *   kind 0 (read):  reads `bytes` of src; every wave XORs what it read and
+ *                   stores its 16-byte sum into dst[wave], so the XOR of dst
+ *                   over rxtest_stream_sink_bytes(wgs_per_cu) bytes equals
+ *                   the XOR of the 16-byte words of src.
  *   kind 1 (write): fills dst[0 .. bytes) with the FP32 pattern 1, 2, 3, 4
  *                   repeated; src is ignored (may be NULL).
  *   kind 2 (copy):  dst[0 .. bytes) = src[0 .. bytes).
+ *   kind 3 (empty): the same launch with no memory access (the launch cost
+ *                   alone); src, dst and bytes are ignored apart from the
+ *                   alignment check, and it launches even for bytes == 0.
  * Launch: wgs_per_cu (1..8) workgroups of 256 threads per compute unit,
  * grid-stride over wave tiles of 4 vectors per lane; nontemporal != 0 uses
  * nontemporal loads and stores. bytes, src and dst must be multiples of 16

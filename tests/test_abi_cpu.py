@@ -182,7 +182,7 @@ def test_allreduce_local_validation():
 def test_stream_ceiling_validation():
     L = rx.lib()
     f = L.rxtest_stream
-    assert f(3, FAKE, FAKE, 1024, 1, 0, None) == ARG        # kind
+    assert f(4, FAKE, FAKE, 1024, 1, 0, None) == ARG        # kind
     assert f(-1, FAKE, FAKE, 1024, 1, 0, None) == ARG
     assert f(0, FAKE, FAKE, 1024, 0, 0, None) == ARG        # workgroups per CU
     assert f(0, FAKE, FAKE, 1024, 9, 0, None) == ARG

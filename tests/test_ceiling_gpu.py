@@ -45,3 +45,13 @@ def test_stream_read_copy_write(nbytes, wgs, nt):
     assert np.array_equal(got, want)
     assert np.array_equal(cp.t.cpu().numpy(), host) and cp.guards_intact()
     assert np.array_equal(wr.t.cpu().numpy(), np.tile(PATTERN, nbytes // 16)) and wr.guards_intact()
+
+
+def test_stream_empty_launch_touches_nothing():
+    log("ceiling kernels: empty launch")
+    g = Guarded(4096, torch.uint8)
+    before = g.t.clone()
+    rx.rxtest_stream(rx.RXTEST_EMPTY, None, g.t, 4096, 4, False)
+    rx.rxtest_stream(rx.RXTEST_EMPTY, None, None, 0, 1, False)
+    torch.cuda.synchronize()
+    assert torch.equal(g.t, before) and g.guards_intact()
