@@ -372,6 +372,8 @@ rx_status_t rx_allreduce_local(void* const* bufs, int nsrc, size_t count,
     if (algo == RX_ALGO_LOWPREC) {
         if (!valid_block(block))
             return RX_ERR_ARG;
+        if ((count / 256 + 1) * (size_t)nsrc >= ((size_t)1 << 32))   // the quantizer's limit
+            return RX_ERR_ARG;
         if (!fp8_type(fp8_dtype))
             return RX_ERR_DTYPE;
         if (!workspace)

@@ -174,6 +174,9 @@ def test_allreduce_local_validation():
     assert f(bufs, 2, 1000, F32, LP, E4, 128, ws + 16, need, None) == ALIGN
     assert f(bufs, 2, 1000, F32, LP, E4, 96, ws, need, None) == ARG
     assert f(bufs, 2, 1000, F32, LP, rx.RX_BF16, 128, ws, need, None) == DTYPE
+    # the quantizer's 32-bit tile indices bound count * nsrc (checked first)
+    big = ptrs(*[FAKE + 4096 * j for j in range(16)])
+    assert f(big, 16, 1 << 36, F32, LP, E4, 128, ws, 1 << 62, None) == ARG
     # nothing to do: no launch
     assert f(bufs, 2, 0, F32, LP, E4, 128, ws, need, None) == OK
     assert f(bufs, 2, 0, F32, AUTO, E4, 128, None, 0, None) == OK
