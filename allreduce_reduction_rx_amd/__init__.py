@@ -131,8 +131,12 @@ def _rx_dtype(t) -> int:
 
 
 def _gpu(t, name: str) -> None:
+    import torch
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
@@ -321,28 +325,43 @@ def rx_allreduce_local(bufs: Sequence, algo: int = RX_ALGO_AUTO, fmt="e4m3", blo
 
 # ---- test hooks (rx_testhooks.h) -------------------------------------------
 
+def _hook_buf(t, name: str, nbytes: int) -> None:
+    _gpu(t, name)
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} must hold {nbytes} bytes")
+
+
 def rxtest_fp8_encode_bits(first: int, n: int, fmt, out, stream=None) -> None:
+    _hook_buf(out, "out", n)
     _check(lib().rxtest_fp8_encode_bits(first, n, _fp8_code(fmt), out.data_ptr(), _stream(stream)),
            "rxtest_fp8_encode_bits")
 
 
 def rxtest_block_scale_bits(first: int, n: int, fmt, s, r, stream=None) -> None:
+    _hook_buf(s, "s", 4 * n)
+    _hook_buf(r, "r", 4 * n)
     _check(lib().rxtest_block_scale_bits(first, n, _fp8_code(fmt), s.data_ptr(), r.data_ptr(),
                                          _stream(stream)), "rxtest_block_scale_bits")
 
 
 def rxtest_fp8_decode(codes, fmt, out, stream=None) -> None:
+    _hook_buf(codes, "codes", codes.numel())
+    _hook_buf(out, "out", 4 * codes.numel())
     _check(lib().rxtest_fp8_decode(codes.data_ptr(), codes.numel(), _fp8_code(fmt),
                                    out.data_ptr(), _stream(stream)), "rxtest_fp8_decode")
 
 
 def rxtest_bf16_round_bits(first: int, n: int, out, stream=None) -> None:
+    _hook_buf(out, "out", 2 * n)
     _check(lib().rxtest_bf16_round_bits(first, n, out.data_ptr(), _stream(stream)),
            "rxtest_bf16_round_bits")
 
 
 def rxtest_group_max(values, g: int, out, stream=None) -> None:
-    _check(lib().rxtest_group_max(values.data_ptr(), values.numel() // 64, g, out.data_ptr(),
+    nw = values.numel() // 64
+    _hook_buf(values, "values", 4 * 64 * nw)
+    _hook_buf(out, "out", 4 * 64 * nw)
+    _check(lib().rxtest_group_max(values.data_ptr(), nw, g, out.data_ptr(),
                                   _stream(stream)), "rxtest_group_max")
 
 
@@ -357,6 +376,17 @@ def rxtest_stream(kind: int, src, dst, nbytes: int, wgs_per_cu: int = 1, nontemp
                   stream=None) -> None:
     """Streaming ceiling kernel (read / write / copy / empty) over nbytes; for
     a read, dst is the per-wave XOR sink of rxtest_stream_sink_bytes(wgs_per_cu)."""
+    def size(t):
+        return t.numel() * t.element_size()
+    for name, t in (("src", src), ("dst", dst)):
+        if t is not None:
+            _gpu(t, name)
+    if kind in (RXTEST_READ, RXTEST_COPY) and (src is None or size(src) < nbytes):
+        raise ValueError("src must hold nbytes")
+    if kind in (RXTEST_WRITE, RXTEST_COPY) and (dst is None or size(dst) < nbytes):
+        raise ValueError("dst must hold nbytes")
+    if kind == RXTEST_READ and (dst is None or size(dst) < rxtest_stream_sink_bytes(wgs_per_cu)):
+        raise ValueError("dst must hold rxtest_stream_sink_bytes(wgs_per_cu) bytes")
     _check(lib().rxtest_stream(kind, src.data_ptr() if src is not None else None,
                                dst.data_ptr() if dst is not None else None,
                                nbytes, wgs_per_cu, int(bool(nontemporal)), _stream(stream)),
