@@ -390,8 +390,8 @@ def test_lp_tree_fp32_workload_all_ranks():
 
 def test_lp_fp32_workload_full():
     """Low-precision allreduce on 8 x 16,777,216 FP32 (N(0,1), 1% outliers
-    x100), E4M3, blocks of 128: quant and DRR-REQUANT (+FP32 output)
-    compared in full."""
+    x100), E4M3, blocks of 128: the flat reduce, the tree step of rank 3,
+    quant and DRR-REQUANT (+FP32 output) compared in full."""
     w = G.WORKLOADS["lp_fp32"]
     fmt, block = O.FMT[w.fp8], w.block
     log("lp_fp32 generate")
@@ -410,8 +410,30 @@ def test_lp_fp32_workload_full():
     assert bits_equal(oc, r_oc), first_mismatch(oc, r_oc)
     assert bits_equal(osc, r_os), first_mismatch(osc, r_os)
     assert bits_equal(hp, r_hp), first_mismatch(hp, r_hp)
+    # the full-precision legs of the same message: flat reduce in full, and
+    # the tree step of rank 3 (its chunk in all 8 destinations, nothing else)
+    log("lp_fp32 flat + tree")
+    T32 = O.reduce_flat(srcs, O.FP32)
+    ts = [to_gpu(x) for x in srcs]
+    flat = torch.empty(w.count, dtype=torch.float32, device=DEV)
+    rx.rx_reduce_flat(ts, flat)
+    sync()
+    got = to_host(flat)
+    assert bits_equal(got, T32), first_mismatch(got, T32)
+    del flat, got
+    k = 3
+    lo, hi = O.tree_chunk(w.count, w.nsrc, O.FP32, k)
+    dsts = [torch.zeros(w.count, dtype=torch.float32, device=DEV) for _ in range(w.nsrc)]
+    rx.rx_reduce_scatter_chunk_bcast(ts, k, dsts)
+    sync()
+    want = torch.from_numpy(T32[lo:hi]).to(DEV)
+    for j, d in enumerate(dsts):
+        assert torch.equal(d[lo:hi].view(torch.int32), want.view(torch.int32)), f"tree dst {j}"
+        assert not d[:lo].view(torch.int32).any().item() and not d[hi:].view(torch.int32).any().item()
+    del ts, dsts, want
+    torch.cuda.empty_cache()
     # end-to-end error against the unquantized FP32 sum: N * 2^-4 * blockabsmax
-    T = O.reduce_flat(srcs, O.FP32).astype(np.float64)
+    T = T32.astype(np.float64)
     X_absmax = np.zeros(w.count // block)
     for s in srcs:
         X_absmax = np.maximum(X_absmax, np.abs(s.astype(np.float64)).reshape(-1, block).max(axis=1))
@@ -423,9 +445,11 @@ def test_lp_fp32_workload_full():
 
 def test_lp_bf16_workload_sampled():
     """Low-precision large message: 8 x 268,435,456 BF16 (Laplace(0,1)),
-    E5M2, blocks of 256, in the launch configuration the benchmark times;
-    quant, fused DRR-REQUANT with BF16 output and the separate N=1 dequant,
-    compared with the oracle on 4096 sampled blocks."""
+    E5M2, blocks of 256, in the launch configuration the benchmark times:
+    the flat reduce and the tree step of rank 5 (sampled elements, and
+    nothing outside the chunk), quant, fused DRR-REQUANT with BF16 output and
+    the separate N=1 dequant, compared with the oracle on 4096 sampled
+    blocks."""
     w = G.WORKLOADS["lp_bf16"]
     fmt, block, n, count = O.FMT[w.fp8], w.block, w.nsrc, w.count
     nb = count // block
@@ -437,6 +461,13 @@ def test_lp_bf16_workload_sampled():
         ts.append(to_gpu(w.source(r)))
     codes = [torch.empty(count, dtype=torch.uint8, device=DEV) for _ in range(n)]
     scales = [torch.empty(nb, dtype=torch.float32, device=DEV) for _ in range(n)]
+    log("lp_bf16 flat + tree")
+    flat = torch.empty(count, dtype=torch.bfloat16, device=DEV)
+    rx.rx_reduce_flat(ts, flat)
+    k = 5
+    lo, hi = O.tree_chunk(count, n, O.BF16, k)
+    dsts = [torch.zeros(count, dtype=torch.bfloat16, device=DEV) for _ in range(n)]
+    rx.rx_reduce_scatter_chunk_bcast(ts, k, dsts)
     log("lp_bf16 quant")
     rx.rx_quant_fp8(ts, w.fp8, block, codes, scales)
     oc = torch.empty(count, dtype=torch.uint8, device=DEV)
@@ -454,8 +485,25 @@ def test_lp_bf16_workload_sampled():
     g_scales = [scales[r][sidx].cpu().numpy() for r in range(n)]
     g_oc, g_os = oc[idx].cpu().numpy(), osc[sidx].cpu().numpy()
     g_hp, g_hp2 = to_host(hp[idx]), to_host(hp2[idx])
-    del ts, codes, scales, oc, osc, hp, hp2
+    g_flat = to_host(flat[idx])
+    # tree step: sampled windows inside chunk k in every destination, and
+    # nothing written outside the chunk
+    tw = np.unique(np.concatenate([[lo, hi - 256], rng.integers(lo, hi - 256, 254)]))
+    tidx_np = (tw[:, None] + np.arange(256)[None, :]).ravel()
+    tidx = torch.from_numpy(tidx_np).to(DEV)
+    t_src = [to_host(t[tidx]) for t in ts]
+    g_tree = [to_host(d[tidx]) for d in dsts]
+    outside_clean = all(not d[:lo].view(torch.int16).any().item() and
+                        not d[hi:].view(torch.int16).any().item() for d in dsts)
+    del ts, codes, scales, oc, osc, hp, hp2, flat, dsts
     torch.cuda.empty_cache()
+    log("lp_bf16 oracle flat + tree on sampled elements")
+    r_flat = O.reduce_flat(g_src, O.BF16)
+    assert bits_equal(g_flat, r_flat), first_mismatch(g_flat, r_flat)
+    r_tree = O.reduce_flat(t_src, O.BF16)
+    for j in range(n):
+        assert bits_equal(g_tree[j], r_tree), f"tree dst {j}: " + first_mismatch(g_tree[j], r_tree)
+    assert outside_clean
     log("lp_bf16 oracle on sampled blocks")
     # the sampled blocks are independent: the oracle runs on them as one
     # message of len(sample) blocks
