@@ -135,21 +135,32 @@ __global__ __launch_bounds__(256) void k_reduce_flat_tiles(FlatArgs a)
         store_elem<DT>(a.dst, i, fold_vec_tail<DT, N>(a.src, i));
 }
 
-// Nontemporal source loads: measured 6-9% faster for decode-size chunks, 6%
-// for large FP32 chunks and 6-14% for the in-place one-device allreduce.
+// Two lanes per 16-byte vector: the two half-waves fold the same 32 vectors
+// (their loads share cache lines) and each writes half of the N
+// destinations, so twice the threads share the stores (2-6% faster than one
+// lane writing all N). Nontemporal source loads: 6-9% faster for decode-size
+// chunks, 6% for large FP32 chunks, 6-14% for the in-place allreduce.
 template <int DT, int N>
 __global__ __launch_bounds__(256) void k_tree(TreeArgs a)
 {
     constexpr int VE = Elem<DT>::kVE;
+    constexpr int H = (N + 1) / 2;        // destinations of the first half-wave
     const size_t v0 = a.lo / VE;          // lo is 16-B aligned (or == hi)
     const size_t v1 = a.hi / VE;
     const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t v = v0 + gid; v < v1; v += stride) {
+    const int lane = lane_id();
+    const int half = lane / (kWave / 2);
+    const int first = half ? H : 0;
+    const int cnt = half ? N - H : H;
+    // wave w takes vectors 32w .. 32w + 31, both halves the same ones
+    const size_t vv = (gid / kWave) * (kWave / 2) + (size_t)(lane % (kWave / 2));
+    for (size_t v = v0 + vv; v < v1; v += stride / 2) {
         u32x4 y = fold_vec<DT, N, true>(a.src, v);
 #pragma unroll
-        for (int j = 0; j < N; ++j)
-            st16_stream(a.dst[j], v, y);
+        for (int j = 0; j < H; ++j)
+            if (j < cnt)
+                st16_stream(a.dst[first + j], v, y);
     }
     // hi is a multiple of VE unless it is the end of a ragged message
     const size_t i = (v1 > v0 ? v1 : v0) * VE + gid;
@@ -243,13 +254,13 @@ const std::array<TreeFn, kMaxSrc> kTreeTiles[2] = {
 LaunchPolicy policy_flat() { return {128u, 256u, 1u}; }
 LaunchPolicy policy_tree() { return {64u, 256u, 1u}; }
 
-// Decode-size tree chunks: one 128-thread workgroup per CU once the chunk
-// fills that many threads (8 x 4 MiB messages: 3.37 -> 3.06 us), 64-thread
-// workgroups below (8 x 512 KiB: 128 threads measured 5% slower).
-LaunchPolicy policy_tree_for(size_t nvec)
+// Decode-size tree chunks: 128-thread workgroups once the chunk fills one
+// per CU (8 x 4 MiB messages: 3.37 -> 3.06 us), 64-thread workgroups below
+// (8 x 512 KiB: 128 threads measured 5% slower).
+LaunchPolicy policy_tree_for(size_t threads)
 {
     LaunchPolicy p = policy_tree();
-    if (nvec >= (size_t)128 * (size_t)device_cu_count())
+    if (threads >= (size_t)128 * (size_t)device_cu_count())
         p.wg_small = 128u;
     return p;
 }
@@ -277,7 +288,8 @@ hipError_t launch_tree(const TreeArgs& a, int nsrc, int dtype, hipStream_t s)
     const size_t nvec = (a.hi - a.lo) / ve;
     const bool small = small_job(nvec);
     dim3 grid, block;
-    launch_geometry(nvec, small, policy_tree_for(nvec), grid, block);
+    // k_tree: two threads per vector
+    launch_geometry(small ? 2 * nvec : nvec, small, policy_tree_for(2 * nvec), grid, block);
     TreeArgs arg = a;
     void* params[] = {&arg};
     // large chunks: tiles measured 5% faster for BF16 and 5% slower for FP32
