@@ -812,3 +812,56 @@ def test_lp_tree_in_place(count):
                                         fmt, block, k, ref_c, ref_s)
     for j in range(n):
         assert bits_equal(to_host(tc[j]), ref_c[j]) and bits_equal(to_host(tsc[j]), ref_s[j])
+
+
+# ---------------------------------------------------------------------------
+# Launch-shape independence: the decode-size and large-message kernels (and
+# their different grids) give the same bits on the same data
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
+def test_paths_agree_across_launch_shapes(dtype):
+    n, big, small = 8, 1 << 22, 1 << 17      # large-message vs decode-size launches
+    log(f"launch-shape independence dtype={dtype}")
+    srcs = [to_gpu(G.fill(big, dtype, G.NORMAL, seed=7100 + dtype, rank=r)) for r in range(n)]
+    td = TD[dtype]
+    # flat reduce
+    yb = torch.empty(big, dtype=td, device=DEV)
+    ys = torch.empty(small, dtype=td, device=DEV)
+    rx.rx_reduce_flat(srcs, yb)
+    rx.rx_reduce_flat(srcs, ys, count=small)
+    # in-place flat allreduce (tree kernels over the whole range)
+    ab = [s.clone() for s in srcs]
+    as_ = [s[:small].clone() for s in srcs]
+    rx.rx_allreduce_local(ab, rx.RX_ALGO_FLAT)
+    rx.rx_allreduce_local(as_, rx.RX_ALGO_FLAT)
+    # quantizer and DRR with the high-precision output
+    for fmt, block in ((O.E4M3, 128), (O.E5M2, 256)):
+        f = FMTS[fmt]
+        cb = [torch.empty(big, dtype=torch.uint8, device=DEV) for _ in range(n)]
+        sb = [torch.empty(big // block, dtype=torch.float32, device=DEV) for _ in range(n)]
+        cs = [torch.empty(small, dtype=torch.uint8, device=DEV) for _ in range(n)]
+        ss = [torch.empty(small // block, dtype=torch.float32, device=DEV) for _ in range(n)]
+        rx.rx_quant_fp8(srcs, f, block, cb, sb)
+        rx.rx_quant_fp8(srcs, f, block, cs, ss, count=small)
+        ob, osb, hb = (torch.empty(big, dtype=torch.uint8, device=DEV),
+                       torch.empty(big // block, dtype=torch.float32, device=DEV),
+                       torch.empty(big, dtype=td, device=DEV))
+        os1, oss, hs = (torch.empty(small, dtype=torch.uint8, device=DEV),
+                        torch.empty(small // block, dtype=torch.float32, device=DEV),
+                        torch.empty(small, dtype=td, device=DEV))
+        rx.rx_dequant_reduce_requant(cb, sb, f, block, rx.RX_DRR_REQUANT, ob, osb, hb)
+        rx.rx_dequant_reduce_requant(cs, ss, f, block, rx.RX_DRR_REQUANT, os1, oss, hs, count=small)
+        sync()
+        for j in range(n):
+            assert torch.equal(cb[j][:small], cs[j]) and torch.equal(
+                sb[j][:small // block].view(torch.int32), ss[j].view(torch.int32)), f"quant {fmt} src {j}"
+        assert torch.equal(ob[:small], os1)
+        assert torch.equal(osb[:small // block].view(torch.int32), oss.view(torch.int32))
+        iv = torch.int16 if dtype == O.BF16 else torch.int32
+        assert torch.equal(hb[:small].view(iv), hs.view(iv)), f"drr hp {fmt}"
+    sync()
+    iv = torch.int16 if dtype == O.BF16 else torch.int32
+    assert torch.equal(yb[:small].view(iv), ys.view(iv)), "flat"
+    for j in range(n):
+        assert torch.equal(ab[j][:small].view(iv), as_[j].view(iv)), f"allreduce buffer {j}"
