@@ -43,6 +43,24 @@ void launch_geometry(size_t threads, bool small, const LaunchPolicy& p, dim3& gr
     block = dim3(wg);
 }
 
+bool debug_enabled()
+{
+    static const bool debug = [] {
+        const char* d = getenv("RX_DEBUG");
+        return d && d[0] == '1';
+    }();
+    return debug;
+}
+
+hipError_t launch_logged(const char* what, const void* fn, dim3 grid, dim3 block, void** params,
+                         hipStream_t s)
+{
+    if (debug_enabled())
+        fprintf(stderr, "librx: %s grid %u x %u threads, stream %p\n", what, grid.x, block.x,
+                (void*)s);
+    return hipLaunchKernel(fn, grid, block, params, 0, s);
+}
+
 }  // namespace rx
 
 namespace {

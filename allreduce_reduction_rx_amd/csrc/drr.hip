@@ -1,5 +1,7 @@
 // drr.hip -- launch of the dequantize-reduce-requantize kernel (drr.hpp):
 // lane layout and launch geometry by message size and output type.
+#include <stdio.h>
+
 #include "drr.hpp"
 
 namespace rx {
@@ -50,7 +52,10 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     void* params[] = {&arg};
     const DrrFn fn = cpc == 4 ? (u == 4 ? drr_fns_4x4().fn[fmt][r][nsrc - 1] : drr_fns_4x1().fn[fmt][r][nsrc - 1])
                    : cpc == 8 ? drr_fns_8x2().fn[fmt][r][nsrc - 1] : drr_fns_16x1().fn[fmt][r][nsrc - 1];
-    return hipLaunchKernel((const void*)fn, grid, blk, params, 0, s);
+    char what[64] = "k_drr";
+    if (debug_enabled())
+        snprintf(what, sizeof what, "k_drr mode %d layout %dx%d", r, cpc, u);
+    return launch_logged(what, (const void*)fn, grid, blk, params, s);
 }
 
 }  // namespace rx

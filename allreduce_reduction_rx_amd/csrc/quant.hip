@@ -252,7 +252,8 @@ hipError_t launch_quant(const QuantArgs& a, int src_dtype, int fmt, int block, h
     QuantArgs arg = a;
     void* params[] = {&arg};
     QuantFn fn = small ? kQuantSmall.fn[src_dtype][fmt][lb] : kQuantLarge.fn[src_dtype][fmt][lb];
-    return hipLaunchKernel((const void*)fn, grid, blk, params, 0, s);
+    return launch_logged(small ? "k_quant (decode size)" : "k_quant", (const void*)fn, grid, blk,
+                         params, s);
 }
 
 }  // namespace rx

@@ -71,6 +71,12 @@ constexpr size_t kSmallTilesPerCu = 8;
 
 void launch_geometry(size_t threads, bool small, const LaunchPolicy& p, dim3& grid, dim3& block);
 
+// RX_DEBUG=1 in the environment (read once): every launch prints its
+// kernel, grid and workgroup size to stderr before it is launched.
+bool debug_enabled();
+hipError_t launch_logged(const char* what, const void* fn, dim3 grid, dim3 block, void** params,
+                         hipStream_t s);
+
 // Launchers (return the hipError_t of the launch). dtype: 0 FP32, 1 BF16.
 // fmt: 0 E4M3, 1 E5M2.
 hipError_t launch_reduce_flat(const FlatArgs& a, int nsrc, int dtype, hipStream_t s);

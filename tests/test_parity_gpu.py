@@ -865,3 +865,24 @@ def test_paths_agree_across_launch_shapes(dtype):
     assert torch.equal(yb[:small].view(iv), ys.view(iv)), "flat"
     for j in range(n):
         assert torch.equal(ab[j][:small].view(iv), as_[j].view(iv)), f"allreduce buffer {j}"
+
+
+def test_debug_env_logs_launches():
+    """RX_DEBUG=1 prints every launch's kernel and grid (read once per
+    process, so checked in a child process)."""
+    import os
+    import subprocess
+    import sys
+    log("RX_DEBUG launch log (child process)")
+    code = ("import torch, allreduce_reduction_rx_amd as rx\n"
+            "s = [torch.ones(1 << 12, device='cuda') for _ in range(3)]\n"
+            "d = torch.empty(1 << 12, device='cuda')\n"
+            "rx.rx_reduce_flat(s, d)\n"
+            "torch.cuda.synchronize()\n"
+            "assert torch.all(d == 3).item()\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, RX_DEBUG="1", PYTHONPATH=root + os.pathsep + os.environ.get("PYTHONPATH", ""))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       timeout=240, cwd=root)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "librx: k_reduce_flat grid" in r.stderr
