@@ -30,6 +30,10 @@
  *     nearest even. No NaN/Inf inputs are supported.
  *   - Stateless and reentrant; concurrent calls on different streams are
  *     independent.
+ *   - Environment: RX_DEBUG=1 (read once per process) prints every launch's
+ *     kernel, grid and workgroup size, and the HIP error of a failed
+ *     launch, to stderr. RX_LOW_PRECISION_ENABLE=1 lets rx_allreduce_local's
+ *     RX_ALGO_AUTO choose the low-precision algorithm. Nothing else is read.
  */
 #ifndef RX_H
 #define RX_H
