@@ -14,8 +14,11 @@ per rank), low-precision leg in E5M2 with 256-element blocks. Inputs are
 resident in HBM before timing starts; the batches rotate over enough copies
 (>= 2 GiB in total) that every step reads its inputs from HBM rather than
 from the 256 MB Infinity Cache. The low-precision tree step (one rank's
-share of a low-precision reduce-scatter + all-gather) is timed beside the
-step.
+share of a low-precision reduce-scatter + all-gather), the separate
+dequantization pass, the flat low-precision sum without requantization and
+the in-place one-device allreduces (rx_allreduce_local, flat / tree / low
+precision) are timed beside the step, as is the tree step for each rank on
+its own (`tree_step_by_rank_us`).
 
 Output: one JSON line (see the fields below). Per-kernel times come from HIP
 events around back-to-back launches of that kernel alone, on the stream the
@@ -44,6 +47,8 @@ KERNEL_SOURCES = {
     "quant_fp8": ["quant.hip", "rx_device.hpp"],
     "dequant_reduce_requant": ["drr.hpp", "drr.hip", "rx_device.hpp"],
     "lp_tree_step": ["drr.hpp", "drr.hip", "rx_device.hpp"],
+    "dequant_separate": ["drr.hpp", "drr.hip", "rx_device.hpp"],
+    "lp_flat_sum": ["drr.hpp", "drr.hip", "rx_device.hpp"],
     "allreduce_local_flat": ["reduce.hip", "rx_device.hpp"],
     "allreduce_local_tree": ["reduce.hip", "rx_device.hpp"],
     "allreduce_local_lowprec": ["quant.hip", "drr.hpp", "drr.hip", "rx_device.hpp"],
@@ -55,6 +60,8 @@ KERNEL_SYMBOLS = {
     "quant_fp8": "k_quant",
     "dequant_reduce_requant": "k_drr",
     "lp_tree_step": "k_drr",
+    "dequant_separate": "k_drr",
+    "lp_flat_sum": "k_drr",
     "allreduce_local_flat": "k_tree",
     "allreduce_local_tree": "k_tree (N launches)",
     "allreduce_local_lowprec": "k_quant, k_drr",
@@ -176,6 +183,11 @@ def main():
     # low precision: quantize every buffer, then one pass that reduces,
     # requantizes, dequantizes and writes every buffer)
     bytes_k["lp_tree_step"] = 2 * n * (lp_chunk + 4 * (lp_chunk // lp_block))
+    # the separate dequantization of the requantized message (SUM, one
+    # source) and the flat low-precision reduce without requantization (SUM
+    # over the N quantized sources), both into the message's dtype
+    bytes_k["dequant_separate"] = (count + 4 * nb) + count * e
+    bytes_k["lp_flat_sum"] = n * (count + 4 * nb) + count * e
     bytes_k["allreduce_local_flat"] = 2 * n * count * e
     bytes_k["allreduce_local_tree"] = 2 * n * count * e
     bytes_k["allreduce_local_lowprec"] = (n * (count * e + count + 4 * nb)   # quantize
@@ -214,6 +226,14 @@ def main():
         rx.rx_lp_reduce_scatter_chunk_bcast(b.codes, b.scales, lp_fmt, lp_block, i % n,
                                             b.lp_dst_codes, b.lp_dst_scales)
 
+    def k_dequant(b, i):
+        rx.rx_dequant_reduce_requant([b.out_codes], [b.out_scales], lp_fmt, lp_block,
+                                     rx.RX_DRR_SUM, out_hp=b.out_hp)
+
+    def k_lp_flat(b, i):
+        rx.rx_dequant_reduce_requant(b.codes, b.scales, lp_fmt, lp_block, rx.RX_DRR_SUM,
+                                     out_hp=b.out_hp)
+
     kernels = [("reduce_flat", k_flat), ("tree_step", k_tree),
                ("quant_fp8", k_quant), ("dequant_reduce_requant", k_drr)]
 
@@ -239,7 +259,8 @@ def main():
     def k_ar_lp(b, i):
         rx.rx_allreduce_local(ar_bufs[i % len(ar_bufs)], rx.RX_ALGO_LOWPREC, lp_fmt, lp_block, ar_ws)
 
-    kernels_timed = kernels + [("lp_tree_step", k_lp_tree), ("allreduce_local_flat", k_ar_flat),
+    kernels_timed = kernels + [("lp_tree_step", k_lp_tree), ("dequant_separate", k_dequant),
+                               ("lp_flat_sum", k_lp_flat), ("allreduce_local_flat", k_ar_flat),
                                ("allreduce_local_tree", k_ar_tree),
                                ("allreduce_local_lowprec", k_ar_lp)]
 
@@ -297,6 +318,22 @@ def main():
         per_kernel[name] = {"us": round(us, 3), "GB/s": round(gbs, 1),
                             "frac": round(gbs / PEAK_HBM_GBS, 4),
                             "bytes": bytes_k[name], "launches": reps}
+
+    # ---- the tree step for each rank on its own (median over ranks) ----
+    by_rank = []
+    for k in range(n):
+        reps = per_kernel["tree_step"]["launches"]
+        calls = [lambda i=i, k=k: rx.rx_reduce_scatter_chunk_bcast(batches[i % nsets].srcs, k,
+                                                                   batches[i % nsets].tree_dsts)
+                 for i in range(reps)]
+        if args.no_graph:
+            us = timed(lambda: [c() for c in calls], reps) * 1000.0
+        else:
+            g = capture(calls)
+            g.replay()
+            us = timed(g.replay, reps) * 1000.0
+            del g
+        by_rank.append(round(us, 3))
 
     # ---- parity spot check of batch 0 against the oracle-free invariants:
     # the tree chunk must equal the flat result on that chunk ----
@@ -358,6 +395,8 @@ def main():
         },
         "kernels": per_kernel,
         "us_reduce_flat": per_kernel["reduce_flat"]["us"],
+        "tree_step_by_rank_us": by_rank,
+        "tree_step_median_over_ranks_us": sorted(by_rank)[len(by_rank) // 2],
         "us_reduce_flat_single_launch": us_single,
         "us_event_pair_alone": us_events,
         "launch_floors": floors,
