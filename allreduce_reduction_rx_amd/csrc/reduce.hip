@@ -7,10 +7,10 @@
 // and pushes it to every destination. Sums are FP32 ("Core feature 2", table
 // row "Compute precision"), folded in source order 0..N-1.
 //
-// Both kernels are HBM-bound streams: one 16-byte nontemporal load per
-// source per lane (all N issued before the first add), FP32 adds, one
-// 16-byte store per destination. N is a template parameter so the source loop unrolls and the
-// pointer table is read with scalar loads from the kernarg segment.
+// Both are HBM-bound streams: 16-byte nontemporal loads of every source (all
+// N issued before the first add), FP32 adds, 16-byte nontemporal stores into
+// every destination. N is a template parameter, so the source loop unrolls
+// and the pointer table is read with scalar loads from the kernarg segment.
 #include <array>
 #include <utility>
 
