@@ -758,6 +758,28 @@ def test_allreduce_local(dtype, algo):
             assert bits_equal(got, ref[j]), f"count={count} rank={j}: " + first_mismatch(got, ref[j])
 
 
+@pytest.mark.parametrize("n", [1, 3, 16])
+def test_allreduce_local_rank_counts(n):
+    """Every algorithm with other rank counts, ragged length."""
+    count = 4133
+    for dtype in (O.FP32, O.BF16):
+        fmt, block = (O.E4M3, 64) if dtype == O.FP32 else (O.E5M2, 512)
+        srcs = [G.fill(count, dtype, G.NORMAL, seed=8300 + n, rank=r) for r in range(n)]
+        for algo, oalgo in ((rx.RX_ALGO_FLAT, O.ALGO_FLAT), (rx.RX_ALGO_TREE, O.ALGO_TREE),
+                            (rx.RX_ALGO_LOWPREC, O.ALGO_LOWPREC)):
+            log(f"allreduce_local n={n} dtype={dtype} algo={algo}")
+            ts = [to_gpu(s) for s in srcs]
+            ws = torch.empty(rx.rx_allreduce_local_workspace(n, count, block), dtype=torch.uint8,
+                             device=DEV)
+            rx.rx_allreduce_local(ts, algo, FMTS[fmt], block, ws)
+            sync()
+            ref = [s.copy() for s in srcs]
+            O.allreduce_local(ref, dtype, oalgo, fmt, block)
+            for j in range(n):
+                got = to_host(ts[j])
+                assert bits_equal(got, ref[j]), f"algo={algo} rank={j}: " + first_mismatch(got, ref[j])
+
+
 def test_allreduce_local_rank_id_example():
     for algo in (rx.RX_ALGO_FLAT, rx.RX_ALGO_TREE, rx.RX_ALGO_LOWPREC, rx.RX_ALGO_AUTO):
         ts = [torch.full((10, 20), float(r), dtype=torch.float32, device=DEV) for r in range(8)]
