@@ -197,3 +197,21 @@ def test_stream_ceiling_validation():
     assert f(1, None, FAKE, 0, 1, 0, None) == OK            # nothing to do
     assert L.rxtest_stream_sink_bytes(0) == 0
     assert L.rxtest_stream_sink_bytes(9) == 0
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """No CPU fallback: with librx.so absent every entry point raises."""
+    import subprocess
+    import sys
+    code = ("import allreduce_reduction_rx_amd as rx\n"
+            "rx.lib_path = lambda: '/nonexistent/librx.so'\n"
+            "rx._lib = None\n"
+            "try:\n"
+            "    rx.rx_status_string(0)\n"
+            "except RuntimeError as e:\n"
+            "    assert 'missing' in str(e)\n"
+            "    print('raised')\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "raised"
