@@ -132,7 +132,7 @@ class Batch:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+        print(f"bench.py: this benchmark runs on one GPU only (got --gpus {args.gpus}); "
               "the multi-GPU collective is out of scope here", file=sys.stderr)
         sys.exit(2)
 
