@@ -315,6 +315,22 @@ def test_p7_torch_bf16_conversion():
     assert np.array_equal(O.f32_to_bf16(x), ref)
 
 
+def test_p7_torch_bf16_conversion_every_pattern():
+    # Every FP32 bit pattern but the NaNs, in chunks of 2^26: the oracle's
+    # round-to-nearest-even narrowing against torch's (values near the top
+    # of the range round to +-Inf in both). About half a minute.
+    step = 1 << 26
+    for start in range(0, 1 << 32, step):
+        u = np.arange(start, start + step, dtype=np.uint64).astype(np.uint32)
+        x = u.view(np.float32)
+        ref = torch.from_numpy(x).bfloat16().view(torch.int16).numpy().view(np.uint16)
+        got = O.f32_to_bf16(x)
+        if (start & 0x7FFFFFFF) + step > 0x7F800000:    # the chunk holds NaN patterns
+            keep = ~np.isnan(x)
+            got, ref = got[keep], ref[keep]
+        assert np.array_equal(got, ref), f"chunk at {start:#010x}"
+
+
 def test_p7_bf16_widening_exact():
     h = np.arange(0, 0x7F80, dtype=np.uint16)
     ref = torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).float().numpy()
