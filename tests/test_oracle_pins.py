@@ -364,6 +364,48 @@ def test_block_scale_exact_rationals(fmt):
         assert _is_correctly_rounded_f32(r, fm / a)
 
 
+@pytest.fixture(scope="module")
+def scale_sweep():
+    """tests/bruteforce/scale_sweep.c built for the host: exact checks of
+    correctly rounded division over every non-negative finite FP32 A."""
+    import ctypes
+    import shutil
+    import subprocess
+    import tempfile
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    tmp = tempfile.mkdtemp()
+    so = os.path.join(tmp, "libscalesweep.so")
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bruteforce", "scale_sweep.c")
+    r = subprocess.run([gcc, "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-pthread",
+                        src, "-o", so, "-lm"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    L = ctypes.CDLL(so)
+    U64 = ctypes.POINTER(ctypes.c_uint64)
+    L.scale_sweep.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_int, U64, U64,
+                              ctypes.POINTER(ctypes.c_uint32)]
+    L.scale_sweep.restype = ctypes.c_int
+    yield L
+    shutil.rmtree(tmp, ignore_errors=True)
+
+
+@pytest.mark.parametrize("fmt", [O.E4M3, O.E5M2])
+def test_block_scale_every_absmax(fmt, scale_sweep):
+    # Every non-negative finite FP32 block absmax A (2,139,095,040 values):
+    # s and r correctly rounded (ties to even), checked with exact products,
+    # and s = r = 1 exactly on the degenerate blocks. ~20 s per format.
+    import ctypes
+    entry = ctypes.cast(O.lib().rxo_block_scale_bits_range, ctypes.c_void_p)
+    checked, bad, first = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint32()
+    threads = max(1, min(os.cpu_count() or 1, 16))
+    rc = scale_sweep.scale_sweep(fmt, FMAXV[fmt], entry, threads, ctypes.byref(checked),
+                                 ctypes.byref(bad), ctypes.byref(first))
+    assert rc == 0
+    assert checked.value == 0x7F7FFFFF + 1
+    assert bad.value == 0, f"{bad.value} wrong scales, first at A bits {first.value:#010x}"
+
+
 def test_block_scale_degenerate():
     for fmt in (O.E4M3, O.E5M2):
         assert O.block_scale(f32([0.0, -0.0, 0.0]), fmt) == (1.0, 1.0)
