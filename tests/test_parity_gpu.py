@@ -889,6 +889,74 @@ def test_paths_agree_across_launch_shapes(dtype):
         assert torch.equal(ab[j][:small].view(iv), as_[j].view(iv)), f"allreduce buffer {j}"
 
 
+@pytest.mark.parametrize("n", list(range(1, 17)))
+def test_every_source_count(n):
+    """Every source count 1..16 (each is its own kernel instance) through
+    every entry point on ragged decode-size messages, every rank of both
+    tree steps included; the flat reduce also above the decode-size
+    threshold (the tiled kernel)."""
+    algos = ((rx.RX_ALGO_FLAT, O.ALGO_FLAT), (rx.RX_ALGO_TREE, O.ALGO_TREE),
+             (rx.RX_ALGO_LOWPREC, O.ALGO_LOWPREC))
+    for dtype in (O.FP32, O.BF16):
+        fmt, block = (O.E4M3, 128) if dtype == O.FP32 else (O.E5M2, 256)
+        for count in (1003, 37_777):
+            srcs = [G.fill(count, dtype, G.NORMAL_OUTLIER, seed=9000 + 7 * n + count % 13, rank=r)
+                    for r in range(n)]
+            log(f"every-n n={n} dtype={dtype} count={count}: flat, tree (all ranks)")
+            g = Guarded(count, TD[dtype])
+            rx.rx_reduce_flat([to_gpu(x) for x in srcs], g.t)
+            sync()
+            ref = O.reduce_flat(srcs, dtype)
+            got = to_host(g.t)
+            assert bits_equal(got, ref), "flat: " + first_mismatch(got, ref)
+            assert g.guards_intact()
+            for k in range(n):
+                _tree_case(srcs, dtype, count, k)
+
+            log(f"every-n n={n} dtype={dtype} count={count}: quant, dequant-reduce-requant")
+            gc, gs = _quant_gpu(srcs, dtype, fmt, block, count)
+            rc, rs = O.quant_fp8(srcs, dtype, fmt, block)
+            for j in range(n):
+                assert bits_equal(gc[j], rc[j]), f"codes src={j}: " + first_mismatch(gc[j], rc[j])
+                assert bits_equal(gs[j], rs[j]), f"scales src={j}: " + first_mismatch(gs[j], rs[j])
+            for mode, hp_dtype, want_hp in ((O.DRR_SUM, dtype, True), (O.DRR_REQUANT, dtype, True),
+                                            (O.DRR_REQUANT, O.FP32, False)):
+                got = _drr_gpu(rc, rs, fmt, block, mode, hp_dtype, want_hp, count)
+                ref = O.dequant_reduce_requant(rc, rs, fmt, block, mode, hp_dtype, want_hp)
+                for name, a, b in zip(("codes", "scales", "hp"), got, ref):
+                    assert (a is None) == (b is None)
+                    if a is not None:
+                        assert bits_equal(a, b), f"drr mode={mode} {name}: " + first_mismatch(a, b)
+
+            log(f"every-n n={n} dtype={dtype} count={count}: low-precision tree (all ranks), allreduce")
+            for k in range(n):
+                _lp_tree_case(rc, rs, fmt, block, k, count, hp_dtype=(dtype, None)[k % 2])
+            for algo, oalgo in algos:
+                ts = [to_gpu(x) for x in srcs]
+                ws = torch.empty(max(1, rx.rx_allreduce_local_workspace(n, count, block)),
+                                 dtype=torch.uint8, device=DEV)
+                rx.rx_allreduce_local(ts, algo, FMTS[fmt], block, ws)
+                sync()
+                ref = [x.copy() for x in srcs]
+                O.allreduce_local(ref, dtype, oalgo, fmt, block)
+                for j in range(n):
+                    got = to_host(ts[j])
+                    assert bits_equal(got, ref[j]), f"allreduce algo={algo} rank={j}: " + first_mismatch(got, ref[j])
+
+    # above the decode-size threshold: the tiled flat kernel, ragged end
+    count = (1 << 20) + 4101
+    for dtype in (O.FP32, O.BF16):
+        log(f"every-n n={n} dtype={dtype} count={count}: flat (tiled)")
+        srcs = [G.fill(count, dtype, G.NORMAL, seed=9500 + n, rank=r) for r in range(n)]
+        g = Guarded(count, TD[dtype])
+        rx.rx_reduce_flat([to_gpu(x) for x in srcs], g.t)
+        sync()
+        ref = O.reduce_flat(srcs, dtype)
+        got = to_host(g.t)
+        assert bits_equal(got, ref), "flat tiled: " + first_mismatch(got, ref)
+        assert g.guards_intact()
+
+
 def test_debug_env_logs_launches():
     """RX_DEBUG=1 prints every launch's kernel and grid (read once per
     process, so checked in a child process)."""
