@@ -18,7 +18,8 @@ share of a low-precision reduce-scatter + all-gather), the separate
 dequantization pass, the flat low-precision sum without requantization and
 the in-place one-device allreduces (rx_allreduce_local, flat / tree / low
 precision) are timed beside the step, as is the tree step for each rank on
-its own (`tree_step_by_rank_us`).
+its own (`tree_step_by_rank_us`), and the flat reduce over the first k rank
+buffers for k = 1..N (`reduce_flat_us_by_nsrc`).
 
 Output: one JSON line (see the fields below). Per-kernel times come from HIP
 events around back-to-back launches of that kernel alone, on the stream the
@@ -335,6 +336,23 @@ def main():
             del g
         by_rank.append(round(us, 3))
 
+    # ---- the flat reduce over the first k rank buffers, k = 1..N (DDA
+    # flat's latency against the number of ranks, one GPU's share) ----
+    flat_by_nsrc = []
+    for k in range(1, n + 1):
+        reps = per_kernel["reduce_flat"]["launches"]
+        calls = [lambda i=i, k=k: rx.rx_reduce_flat(batches[i % nsets].srcs[:k],
+                                                    batches[i % nsets].flat_out)
+                 for i in range(reps)]
+        if args.no_graph:
+            us = timed(lambda: [c() for c in calls], reps) * 1000.0
+        else:
+            g = capture(calls)
+            g.replay()
+            us = timed(g.replay, reps) * 1000.0
+            del g
+        flat_by_nsrc.append(round(us, 3))
+
     # ---- parity spot check of batch 0 against the oracle-free invariants:
     # the tree chunk must equal the flat result on that chunk ----
     b0 = batches[0]
@@ -395,6 +413,7 @@ def main():
         },
         "kernels": per_kernel,
         "us_reduce_flat": per_kernel["reduce_flat"]["us"],
+        "reduce_flat_us_by_nsrc": flat_by_nsrc,
         "tree_step_by_rank_us": by_rank,
         "tree_step_median_over_ranks_us": sorted(by_rank)[len(by_rank) // 2],
         "us_reduce_flat_single_launch": us_single,
