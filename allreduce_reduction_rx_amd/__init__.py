@@ -67,6 +67,13 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(path):
             raise RuntimeError(
                 f"{path} is missing: build it with __graft_entry__.build()")
+        # torch ships its own HIP runtime under the same soname as the system
+        # one librx is linked against. With torch loaded first, the loader
+        # resolves librx to that runtime: one HIP runtime in the process.
+        # Loading librx first would bind it to the system runtime, and torch
+        # would then map its bundled copy beside it (two HIP runtimes, whose
+        # device memory, streams and modules the other does not know).
+        import torch  # noqa: F401
         L = ctypes.CDLL(path)
         sig = {
             "rx_reduce_flat": [_PP, _I, _SZ, _I, _P, _P],
@@ -391,3 +398,4 @@ def rxtest_stream(kind: int, src, dst, nbytes: int, wgs_per_cu: int = 1, nontemp
                                dst.data_ptr() if dst is not None else None,
                                nbytes, wgs_per_cu, int(bool(nontemporal)), _stream(stream)),
            "rxtest_stream")
+

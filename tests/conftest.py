@@ -16,17 +16,15 @@ def pytest_configure(config):
 
 
 def pytest_sessionstart(session):
-    """A fresh checkout has no compiled libraries (they are not committed):
-    build them once, through the same build() the package uses (hipcc for
-    librx.so, gcc for the oracle and the input generator). Nothing is built
-    when all three exist."""
-    needed = [os.path.join(ROOT, "allreduce_reduction_rx_amd", "librx.so"),
-              os.path.join(ROOT, "oracle", "librxoracle.so"),
-              os.path.join(ROOT, "rxgen", "librxgen.so")]
-    if all(os.path.exists(p) for p in needed):
-        return
+    """Build the compiled libraries (they are not committed) when one is
+    missing or older than its sources: each build records a SHA-256 of the
+    sources and flags it was made from beside the library, and a library
+    whose record differs from the tree is rebuilt through the same build()
+    the package uses (hipcc for librx.so, gcc for the oracle and the input
+    generator), so no test runs a stale binary."""
     import __graft_entry__
-    __graft_entry__.build()
+    if __graft_entry__.stale():
+        __graft_entry__.build()
 
 
 def _gpu_available() -> bool:

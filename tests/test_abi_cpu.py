@@ -182,6 +182,43 @@ def test_allreduce_local_validation():
     assert f(bufs, 2, 0, F32, AUTO, E4, 128, None, 0, None) == OK
 
 
+def test_one_hip_runtime_per_process():
+    """The binding loads torch before librx, so librx binds to the HIP
+    runtime torch brings (same soname as the system one): a process that
+    loads the library through the binding maps exactly one HIP runtime, even
+    when the binding loads it before any torch import."""
+    import subprocess
+    import sys
+    code = ("import allreduce_reduction_rx_amd as rx\n"
+            "rx.lib()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(sorted({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    libs = eval(r.stdout.strip().splitlines()[-1])
+    assert len(libs) == 1, libs
+
+
+def test_source_hash_does_not_depend_on_the_checkout_path(tmp_path):
+    """A checkout at another path (the GPU machine's) with the same sources and
+    stamps is not stale, so the tests never rebuild there."""
+    import shutil
+    import subprocess
+    import sys
+    for d in ("allreduce_reduction_rx_amd", "include", "oracle", "rxgen"):
+        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
+                        ignore=shutil.ignore_patterns("__pycache__"))
+    shutil.copy(os.path.join(ROOT, "__graft_entry__.py"), tmp_path)
+    here = subprocess.run([sys.executable, "-c", "import __graft_entry__ as g; print(g.stale())"],
+                          capture_output=True, text=True, cwd=ROOT, timeout=120)
+    there = subprocess.run([sys.executable, "-c", "import __graft_entry__ as g; print(g.stale())"],
+                           capture_output=True, text=True, cwd=str(tmp_path), timeout=120)
+    assert here.stdout.strip() == "[]", here.stdout + here.stderr
+    assert there.stdout.strip() == "[]", there.stdout + there.stderr
+
+
 def test_stream_ceiling_validation():
     L = rx.lib()
     f = L.rxtest_stream
