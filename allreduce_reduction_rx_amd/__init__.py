@@ -36,7 +36,7 @@ EXPORTED_SYMBOLS = (
     "rx_quant_fp8", "rx_dequant_reduce_requant", "rx_status_string",
     "rx_lp_reduce_scatter_chunk_bcast", "rx_lp_tree_chunk", "rx_allreduce_local",
     "rx_allreduce_local_workspace", "rxtest_block_scale_bits", "rxtest_fp8_encode_bits", "rxtest_fp8_decode", "rxtest_bf16_round_bits",
-    "rxtest_group_max", "rxtest_stream", "rxtest_stream_sink_bytes",
+    "rxtest_group_max", "rxtest_stream", "rxtest_stream_sink_bytes", "rxtest_stream_mixed",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -91,6 +91,7 @@ def lib() -> ctypes.CDLL:
             "rxtest_bf16_round_bits": [ctypes.c_uint32, _SZ, _P, _P],
             "rxtest_group_max": [_P, _SZ, _I, _P, _P],
             "rxtest_stream": [_I, _P, _P, _SZ, _I, _I, _P],
+            "rxtest_stream_mixed": [_I, _PP, _I, _P, _SZ, _I, _I, _P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -399,3 +400,26 @@ def rxtest_stream(kind: int, src, dst, nbytes: int, wgs_per_cu: int = 1, nontemp
                                nbytes, wgs_per_cu, int(bool(nontemporal)), _stream(stream)),
            "rxtest_stream")
 
+
+RXTEST_MIXED_REDUCE, RXTEST_MIXED_NARROW2, RXTEST_MIXED_NARROW4 = 0, 1, 2
+
+
+def rxtest_stream_mixed(kind: int, srcs: Sequence, dst, src_bytes: int, wgs_per_cu: int = 1,
+                        nontemporal: bool = False, stream=None) -> None:
+    """Mixed read/write ceiling kernel: reduce (len(srcs) : 1, dst = XOR of
+    the sources) or narrow (one source, dst of src_bytes / 2 or / 4)."""
+    def size(t):
+        return t.numel() * t.element_size()
+    for k, t in enumerate(srcs):
+        _gpu(t, f"srcs[{k}]")
+        if size(t) < src_bytes:
+            raise ValueError(f"srcs[{k}] must hold src_bytes")
+    _gpu(dst, "dst")
+    out = src_bytes // {RXTEST_MIXED_REDUCE: 1, RXTEST_MIXED_NARROW2: 2,
+                        RXTEST_MIXED_NARROW4: 4}.get(kind, 1)
+    if size(dst) < out:
+        raise ValueError("dst too small")
+    _check(lib().rxtest_stream_mixed(kind, _ptr_array([t.data_ptr() for t in srcs]), len(srcs),
+                                     dst.data_ptr(), src_bytes, wgs_per_cu,
+                                     int(bool(nontemporal)), _stream(stream)),
+           "rxtest_stream_mixed")

@@ -73,13 +73,12 @@ bool hp_type(rx_dtype_t t) { return t == RX_FP32 || t == RX_BF16; }
 bool fp8_type(rx_dtype_t t) { return t == RX_FP8_E4M3 || t == RX_FP8_E5M2; }
 bool valid_block(int b) { return b >= 32 && b <= 1024 && (b & (b - 1)) == 0; }
 
+// A failed launch is always reported on stderr with the HIP error's name.
 rx_status_t launched(hipError_t e)
 {
     if (e == hipSuccess)
         return RX_OK;
-    const char* dbg = getenv("RX_DEBUG");
-    if (dbg && dbg[0] == '1')
-        fprintf(stderr, "librx: launch failed: %s\n", hipGetErrorString(e));
+    fprintf(stderr, "librx: launch failed: %s (%s)\n", hipGetErrorName(e), hipGetErrorString(e));
     return RX_ERR_HIP;
 }
 

@@ -1,7 +1,10 @@
 // ceiling.hip -- plain streaming kernels (read, write, copy; 16 bytes per
 // lane per access) that measure the HBM ceilings the hot-path kernels are
 // compared against on the same GPU in the same run.
+#include <array>
 #include <stdint.h>
+#include <stdio.h>
+#include <utility>
 
 #include "rx_device.hpp"
 #include "rx_internal.hpp"
@@ -87,6 +90,98 @@ __global__ __launch_bounds__(256) void k_stream(const void* __restrict__ src, vo
     }
 }
 
+// Mixed read/write ceilings: the access patterns of the hot-path kernels
+// with their arithmetic replaced by XOR, so their rate is what the memory
+// system gives that mix of reads and writes.
+//   reduce: NSRC source streams read at the same index, one stream written
+//           (NSRC : 1, the flat reduce's pattern; NSRC = 1 is a copy);
+//   narrow: one stream read, one written at 1/K of its bytes (16 bytes read
+//           and 16/K written per lane: the quantizer's pattern, K = 4 for
+//           FP32 and 2 for BF16 input).
+struct MixedArgs {
+    const void* src[kMaxSrc];
+    void* dst;
+    size_t nvec;   // 16-byte vectors per source
+};
+
+template <int NSRC, bool NT>
+__global__ __launch_bounds__(256) void k_mixed_reduce(MixedArgs a)
+{
+    constexpr int U = NSRC <= 8 ? 4 : 2;
+    constexpr size_t kTile = (size_t)kWave * U;
+    const size_t waves = (size_t)gridDim.x * (blockDim.x / kWave);
+    const size_t wave = (size_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const size_t lane = threadIdx.x % kWave;
+    for (size_t t = wave; t * kTile < a.nvec; t += waves) {
+        const size_t base = t * kTile + lane;
+        u32x4 y[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t v = base + (size_t)u * kWave;
+            if (v < a.nvec) {
+                u32x4 x[NSRC];
+#pragma unroll
+                for (int r = 0; r < NSRC; ++r) x[r] = ld<NT>(a.src[r], v);
+                y[u] = x[0];
+#pragma unroll
+                for (int r = 1; r < NSRC; ++r) y[u] ^= x[r];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t v = base + (size_t)u * kWave;
+            if (v < a.nvec) st<NT>(a.dst, v, y[u]);
+        }
+    }
+}
+
+template <int K, bool NT>
+__global__ __launch_bounds__(256) void k_mixed_narrow(MixedArgs a)
+{
+    constexpr int U = 4;
+    constexpr size_t kTile = (size_t)kWave * U;
+    const size_t waves = (size_t)gridDim.x * (blockDim.x / kWave);
+    const size_t wave = (size_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const size_t lane = threadIdx.x % kWave;
+    for (size_t t = wave; t * kTile < a.nvec; t += waves) {
+        const size_t base = t * kTile + lane;
+        u32x4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t v = base + (size_t)u * kWave;
+            x[u] = v < a.nvec ? ld<NT>(a.src[0], v) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t v = base + (size_t)u * kWave;
+            if (v >= a.nvec) continue;
+            if constexpr (K == 2) {
+                u32x2 w = {x[u][0] ^ x[u][1], x[u][2] ^ x[u][3]};
+                if constexpr (NT) __builtin_nontemporal_store(w, static_cast<u32x2*>(a.dst) + v);
+                else static_cast<u32x2*>(a.dst)[v] = w;
+            } else {
+                uint32_t w = x[u][0] ^ x[u][1] ^ x[u][2] ^ x[u][3];
+                if constexpr (NT) __builtin_nontemporal_store(w, static_cast<uint32_t*>(a.dst) + v);
+                else static_cast<uint32_t*>(a.dst)[v] = w;
+            }
+        }
+    }
+}
+
+using MixedFn = void (*)(MixedArgs);
+
+template <bool NT, int... I>
+constexpr std::array<MixedFn, sizeof...(I)> mixed_reduce_table(std::integer_sequence<int, I...>)
+{
+    return {{&k_mixed_reduce<I + 1, NT>...}};
+}
+
+const std::array<MixedFn, kMaxSrc> kMixedReduce[2] = {
+    mixed_reduce_table<false>(std::make_integer_sequence<int, kMaxSrc>{}),
+    mixed_reduce_table<true>(std::make_integer_sequence<int, kMaxSrc>{})};
+const MixedFn kMixedNarrow[2][2] = {{k_mixed_narrow<2, false>, k_mixed_narrow<2, true>},
+                                    {k_mixed_narrow<4, false>, k_mixed_narrow<4, true>}};
+
 typedef void (*StreamFn)(const void*, void*, size_t, u32x4);
 const StreamFn kStream[4][2] = {
     {k_stream<0, false>, k_stream<0, true>},
@@ -122,7 +217,36 @@ rx_status_t rxtest_stream(int kind, const void* src, void* dst, size_t bytes, in
     void* params[] = {&args_src, &args_dst, &nvec, &pat};
     const hipError_t e = hipLaunchKernel((const void*)rx::kStream[kind][nontemporal ? 1 : 0],
                                          dim3(grid), dim3(256), params, 0, stream);
-    return e == hipSuccess && hipGetLastError() == hipSuccess ? RX_OK : RX_ERR_HIP;
+    if (e != hipSuccess)
+        fprintf(stderr, "librx: launch failed: %s\n", hipGetErrorName(e));
+    return e == hipSuccess ? RX_OK : RX_ERR_HIP;
+}
+
+rx_status_t rxtest_stream_mixed(int kind, const void* const* srcs, int nsrc, void* dst,
+                                size_t src_bytes, int wgs_per_cu, int nontemporal,
+                                hipStream_t stream)
+{
+    if (kind < 0 || kind > 2 || wgs_per_cu < 1 || wgs_per_cu > 8) return RX_ERR_ARG;
+    if (nsrc < 1 || nsrc > RX_MAX_SRC || (kind != 0 && nsrc != 1)) return RX_ERR_ARG;
+    if (!srcs || !dst) return RX_ERR_NULL;
+    for (int j = 0; j < nsrc; ++j)
+        if (!srcs[j]) return RX_ERR_NULL;
+    for (int j = 0; j < nsrc; ++j)
+        if ((uintptr_t)srcs[j] % 16) return RX_ERR_ALIGN;
+    if (src_bytes % 16 || (uintptr_t)dst % 16) return RX_ERR_ALIGN;
+    if (src_bytes == 0) return RX_OK;
+    rx::MixedArgs a = {};
+    for (int j = 0; j < nsrc; ++j) a.src[j] = srcs[j];
+    a.dst = dst;
+    a.nvec = src_bytes / 16;
+    const int nt = nontemporal ? 1 : 0;
+    const rx::MixedFn fn = kind == 0 ? rx::kMixedReduce[nt][nsrc - 1] : rx::kMixedNarrow[kind - 1][nt];
+    const unsigned grid = (unsigned)(rx::device_cu_count() * wgs_per_cu);
+    void* params[] = {&a};
+    const hipError_t e = hipLaunchKernel((const void*)fn, dim3(grid), dim3(256), params, 0, stream);
+    if (e != hipSuccess)
+        fprintf(stderr, "librx: launch failed: %s\n", hipGetErrorName(e));
+    return e == hipSuccess ? RX_OK : RX_ERR_HIP;
 }
 
 }  // extern "C"

@@ -1,6 +1,7 @@
 // testhooks.hip -- kernels that run the device conversion and cross-lane
 // helpers on their own, for exhaustive comparison with the CPU oracle.
 #include <stdint.h>
+#include <stdio.h>
 
 #include "rx_device.hpp"
 #include "rx_internal.hpp"
@@ -67,6 +68,22 @@ unsigned blocks_for(size_t threads) { return (unsigned)((threads + 255) / 256); 
 }  // namespace
 }  // namespace rx
 
+namespace {
+
+// Status of the launch just made: the triple-chevron launch reports through
+// the per-thread last error, which each hook clears right before launching
+// (it also holds whatever an earlier, unrelated HIP call returned).
+rx_status_t launch_status()
+{
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess)
+        return RX_OK;
+    fprintf(stderr, "librx: launch failed: %s\n", hipGetErrorName(e));
+    return RX_ERR_HIP;
+}
+
+}  // namespace
+
 extern "C" {
 
 rx_status_t rxtest_fp8_encode_bits(uint32_t first, size_t n, rx_dtype_t fmt,
@@ -77,11 +94,12 @@ rx_status_t rxtest_fp8_encode_bits(uint32_t first, size_t n, rx_dtype_t fmt,
     if (n > ((size_t)1 << 32) - first) return RX_ERR_ARG;
     if (n == 0) return RX_OK;
     const size_t th = (n + 3) / 4;
+    (void)hipGetLastError();   // drop an earlier call's error
     if (fmt == RX_FP8_E4M3)
         hipLaunchKernelGGL(rx::k_enc_bits<rx::kE4M3>, dim3(rx::blocks_for(th)), dim3(256), 0, stream, first, n, out);
     else
         hipLaunchKernelGGL(rx::k_enc_bits<rx::kE5M2>, dim3(rx::blocks_for(th)), dim3(256), 0, stream, first, n, out);
-    return hipGetLastError() == hipSuccess ? RX_OK : RX_ERR_HIP;
+    return launch_status();
 }
 
 rx_status_t rxtest_fp8_decode(const uint8_t* in, size_t n, rx_dtype_t fmt,
@@ -91,11 +109,12 @@ rx_status_t rxtest_fp8_decode(const uint8_t* in, size_t n, rx_dtype_t fmt,
     if (fmt != RX_FP8_E4M3 && fmt != RX_FP8_E5M2) return RX_ERR_DTYPE;
     if (n == 0) return RX_OK;
     const size_t th = (n + 3) / 4;
+    (void)hipGetLastError();   // drop an earlier call's error
     if (fmt == RX_FP8_E4M3)
         hipLaunchKernelGGL(rx::k_dec<rx::kE4M3>, dim3(rx::blocks_for(th)), dim3(256), 0, stream, in, n, out);
     else
         hipLaunchKernelGGL(rx::k_dec<rx::kE5M2>, dim3(rx::blocks_for(th)), dim3(256), 0, stream, in, n, out);
-    return hipGetLastError() == hipSuccess ? RX_OK : RX_ERR_HIP;
+    return launch_status();
 }
 
 rx_status_t rxtest_block_scale_bits(uint32_t first, size_t n, rx_dtype_t fmt,
@@ -105,11 +124,12 @@ rx_status_t rxtest_block_scale_bits(uint32_t first, size_t n, rx_dtype_t fmt,
     if (fmt != RX_FP8_E4M3 && fmt != RX_FP8_E5M2) return RX_ERR_DTYPE;
     if ((size_t)first + n > 0x7F800000u) return RX_ERR_ARG;
     if (n == 0) return RX_OK;
+    (void)hipGetLastError();   // drop an earlier call's error
     if (fmt == RX_FP8_E4M3)
         hipLaunchKernelGGL(rx::k_scale_bits<rx::kE4M3>, dim3(rx::blocks_for(n)), dim3(256), 0, stream, first, n, s, r);
     else
         hipLaunchKernelGGL(rx::k_scale_bits<rx::kE5M2>, dim3(rx::blocks_for(n)), dim3(256), 0, stream, first, n, s, r);
-    return hipGetLastError() == hipSuccess ? RX_OK : RX_ERR_HIP;
+    return launch_status();
 }
 
 rx_status_t rxtest_bf16_round_bits(uint32_t first, size_t n, uint16_t* out, hipStream_t stream)
@@ -118,8 +138,9 @@ rx_status_t rxtest_bf16_round_bits(uint32_t first, size_t n, uint16_t* out, hipS
     if (n > ((size_t)1 << 32) - first) return RX_ERR_ARG;
     if (n == 0) return RX_OK;
     const size_t th = (n + 1) / 2;
+    (void)hipGetLastError();   // drop an earlier call's error
     hipLaunchKernelGGL(rx::k_bf16_bits, dim3(rx::blocks_for(th)), dim3(256), 0, stream, first, n, out);
-    return hipGetLastError() == hipSuccess ? RX_OK : RX_ERR_HIP;
+    return launch_status();
 }
 
 rx_status_t rxtest_group_max(const uint32_t* in, size_t nwaves, int g, uint32_t* out,
@@ -128,8 +149,9 @@ rx_status_t rxtest_group_max(const uint32_t* in, size_t nwaves, int g, uint32_t*
     if (!in || !out) return RX_ERR_NULL;
     if (g < 1 || g > 64 || (g & (g - 1)) || nwaves > 0x7FFFFFFF) return RX_ERR_ARG;
     if (nwaves == 0) return RX_OK;
+    (void)hipGetLastError();   // drop an earlier call's error
     hipLaunchKernelGGL(rx::k_group_max, dim3((unsigned)nwaves), dim3(64), 0, stream, in, g, out);
-    return hipGetLastError() == hipSuccess ? RX_OK : RX_ERR_HIP;
+    return launch_status();
 }
 
 }  // extern "C"

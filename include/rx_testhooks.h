@@ -61,6 +61,26 @@ rx_status_t rxtest_group_max(const uint32_t* in, size_t nwaves, int g,
 rx_status_t rxtest_stream(int kind, const void* src, void* dst, size_t bytes,
                           int wgs_per_cu, int nontemporal, hipStream_t stream);
 
+/* Mixed read/write ceiling kernels: the access patterns of the hot-path
+ * kernels with XOR in place of their arithmetic, so their rate is what the
+ * memory system gives that mix of reads and writes.
+ *   kind 0 (reduce): nsrc (1..16) sources of src_bytes each; dst (src_bytes)
+ *                    = XOR of the sources, 16-byte word by word: nsrc : 1
+ *                    bytes read : written (the flat reduce; nsrc = 1 copies).
+ *   kind 1 (narrow 2:1), kind 2 (narrow 4:1): nsrc == 1; each 16-byte word
+ *                    of the source is folded by XOR into 8 (kind 1: words
+ *                    w0^w1, w2^w3) or 4 bytes (kind 2: w0^w1^w2^w3), written
+ *                    at dst + 8 v or dst + 4 v: the quantizer's pattern for
+ *                    BF16 (2:1) and FP32 (4:1) input.
+ * srcs is a host array of device pointers (16-B aligned); src_bytes a
+ * multiple of 16. Launch as rxtest_stream: wgs_per_cu (1..8) workgroups of
+ * 256 threads per compute unit, grid-stride over wave tiles of 4 vectors per
+ * lane (2 for more than 8 sources); nontemporal != 0 uses nontemporal loads
+ * and stores. dst must not overlap a source. */
+rx_status_t rxtest_stream_mixed(int kind, const void* const* srcs, int nsrc, void* dst,
+                                size_t src_bytes, int wgs_per_cu, int nontemporal,
+                                hipStream_t stream);
+
 /* Size in bytes of the read kernel's dst for this wgs_per_cu (0 if out of
  * range). */
 size_t rxtest_stream_sink_bytes(int wgs_per_cu);

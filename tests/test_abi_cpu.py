@@ -234,6 +234,19 @@ def test_stream_ceiling_validation():
     assert f(1, None, FAKE, 0, 1, 0, None) == OK            # nothing to do
     assert L.rxtest_stream_sink_bytes(0) == 0
     assert L.rxtest_stream_sink_bytes(9) == 0
+    m = L.rxtest_stream_mixed
+    two = ptrs(FAKE, FAKE + 4096)
+    assert m(3, two, 2, FAKE, 1024, 1, 0, None) == ARG          # kind
+    assert m(1, two, 2, FAKE, 1024, 1, 0, None) == ARG          # narrow takes one source
+    assert m(0, two, 0, FAKE, 1024, 1, 0, None) == ARG
+    assert m(0, ptrs(*[FAKE] * 17), 17, FAKE, 1024, 1, 0, None) == ARG
+    assert m(0, two, 2, FAKE, 1024, 9, 0, None) == ARG          # workgroups per CU
+    assert m(0, None, 2, FAKE, 1024, 1, 0, None) == NULL
+    assert m(0, two, 2, None, 1024, 1, 0, None) == NULL
+    assert m(0, ptrs(FAKE, 0), 2, FAKE, 1024, 1, 0, None) == NULL
+    assert m(0, ptrs(FAKE, FAKE + 8), 2, FAKE, 1024, 1, 0, None) == ALIGN
+    assert m(2, ptrs(FAKE), 1, FAKE, 1000, 1, 0, None) == ALIGN  # bytes % 16
+    assert m(0, two, 2, FAKE, 0, 1, 0, None) == OK               # nothing to do
 
 
 def test_binding_fails_loudly_without_the_library(tmp_path):

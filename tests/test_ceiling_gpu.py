@@ -55,3 +55,32 @@ def test_stream_empty_launch_touches_nothing():
     rx.rxtest_stream(rx.RXTEST_EMPTY, None, None, 0, 1, False)
     torch.cuda.synchronize()
     assert torch.equal(g.t, before) and g.guards_intact()
+
+
+@pytest.mark.parametrize("nbytes", SIZES)
+@pytest.mark.parametrize("wgs,nt", [(1, False), (4, True)])
+def test_stream_mixed(nbytes, wgs, nt):
+    """Mixed read/write ceilings: reduce over 1, 3, 8 and 16 sources (XOR of
+    the sources, 16-byte word by word) and the 2:1 / 4:1 narrowing folds,
+    exactly over the range (guard bands intact)."""
+    log(f"mixed ceiling kernels bytes={nbytes} wgs={wgs} nt={nt}")
+    hosts = [random_bytes(nbytes, 7 * nbytes + r) for r in range(16)]
+    srcs = [torch.from_numpy(h).to(DEV) for h in hosts]
+    for nsrc in (1, 3, 8, 16):
+        out = Guarded(nbytes, torch.uint8)
+        rx.rxtest_stream_mixed(rx.RXTEST_MIXED_REDUCE, srcs[:nsrc], out.t, nbytes, wgs, nt)
+        torch.cuda.synchronize()
+        want = np.bitwise_xor.reduce(np.stack(hosts[:nsrc]), axis=0)
+        assert np.array_equal(out.t.cpu().numpy(), want), f"reduce nsrc={nsrc}"
+        assert out.guards_intact()
+    words = hosts[0].view(np.uint32).reshape(-1, 4)
+    for kind, k in ((rx.RXTEST_MIXED_NARROW2, 2), (rx.RXTEST_MIXED_NARROW4, 4)):
+        out = Guarded(nbytes // k, torch.uint8)
+        rx.rxtest_stream_mixed(kind, srcs[:1], out.t, nbytes, wgs, nt)
+        torch.cuda.synchronize()
+        if k == 2:
+            want = np.stack([words[:, 0] ^ words[:, 1], words[:, 2] ^ words[:, 3]], axis=1)
+        else:
+            want = words[:, 0] ^ words[:, 1] ^ words[:, 2] ^ words[:, 3]
+        assert np.array_equal(out.t.cpu().numpy(), want.astype(np.uint32).ravel().view(np.uint8)), k
+        assert out.guards_intact()
