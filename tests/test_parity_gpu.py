@@ -7,6 +7,9 @@ Workloads (named in rxgen): the RCCLX article's rank-id example
 tree step on 4 MiB messages, and the two >= 16 MB low-precision messages
 ("Core feature 2: Low-Precision Collectives").
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -443,78 +446,118 @@ def test_lp_fp32_workload_full():
     assert np.all(err <= bound)
 
 
-def test_lp_bf16_workload_sampled():
+def _pool_size() -> int:
+    # the GPU machine's CPU share is 16 threads, whatever os.cpu_count() shows
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def test_lp_bf16_workload_full():
     """Low-precision large message: 8 x 268,435,456 BF16 (Laplace(0,1)),
-    E5M2, blocks of 256, in the launch configuration the benchmark times:
-    the flat reduce and the tree step of rank 5 (sampled elements, and
-    nothing outside the chunk), quant, fused DRR-REQUANT with BF16 output and
-    the separate N=1 dequant, compared with the oracle on 4096 sampled
-    blocks."""
+    E5M2, blocks of 256, in the launch configuration the benchmark times,
+    compared with the oracle everywhere: the flat reduce (every element),
+    the tree step of rank 5 (every element of its chunk in all 8
+    destinations, nothing written outside it), the quantizer (every code and
+    scale of every rank), DRR-REQUANT with the fused BF16 output and the
+    separate N=1 dequantization (every block). The oracle is block-local, so
+    it runs over windows of whole blocks in a thread pool; the end-to-end
+    error of the GPU's BF16 result D against the unquantized sum T is
+    asserted on every element: |D - T| <= N 2^-3 A_b + 2^-8 |D|, with A_b the
+    largest absmax of the block over the ranks and 2^-8 the unit roundoff of
+    BF16's 8-bit significand (the output is rounded to BF16); the tighter
+    N 2^-3 A_b + 2^-9 |D| is asserted on this message as well."""
     w = G.WORKLOADS["lp_bf16"]
     fmt, block, n, count = O.FMT[w.fp8], w.block, w.nsrc, w.count
     nb = count // block
-    rng = np.random.default_rng(505)
-    sample = np.unique(np.concatenate([[0, nb - 1], rng.integers(0, nb, 4094)]))
-    log("lp_bf16 generate + upload")
-    ts = []
-    for r in range(n):
-        ts.append(to_gpu(w.source(r)))
-    codes = [torch.empty(count, dtype=torch.uint8, device=DEV) for _ in range(n)]
-    scales = [torch.empty(nb, dtype=torch.float32, device=DEV) for _ in range(n)]
-    log("lp_bf16 flat + tree")
+    log("lp_bf16 generate")
+    srcs = w.sources()
+    log("lp_bf16 upload + gpu")
+    ts = [to_gpu(x) for x in srcs]
     flat = torch.empty(count, dtype=torch.bfloat16, device=DEV)
     rx.rx_reduce_flat(ts, flat)
     k = 5
-    lo, hi = O.tree_chunk(count, n, O.BF16, k)
+    lo5, hi5 = O.tree_chunk(count, n, O.BF16, k)
     dsts = [torch.zeros(count, dtype=torch.bfloat16, device=DEV) for _ in range(n)]
     rx.rx_reduce_scatter_chunk_bcast(ts, k, dsts)
-    log("lp_bf16 quant")
+    codes = [torch.empty(count, dtype=torch.uint8, device=DEV) for _ in range(n)]
+    scales = [torch.empty(nb, dtype=torch.float32, device=DEV) for _ in range(n)]
     rx.rx_quant_fp8(ts, w.fp8, block, codes, scales)
     oc = torch.empty(count, dtype=torch.uint8, device=DEV)
     osc = torch.empty(nb, dtype=torch.float32, device=DEV)
     hp = torch.empty(count, dtype=torch.bfloat16, device=DEV)
-    log("lp_bf16 drr")
     rx.rx_dequant_reduce_requant(codes, scales, w.fp8, block, rx.RX_DRR_REQUANT, oc, osc, hp)
     hp2 = torch.empty(count, dtype=torch.bfloat16, device=DEV)
     rx.rx_dequant_reduce_requant([oc], [osc], w.fp8, block, rx.RX_DRR_SUM, out_hp=hp2)
     sync()
-    idx = torch.from_numpy((sample[:, None] * block + np.arange(block)[None, :]).ravel()).to(DEV)
-    sidx = torch.from_numpy(sample).to(DEV)
-    g_src = [to_host(t[idx]) for t in ts]
-    g_codes = [codes[r][idx].cpu().numpy() for r in range(n)]
-    g_scales = [scales[r][sidx].cpu().numpy() for r in range(n)]
-    g_oc, g_os = oc[idx].cpu().numpy(), osc[sidx].cpu().numpy()
-    g_hp, g_hp2 = to_host(hp[idx]), to_host(hp2[idx])
-    g_flat = to_host(flat[idx])
-    # tree step: sampled windows inside chunk k in every destination, and
-    # nothing written outside the chunk
-    tw = np.unique(np.concatenate([[lo, hi - 256], rng.integers(lo, hi - 256, 254)]))
-    tidx_np = (tw[:, None] + np.arange(256)[None, :]).ravel()
-    tidx = torch.from_numpy(tidx_np).to(DEV)
-    t_src = [to_host(t[tidx]) for t in ts]
-    g_tree = [to_host(d[tidx]) for d in dsts]
-    outside_clean = all(not d[:lo].view(torch.int16).any().item() and
-                        not d[hi:].view(torch.int16).any().item() for d in dsts)
-    del ts, codes, scales, oc, osc, hp, hp2, flat, dsts
+    log("lp_bf16 download")
+    del ts
+    outside_clean = all(not d[:lo5].view(torch.int16).any().item() and
+                        not d[hi5:].view(torch.int16).any().item() for d in dsts)
+    g_tree = [to_host(d[lo5:hi5]) for d in dsts]
+    del dsts
+    g_flat = to_host(flat)
+    g_codes = [c.cpu().numpy() for c in codes]
+    g_scales = [q.cpu().numpy() for q in scales]
+    g_oc, g_os = oc.cpu().numpy(), osc.cpu().numpy()
+    g_hp, g_hp2 = to_host(hp), to_host(hp2)
+    del flat, codes, scales, oc, osc, hp, hp2
     torch.cuda.empty_cache()
-    log("lp_bf16 oracle flat + tree on sampled elements")
-    r_flat = O.reduce_flat(g_src, O.BF16)
-    assert bits_equal(g_flat, r_flat), first_mismatch(g_flat, r_flat)
-    r_tree = O.reduce_flat(t_src, O.BF16)
-    for j in range(n):
-        assert bits_equal(g_tree[j], r_tree), f"tree dst {j}: " + first_mismatch(g_tree[j], r_tree)
-    assert outside_clean
-    log("lp_bf16 oracle on sampled blocks")
-    # the sampled blocks are independent: the oracle runs on them as one
-    # message of len(sample) blocks
-    rc, rs = O.quant_fp8(g_src, O.BF16, fmt, block)
-    for r in range(n):
-        assert bits_equal(g_codes[r], rc[r]), first_mismatch(g_codes[r], rc[r])
-        assert bits_equal(g_scales[r], rs[r]), first_mismatch(g_scales[r], rs[r])
-    r_oc, r_os, r_hp = O.dequant_reduce_requant(rc, rs, fmt, block, O.DRR_REQUANT, O.BF16, True)
-    assert bits_equal(g_oc, r_oc) and bits_equal(g_os, r_os)
-    assert bits_equal(g_hp, r_hp), first_mismatch(g_hp, r_hp)
-    assert bits_equal(g_hp2, r_hp), first_mismatch(g_hp2, r_hp)
+    assert outside_clean, "tree step wrote outside its chunk"
+
+    win = 4096 * block                    # elements per window (whole blocks)
+    u, n_f = 2.0 ** -3, float(n)
+
+    def check(i0):
+        i1 = min(i0 + win, count)
+        b0, b1 = i0 // block, -(-i1 // block)
+        x = [s[i0:i1] for s in srcs]
+        where = f"window [{i0}, {i1})"
+        r_flat = O.reduce_flat(x, O.BF16)
+        if not bits_equal(g_flat[i0:i1], r_flat):
+            return f"flat {where}: " + first_mismatch(g_flat[i0:i1], r_flat)
+        t0, t1 = max(i0, lo5), min(i1, hi5)
+        if t0 < t1:
+            for j in range(n):
+                got = g_tree[j][t0 - lo5:t1 - lo5]
+                if not bits_equal(got, r_flat[t0 - i0:t1 - i0]):
+                    return f"tree dst {j} {where}: " + first_mismatch(got, r_flat[t0 - i0:t1 - i0])
+        rc, rs = O.quant_fp8(x, O.BF16, fmt, block)
+        for r in range(n):
+            if not bits_equal(g_codes[r][i0:i1], rc[r]):
+                return f"codes rank {r} {where}: " + first_mismatch(g_codes[r][i0:i1], rc[r])
+            if not bits_equal(g_scales[r][b0:b1], rs[r]):
+                return f"scales rank {r} {where}: " + first_mismatch(g_scales[r][b0:b1], rs[r])
+        r_oc, r_os, r_hp = O.dequant_reduce_requant(rc, rs, fmt, block, O.DRR_REQUANT, O.BF16, True)
+        if not bits_equal(g_oc[i0:i1], r_oc):
+            return f"requant codes {where}: " + first_mismatch(g_oc[i0:i1], r_oc)
+        if not bits_equal(g_os[b0:b1], r_os):
+            return f"requant scales {where}: " + first_mismatch(g_os[b0:b1], r_os)
+        if not bits_equal(g_hp[i0:i1], r_hp):
+            return f"fused BF16 output {where}: " + first_mismatch(g_hp[i0:i1], r_hp)
+        _, _, r_hp2 = O.dequant_reduce_requant([r_oc], [r_os], fmt, block, O.DRR_SUM, O.BF16)
+        if not bits_equal(g_hp2[i0:i1], r_hp2):
+            return f"separate dequant {where}: " + first_mismatch(g_hp2[i0:i1], r_hp2)
+        # end-to-end error of the GPU's BF16 result against the exact sum
+        X = np.stack([O.bf16_to_f32(xi).astype(np.float64) for xi in x])
+        T = X.sum(axis=0)
+        Ab = np.repeat(np.abs(X).reshape(n, -1, block).max(axis=2).max(axis=0), block)
+        D = O.bf16_to_f32(g_hp[i0:i1]).astype(np.float64)
+        err = np.abs(D - T)
+        bound = n_f * u * Ab + 2.0 ** -8 * np.abs(D)
+        if not np.all(err <= bound):
+            i = int(np.argmax(err - bound))
+            return f"error bound {where}: element {i0 + i} err {err[i]} > bound {bound[i]}"
+        return float(np.max(err / bound)), float(np.max(err / (n_f * u * Ab + 2.0 ** -9 * np.abs(D))))
+
+    log(f"lp_bf16 oracle over {-(-count // win)} windows, {_pool_size()} threads")
+    worst, worst9 = 0.0, 0.0
+    with ThreadPoolExecutor(_pool_size()) as ex:
+        for res in ex.map(check, range(0, count, win)):
+            assert not isinstance(res, str), res
+            worst, worst9 = max(worst, res[0]), max(worst9, res[1])
+    log(f"lp_bf16 max err/bound = {worst:.4f} (with 2^-9 |D|: {worst9:.4f})")
+    # the tighter form N 2^-3 A_b + 2^-9 |D| (not a bound for every input)
+    # holds on this message too
+    assert worst9 <= 1.0
 
 
 # ---------------------------------------------------------------------------
