@@ -9,22 +9,34 @@ rank buffers (N = 8 separate HBM allocations):
   4. fused dequant-reduce-requant, with the dequantized high-precision
      output                             rx_dequant_reduce_requant (REQUANT + hp)
 
-The default workload is the decode-size message: 8 x 32x8192 BF16 (512 KiB
-per rank), low-precision leg in E5M2 with 256-element blocks. Inputs are
-resident in HBM before timing starts; the batches rotate over enough copies
-(>= 2 GiB in total) that every step reads its inputs from HBM rather than
-from the 256 MB Infinity Cache. The low-precision tree step (one rank's
-share of a low-precision reduce-scatter + all-gather), the separate
-dequantization pass, the flat low-precision sum without requantization and
-the in-place one-device allreduces (rx_allreduce_local, flat / tree / low
-precision) are timed beside the step, as is the tree step for each rank on
-its own (`tree_step_by_rank_us`), and the flat reduce over the first k rank
-buffers for k = 1..N (`reduce_flat_us_by_nsrc`).
+The step workload (`value`, `ms_per_step`, `roofline`, `kernels`) is the
+decode-size message the headline "µs at 512 KB" names: 8 x 32x8192 BF16
+(512 KiB per rank); its low-precision leg uses E5M2 with 256-element blocks
+(the BF16 message format of the large low-precision workload). Inputs are
+resident in HBM before timing starts and the batches rotate over >= 2 GiB,
+so every step reads its inputs from HBM rather than from the 256 MB Infinity
+Cache.
 
-Output: one JSON line (see the fields below). Per-kernel times come from HIP
-events around back-to-back launches of that kernel alone, on the stream the
-kernel runs on; `rocprofv3 --kernel-trace --stats` of the same command
-reports the per-dispatch durations.
+`configs` then times, in the same run, the kernels each of the five message
+shapes is quoted on, each with its own rotation (>= 2 GiB of inputs and
+outputs, or one launch when a launch alone moves that much):
+  cfg1  8 x 200 FP32 (10x20), rank-id fill (-> 28.0) and U[-1,1): flat reduce
+  cfg2  8 x 262,144 BF16 (512 KiB), N(0,1): flat reduce
+  cfg3  8 x 2,097,152 BF16 (4 MiB), N(0,1): tree step for every rank
+  cfg4  8 x 16,777,216 FP32 (64 MiB), N(0,1) + 1% x100: quant E4M3/128,
+        DRR-REQUANT with and without the FP32 output
+  cfg5  8 x 268,435,456 BF16 (512 MiB), Laplace(0,1): quant E5M2/256,
+        DRR-REQUANT with the fused BF16 output and without it, the separate
+        dequantization
+Every generated input buffer's SHA-256 is recorded beside its config.
+
+Times: HIP events on the launch stream around back-to-back launches of one
+kernel (captured in a HIP graph), divided by the launch count (`us`,
+`frac`). Where the committed rocprofv3 kernel trace of the same command
+(profiles/kernels_<workload>.md) holds the kernel at the current source
+hash, its average per-dispatch duration is reported beside it (`us_trace`,
+`frac_trace`): under the profiler each dispatch starts on an idle GPU, so at
+decode size the trace durations run longer than the back-to-back interval.
 """
 from __future__ import annotations
 
@@ -35,37 +47,24 @@ import os
 import re
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 METRIC = "effective HBM GB/s (% of MI355X peak) per reduce kernel; µs at 512 KB msg"
+ROTATE_BYTES = 2 << 30  # >= 8x the 256 MB Infinity Cache
 
+_REDUCE = ["reduce.hip", "rx_device.hpp"]
+_QUANT = ["quant.hip", "rx_device.hpp"]
+_DRR = ["drr.hpp", "drr.hip", "rx_device.hpp"]
 KERNEL_SOURCES = {
-    "reduce_flat": ["reduce.hip", "rx_device.hpp"],
-    "tree_step": ["reduce.hip", "rx_device.hpp"],
-    "quant_fp8": ["quant.hip", "rx_device.hpp"],
-    "dequant_reduce_requant": ["drr.hpp", "drr.hip", "rx_device.hpp"],
-    "lp_tree_step": ["drr.hpp", "drr.hip", "rx_device.hpp"],
-    "dequant_separate": ["drr.hpp", "drr.hip", "rx_device.hpp"],
-    "lp_flat_sum": ["drr.hpp", "drr.hip", "rx_device.hpp"],
-    "allreduce_local_flat": ["reduce.hip", "rx_device.hpp"],
-    "allreduce_local_tree": ["reduce.hip", "rx_device.hpp"],
-    "allreduce_local_lowprec": ["quant.hip", "drr.hpp", "drr.hip", "rx_device.hpp"],
-}
-# rocprofv3 kernel names (substrings of the mangled names)
-KERNEL_SYMBOLS = {
-    "reduce_flat": "k_reduce_flat",
-    "tree_step": "k_tree",
-    "quant_fp8": "k_quant",
-    "dequant_reduce_requant": "k_drr",
-    "lp_tree_step": "k_drr",
-    "dequant_separate": "k_drr",
-    "lp_flat_sum": "k_drr",
-    "allreduce_local_flat": "k_tree",
-    "allreduce_local_tree": "k_tree (N launches)",
-    "allreduce_local_lowprec": "k_quant, k_drr",
+    "reduce_flat": _REDUCE, "tree_step": _REDUCE, "quant_fp8": _QUANT,
+    "dequant_reduce_requant": _DRR, "drr_requant": _DRR, "drr_requant_hp": _DRR,
+    "lp_tree_step": _DRR, "dequant_separate": _DRR, "lp_flat_sum": _DRR,
+    "allreduce_local_flat": _REDUCE, "allreduce_local_tree": _REDUCE,
+    "allreduce_local_lowprec": _QUANT + _DRR,
 }
 
 
@@ -75,17 +74,24 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode",
-                   help="decode | tree | lp_fp32 | lp_bf16 | flat_uniform")
+                   help="step workload: decode | tree | lp_fp32 | lp_bf16 | flat_uniform")
+    p.add_argument("--configs", default="cfg1,cfg3,cfg4,cfg5",
+                   help="comma list of the per-config measurements to run beside the "
+                        "step ('' = none); cfg2 is the decode step workload")
     p.add_argument("--kernel-reps", type=int, default=0,
                    help="launches per kernel-only timing (0 = auto)")
     p.add_argument("--warm", action="store_true",
                    help="reuse one batch every step (cache-warm; labelled)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-graph", action="store_true",
-                   help="launch from a Python loop instead of replaying HIP graphs")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-ceilings", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="oracle time, split between the 1-thread and the N-thread legs")
     return p.parse_args()
 
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
 
 def sha_of(files):
     h = hashlib.sha256()
@@ -95,25 +101,130 @@ def sha_of(files):
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary
-    (profiles/traffic_<workload>.md), or None when absent or when the
-    kernel's source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+def _profile_field(path, key, name, field):
+    """`field` of the line '- <key>: source_sha256=<sha> ... field=<v>' of a
+    committed profile summary, when its source hash is the current one."""
     if not os.path.exists(path):
         return None
+    kernel = name.split("@")[0]
     want = sha_of(KERNEL_SOURCES[kernel])
     for line in open(path):
-        m = re.match(r"- (\w+): source_sha256=(\w+) hbm_bytes_per_launch=(\d+)", line.strip())
-        if m and m.group(1) == kernel:
-            return float(m.group(3)) if m.group(2) == want else None
+        m = re.match(r"- ([\w@.]+): source_sha256=(\w+) (.*)$", line.strip())
+        if m and m.group(1) == key:
+            if m.group(2) != want:
+                return None
+            f = dict(kv.split("=", 1) for kv in m.group(3).split())
+            return float(f[field]) if field in f else None
     return None
 
+
+def trace_us(workload, name):
+    """Average per-dispatch µs of `name` in the committed rocprofv3 kernel
+    trace of this workload, or None (absent, or the source changed)."""
+    return _profile_field(os.path.join(ROOT, "profiles", f"kernels_{workload}.md"), name, name,
+                          "avg_us")
+
+
+def read_traffic(workload, name):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary
+    (profiles/traffic_<workload>.md), or None."""
+    return _profile_field(os.path.join(ROOT, "profiles", f"traffic_{workload}.md"), name, name,
+                          "hbm_bytes_per_launch")
+
+
+def entry(nbytes, us, reps, workload=None, name=None, target=None):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    d = {"bytes": int(nbytes), "us": round(us, 3), "GB/s": round(gbs, 1),
+         "frac": round(gbs / PEAK_HBM_GBS, 4), "launches": reps}
+    if workload and name:
+        tu = trace_us(workload, name)
+        if tu:
+            d["us_trace"] = round(tu, 3)
+            d["frac_trace"] = round(nbytes / (tu * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+    if target is not None:
+        d["target_frac"] = target
+    return d
+
+
+def sha256_buffers(bufs):
+    """SHA-256 of each host buffer's bytes (one thread per buffer)."""
+    with ThreadPoolExecutor(max(1, min(len(bufs), 16))) as ex:
+        return list(ex.map(lambda b: hashlib.sha256(memoryview(b).cast("B")).hexdigest(), bufs))
+
+
+def cpu_threads():
+    # the GPU box gives one GPU's job 16 host threads, whatever the OS shows
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+class Timer:
+    """Back-to-back launches captured in one HIP graph, timed with HIP events
+    on the stream the graph replays on (torch's current stream, which is the
+    stream the binding launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.z = torch.cuda.Event(enable_timing=True)
+
+    def capture(self, calls):
+        g = self.torch.cuda.CUDAGraph()
+        with self.torch.cuda.graph(g):
+            for c in calls:
+                c()
+        return g
+
+    def timed(self, run, reps_inner):
+        """ms per inner repetition of run()."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        self.a.record(self.stream)
+        run()
+        self.z.record(self.stream)
+        torch.cuda.synchronize()
+        return self.a.elapsed_time(self.z) / reps_inner
+
+    def us_per_launch(self, calls):
+        g = self.capture(calls)
+        g.replay()
+        us = self.timed(g.replay, len(calls)) * 1000.0
+        del g
+        return us
+
+
+def auto_reps(nbytes, lo=8, hi=2000):
+    """Enough launches for ~50 ms of HBM traffic at 4 TB/s."""
+    return max(lo, min(hi, int(0.05 / max(1e-9, nbytes / 4e12))))
+
+
+def nsets_for(bytes_per_set, torch, cap=1024):
+    free, _ = torch.cuda.mem_get_info()
+    n = -(-ROTATE_BYTES // max(1, bytes_per_set))
+    return max(1, min(cap, n, int(0.5 * free // max(1, bytes_per_set))))
+
+
+def upload(host, torch, dev):
+    import numpy as np
+    out = []
+    for h in host:
+        t = torch.from_numpy(h.view(np.int16) if h.dtype == np.uint16 else h).to(dev)
+        out.append(t.view(torch.bfloat16) if h.dtype == np.uint16 else t)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# the step workload
+# ---------------------------------------------------------------------------
 
 class Batch:
     """One set of device buffers for a step."""
 
-    def __init__(self, w, srcs_dev, lp_fmt, lp_block, torch):
+    def __init__(self, w, srcs_dev, lp_block, torch):
         dev = srcs_dev[0].device
         n, count = w.nsrc, w.count
         dt = srcs_dev[0].dtype
@@ -130,28 +241,11 @@ class Batch:
         self.lp_dst_scales = [torch.empty(nb, dtype=torch.float32, device=dev) for _ in range(n)]
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: this benchmark runs on one GPU only (got --gpus {args.gpus}); "
-              "the multi-GPU collective is out of scope here", file=sys.stderr)
-        sys.exit(2)
-
+def step_workload(args, torch, rx, G, timer):
     import numpy as np
-    import torch
-
-    import allreduce_reduction_rx_amd as rx
-    import rxgen as G
-
-    if not torch.cuda.is_available():
-        print("bench.py: no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    rx.lib()  # fail loudly if the HIP library is missing
-    torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream()
-
-    w = G.WORKLOADS[args.workload]
+    wname = args.workload
+    w = G.WORKLOADS[wname]
     n, count = w.nsrc, w.count
     e = w.elem_bytes
     if w.fp8:
@@ -161,15 +255,11 @@ def main():
     nb = -(-count // lp_block)
     tdt = torch.bfloat16 if w.dtype == G.BF16 else torch.float32
 
-    # ---- inputs: generate once on the host, upload, replicate on device ----
     host = w.sources()
-    base = []
-    for h in host:
-        t = torch.from_numpy(h.view(np.int16) if h.dtype == np.uint16 else h).to(dev)
-        base.append(t.view(tdt) if h.dtype == np.uint16 else t)
+    hashes = sha256_buffers(host)
+    base = upload(host, torch, dev)
     chunk_lo, chunk_hi = rx.rx_tree_chunk(count, n, w.dtype, 0)
     chunk = chunk_hi - chunk_lo
-
     lp_lo, lp_hi = rx.rx_lp_tree_chunk(count, n, lp_block, 0)
     lp_chunk = lp_hi - lp_lo
     bytes_k = {
@@ -179,35 +269,20 @@ def main():
         "dequant_reduce_requant": n * (count + 4 * nb) + (count + 4 * nb) + count * e,
     }
     step_bytes = sum(bytes_k.values())
-    # measured beside the step, not part of it: the low-precision tree step
-    # and the whole local allreduce (every buffer read once and written once;
-    # low precision: quantize every buffer, then one pass that reduces,
-    # requantizes, dequantizes and writes every buffer)
+    # measured beside the step, not part of it
     bytes_k["lp_tree_step"] = 2 * n * (lp_chunk + 4 * (lp_chunk // lp_block))
-    # the separate dequantization of the requantized message (SUM, one
-    # source) and the flat low-precision reduce without requantization (SUM
-    # over the N quantized sources), both into the message's dtype
     bytes_k["dequant_separate"] = (count + 4 * nb) + count * e
     bytes_k["lp_flat_sum"] = n * (count + 4 * nb) + count * e
     bytes_k["allreduce_local_flat"] = 2 * n * count * e
     bytes_k["allreduce_local_tree"] = 2 * n * count * e
-    bytes_k["allreduce_local_lowprec"] = (n * (count * e + count + 4 * nb)   # quantize
-                                          + n * (count + 4 * nb) + n * count * e)  # reduce + write all
-    per_batch_bytes = (n * count * e            # sources
-                       + count * e              # flat out
-                       + n * count * e          # tree destinations
-                       + n * (count + 4 * nb)   # codes + scales
-                       + count + 4 * nb + count * e
-                       + n * (count + 4 * nb))    # low-precision tree destinations
-    if args.warm:
-        nsets = 1
-    else:
-        nsets = max(1, min(256, -(-(2 << 30) // per_batch_bytes)))
-    free, _ = torch.cuda.mem_get_info()
-    nsets = max(1, min(nsets, int(0.6 * free // per_batch_bytes)))
-    batches = [Batch(w, base, lp_fmt, lp_block, torch)]
+    bytes_k["allreduce_local_lowprec"] = (n * (count * e + count + 4 * nb)
+                                          + n * (count + 4 * nb) + n * count * e)
+    per_batch_bytes = (n * count * e + count * e + n * count * e + n * (count + 4 * nb)
+                       + count + 4 * nb + count * e + n * (count + 4 * nb))
+    nsets = 1 if args.warm else nsets_for(per_batch_bytes, torch, cap=256)
+    batches = [Batch(w, base, lp_block, torch)]
     for _ in range(nsets - 1):
-        batches.append(Batch(w, [b.clone() for b in base], lp_fmt, lp_block, torch))
+        batches.append(Batch(w, [b.clone() for b in base], lp_block, torch))
     torch.cuda.synchronize()
 
     def k_flat(b, i):
@@ -245,253 +320,328 @@ def main():
 
     # whole in-place local allreduce (rx_allreduce_local), on buffers of
     # zeros so that repeated in-place sums stay finite (kernel time does not
-    # depend on the values)
-    ar_bufs = [[torch.zeros(count, dtype=tdt, device=dev) for _ in range(n)]
-               for _ in range(max(1, min(nsets, 32)))]
+    # depend on the values); one workspace per set, sets rotating over
+    # >= 2 GiB like the batches
     ws_bytes = rx.rx_allreduce_local_workspace(n, count, lp_block)
-    ar_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ar_set_bytes = n * count * e + ws_bytes
+    n_ar = 1 if args.warm else nsets_for(ar_set_bytes, torch)
+    ar_bufs = [[torch.zeros(count, dtype=tdt, device=dev) for _ in range(n)] for _ in range(n_ar)]
+    ar_ws = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(n_ar)]
 
     def k_ar_flat(b, i):
-        rx.rx_allreduce_local(ar_bufs[i % len(ar_bufs)], rx.RX_ALGO_FLAT, lp_fmt, lp_block)
+        rx.rx_allreduce_local(ar_bufs[i % n_ar], rx.RX_ALGO_FLAT, lp_fmt, lp_block)
 
     def k_ar_tree(b, i):
-        rx.rx_allreduce_local(ar_bufs[i % len(ar_bufs)], rx.RX_ALGO_TREE, lp_fmt, lp_block)
+        rx.rx_allreduce_local(ar_bufs[i % n_ar], rx.RX_ALGO_TREE, lp_fmt, lp_block)
 
     def k_ar_lp(b, i):
-        rx.rx_allreduce_local(ar_bufs[i % len(ar_bufs)], rx.RX_ALGO_LOWPREC, lp_fmt, lp_block, ar_ws)
+        rx.rx_allreduce_local(ar_bufs[i % n_ar], rx.RX_ALGO_LOWPREC, lp_fmt, lp_block,
+                              ar_ws[i % n_ar])
 
     kernels_timed = kernels + [("lp_tree_step", k_lp_tree), ("dequant_separate", k_dequant),
                                ("lp_flat_sum", k_lp_flat), ("allreduce_local_flat", k_ar_flat),
                                ("allreduce_local_tree", k_ar_tree),
                                ("allreduce_local_lowprec", k_ar_lp)]
 
-    def capture(calls):
-        """HIP graph of the given launches (captured on torch's capture
-        stream, which is the stream the binding launches on)."""
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for c in calls:
-                c()
-        return g
-
-    def timed(run, reps_inner):
-        """ms per inner repetition of run(), HIP events on the launch stream."""
-        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        run()
-        z.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(z) / reps_inner
-
     # ---- whole-step timing: W untimed steps, then exactly K timed steps ----
-    if args.no_graph:
-        for i in range(args.warmup):
-            step(i)
-        t_wall = time.perf_counter()
-        step_ms = timed(lambda: [step(i) for i in range(args.steps)], args.steps)
-        wall_s = time.perf_counter() - t_wall
-    else:
-        g_warm = capture([lambda i=i: step(i) for i in range(max(1, args.warmup))])
-        g_steps = capture([lambda i=i: step(i) for i in range(args.steps)])
-        if args.warmup:
-            g_warm.replay()
-        t_wall = time.perf_counter()
-        step_ms = timed(g_steps.replay, args.steps)
-        wall_s = time.perf_counter() - t_wall
-        del g_warm, g_steps
+    g_warm = timer.capture([lambda i=i: step(i) for i in range(max(1, args.warmup))])
+    g_steps = timer.capture([lambda i=i: step(i) for i in range(args.steps)])
+    if args.warmup:
+        g_warm.replay()
+    t_wall = time.perf_counter()
+    step_ms = timer.timed(g_steps.replay, args.steps)
+    wall_s = time.perf_counter() - t_wall
+    del g_warm, g_steps
 
     # ---- per-kernel timing: back-to-back launches of one kernel ----
     per_kernel = {}
     for name, fn in kernels_timed:
-        reps = args.kernel_reps or max(50, min(2000, int(0.05 / max(1e-7, bytes_k[name] / 4e12))))
-        calls = [lambda i=i: fn(batches[i % nsets], i) for i in range(reps)]
-        if args.no_graph:
-            for c in calls[:10]:
-                c()
-            us = timed(lambda: [c() for c in calls], reps) * 1000.0
-        else:
-            g = capture(calls)
-            g.replay()
-            us = timed(g.replay, reps) * 1000.0
-            del g
-        gbs = bytes_k[name] / (us * 1e-6) / 1e9
-        per_kernel[name] = {"us": round(us, 3), "GB/s": round(gbs, 1),
-                            "frac": round(gbs / PEAK_HBM_GBS, 4),
-                            "bytes": bytes_k[name], "launches": reps}
+        reps = args.kernel_reps or auto_reps(bytes_k[name], lo=50)
+        us = timer.us_per_launch([lambda i=i: fn(batches[i % nsets], i) for i in range(reps)])
+        per_kernel[name] = entry(bytes_k[name], us, reps, wname, name)
 
-    # ---- the tree step for each rank on its own (median over ranks) ----
+    # ---- the tree step for each rank on its own ----
     by_rank = []
     for k in range(n):
         reps = per_kernel["tree_step"]["launches"]
-        calls = [lambda i=i, k=k: rx.rx_reduce_scatter_chunk_bcast(batches[i % nsets].srcs, k,
-                                                                   batches[i % nsets].tree_dsts)
-                 for i in range(reps)]
-        if args.no_graph:
-            us = timed(lambda: [c() for c in calls], reps) * 1000.0
-        else:
-            g = capture(calls)
-            g.replay()
-            us = timed(g.replay, reps) * 1000.0
-            del g
-        by_rank.append(round(us, 3))
+        by_rank.append(round(timer.us_per_launch(
+            [lambda i=i, k=k: rx.rx_reduce_scatter_chunk_bcast(batches[i % nsets].srcs, k,
+                                                               batches[i % nsets].tree_dsts)
+             for i in range(reps)]), 3))
 
-    # ---- the flat reduce over the first k rank buffers, k = 1..N (DDA
-    # flat's latency against the number of ranks, one GPU's share) ----
+    # ---- the flat reduce over the first k rank buffers, k = 1..N ----
     flat_by_nsrc = []
     for k in range(1, n + 1):
         reps = per_kernel["reduce_flat"]["launches"]
-        calls = [lambda i=i, k=k: rx.rx_reduce_flat(batches[i % nsets].srcs[:k],
-                                                    batches[i % nsets].flat_out)
-                 for i in range(reps)]
-        if args.no_graph:
-            us = timed(lambda: [c() for c in calls], reps) * 1000.0
-        else:
-            g = capture(calls)
-            g.replay()
-            us = timed(g.replay, reps) * 1000.0
-            del g
-        flat_by_nsrc.append(round(us, 3))
+        flat_by_nsrc.append(round(timer.us_per_launch(
+            [lambda i=i, k=k: rx.rx_reduce_flat(batches[i % nsets].srcs[:k],
+                                                batches[i % nsets].flat_out)
+             for i in range(reps)]), 3))
 
-    # ---- parity spot check of batch 0 against the oracle-free invariants:
-    # the tree chunk must equal the flat result on that chunk ----
+    # ---- invariant spot check of batch 0: the tree chunk equals the flat
+    # result on that chunk ----
     b0 = batches[0]
     rx.rx_reduce_flat(b0.srcs, b0.flat_out)
     rx.rx_reduce_scatter_chunk_bcast(b0.srcs, 0, b0.tree_dsts)
     torch.cuda.synchronize()
     lo, hi = rx.rx_tree_chunk(count, n, w.dtype, 0)
-    tree_ok = all(torch.equal(d[lo:hi].view(torch.int16 if tdt == torch.bfloat16 else torch.int32),
-                              b0.flat_out[lo:hi].view(torch.int16 if tdt == torch.bfloat16 else torch.int32))
-                  for d in b0.tree_dsts)
+    iv = torch.int16 if tdt == torch.bfloat16 else torch.int32
+    tree_ok = all(torch.equal(d[lo:hi].view(iv), b0.flat_out[lo:hi].view(iv)) for d in b0.tree_dsts)
 
-    dominant = max((k for k, _ in kernels), key=lambda k: per_kernel[k]["us"])
-    dk = per_kernel[dominant]
-    traffic = read_traffic(dominant, args.workload)
-    value = step_bytes / (step_ms * 1e-3) / 1e9
+    us_single, us_events = single_launch_us(torch, rx, k_flat, batches, timer.stream)
 
-    us_single, us_events = single_launch_us(torch, rx, k_flat, batches, stream)
-    floors = launch_floors(torch, rx, n * count * e) if n * count * e <= (64 << 20) else None
-    copy = copy_ceiling(torch, stream)
-    ceil = stream_ceilings(torch, rx, stream)
-    for k in per_kernel.values():
-        k["frac_of_copy_ceiling"] = round(k["GB/s"] / ceil["copy"]["GB/s"], 4)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, host, lp_fmt, lp_block, args.cpu_seconds, step_bytes)
-
-    e_name = "BF16" if w.dtype == G.BF16 else "FP32"
-    line = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {
-            "workload": f"{args.workload}: {n} x {count} {e_name} rank buffers "
-                        f"({count * e / 1024:.0f} KiB each), step = flat reduce + tree step "
-                        f"(chunk {chunk}) + FP8 quant ({lp_fmt}, block {lp_block}) + "
-                        f"dequant-reduce-requant with {e_name} output",
-            "nsrc": n, "count": count, "io_dtype": e_name.lower(),
-            "fp8": lp_fmt, "block": lp_block,
-            "cache": "warm (one batch reused)" if args.warm else f"cold (rotating {nsets} batches, "
-                     f"{nsets * per_batch_bytes / 2**30:.2f} GiB)",
-            "step_bytes": step_bytes,
-        },
-        "roofline": {
-            "bound": "hbm", "kernel": dominant,
-            "achieved": dk["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(dk["GB/s"] / PEAK_HBM_GBS, 4),
-            "traffic": traffic,
-        },
-        "kernels": per_kernel,
-        "us_reduce_flat": per_kernel["reduce_flat"]["us"],
-        "reduce_flat_us_by_nsrc": flat_by_nsrc,
-        "tree_step_by_rank_us": by_rank,
-        "tree_step_median_over_ranks_us": sorted(by_rank)[len(by_rank) // 2],
-        "us_reduce_flat_single_launch": us_single,
-        "us_event_pair_alone": us_events,
-        "launch_floors": floors,
-        "tree_matches_flat": bool(tree_ok),
-        "copy_ceiling": copy,
-        "stream_ceilings": ceil,
-        "wall_s": round(wall_s, 4),
-        "launch": "python loop" if args.no_graph else "HIP graph replay",
-        "cpu_baseline": cpu,
+    out = {
+        "w": w, "host": host, "hashes": hashes, "lp_fmt": lp_fmt, "lp_block": lp_block,
+        "step_ms": step_ms, "wall_s": wall_s, "step_bytes": step_bytes, "chunk": chunk,
+        "nsets": nsets, "per_batch_bytes": per_batch_bytes, "per_kernel": per_kernel,
+        "by_rank": by_rank, "flat_by_nsrc": flat_by_nsrc, "tree_ok": tree_ok,
+        "us_single": us_single, "us_events": us_events, "kernels": [k for k, _ in kernels],
+        "n_ar_sets": n_ar, "ar_set_bytes": ar_set_bytes,
     }
-    print(json.dumps(line), flush=True)
-
-
-def copy_ceiling(torch, stream):
-    """A plain device-to-device copy of 1 GiB (4x the Infinity Cache), the
-    practical streaming ceiling on this GPU: (read + write bytes) / time."""
-    nbytes = 1 << 30
-    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    reps = 20
-    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    del batches, ar_bufs, ar_ws, base
     torch.cuda.synchronize()
-    a.record(stream)
-    for _ in range(reps):
-        dst.copy_(src)
-    z.record(stream)
-    torch.cuda.synchronize()
-    us = a.elapsed_time(z) * 1000.0 / reps
-    gbs = 2 * nbytes / (us * 1e-6) / 1e9
-    del src, dst
     torch.cuda.empty_cache()
-    return {"GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "bytes": 2 * nbytes, "us": round(us, 1)}
+    return out
 
 
-def stream_ceilings(torch, rx, stream):
+# ---------------------------------------------------------------------------
+# the five message shapes
+# ---------------------------------------------------------------------------
+
+def describe(w):
+    e_name = "BF16" if w.dtype == 1 else "FP32"
+    s = f"{w.nsrc} x {w.count:,} {e_name} ({w.count * w.elem_bytes / 1024:.0f} KiB per rank), seed {w.seed}"
+    if w.fp8:
+        s += f", {w.fp8.upper()} blocks of {w.block}"
+    return s
+
+
+def cfg_flat_small(wname, torch, rx, G, timer, reps=2000):
+    """cfg1: the pages' rank-id example and its U[-1,1) companion."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    w = G.WORKLOADS[wname]
+    host = w.sources()
+    srcs = upload(host, torch, dev)
+    dst = torch.empty(w.count, dtype=torch.float32, device=dev)
+    nbytes = (w.nsrc + 1) * w.count * w.elem_bytes
+    us = timer.us_per_launch([lambda: rx.rx_reduce_flat(srcs, dst)] * reps)
+    rx.rx_reduce_flat(srcs, dst)
+    torch.cuda.synchronize()
+    d = {"workload": describe(w), "input_sha256": sha256_buffers(host),
+         "cache": "warm (7.2 KB; every launch reads the same buffers)",
+         "kernels": {"reduce_flat": entry(nbytes, us, reps, None, None)}}
+    if wname == "flat_rank":
+        d["check"] = "28.0 everywhere" if bool((dst == 28.0).all()) else "MISMATCH"
+    return d
+
+
+def cfg_tree(torch, rx, G, timer):
+    """cfg3: the tree step on 8 x 4 MiB BF16, every rank, rotating sets."""
+    dev = torch.device("cuda:0")
+    w = G.WORKLOADS["tree"]
+    n, count, e = w.nsrc, w.count, w.elem_bytes
+    host = w.sources()
+    hashes = sha256_buffers(host)
+    base = upload(host, torch, dev)
+    set_bytes = 2 * n * count * e
+    nsets = nsets_for(set_bytes, torch)
+    sets = [(base, [torch.empty_like(base[0]) for _ in range(n)])]
+    for _ in range(nsets - 1):
+        sets.append(([b.clone() for b in base], [torch.empty_like(base[0]) for _ in range(n)]))
+    lo, hi = rx.rx_tree_chunk(count, n, w.dtype, 0)
+    nbytes = 2 * n * (hi - lo) * e
+    reps = 1000
+    by_rank = []
+    for k in range(n):
+        by_rank.append(timer.us_per_launch(
+            [lambda i=i, k=k: rx.rx_reduce_scatter_chunk_bcast(sets[i % nsets][0], k,
+                                                               sets[i % nsets][1])
+             for i in range(reps)]))
+    med = sorted(by_rank)[n // 2]
+    tree = entry(nbytes, med, reps, "tree", "tree_step", target=0.4)
+    tree["us_by_rank"] = [round(x, 3) for x in by_rank]
+    tree["statistic"] = "median over the 8 ranks"
+    fbytes = (n + 1) * count * e
+    freps = auto_reps(fbytes, lo=100)
+    flat_out = [torch.empty_like(base[0]) for _ in range(nsets)]
+    us = timer.us_per_launch([lambda i=i: rx.rx_reduce_flat(sets[i % nsets][0], flat_out[i % nsets])
+                              for i in range(freps)])
+    out = {"workload": describe(w) + f", chunk {hi - lo:,}", "input_sha256": hashes,
+           "cache": f"cold (rotating {nsets} sets, {nsets * set_bytes / 2**30:.2f} GiB)",
+           "kernels": {"tree_step": tree,
+                       "reduce_flat": entry(fbytes, us, freps, "tree", "reduce_flat")}}
+    del sets, base, flat_out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def cfg_lp(wname, torch, rx, G, timer, ceilings):
+    """cfg4 / cfg5: quantizer, DRR-REQUANT with and without the
+    high-precision output, separate dequantization, each rotating over
+    >= 2 GiB (or one launch where a launch moves that much)."""
+    dev = torch.device("cuda:0")
+    w = G.WORKLOADS[wname]
+    n, count, e, fmt, block = w.nsrc, w.count, w.elem_bytes, w.fp8, w.block
+    nb = -(-count // block)
+    tdt = torch.bfloat16 if w.dtype == G.BF16 else torch.float32
+    t0 = time.perf_counter()
+    host = w.sources()
+    hashes = sha256_buffers(host)
+    base = upload(host, torch, dev)
+    del host
+    gen_s = time.perf_counter() - t0
+    kern = {}
+
+    def codes_like():
+        return ([torch.empty(count, dtype=torch.uint8, device=dev) for _ in range(n)],
+                [torch.empty(nb, dtype=torch.float32, device=dev) for _ in range(n)])
+
+    # quantizer: sources + codes + scales per set
+    q_bytes = n * (count * e + count + 4 * nb)
+    nq = nsets_for(q_bytes, torch)
+    qsets = [(base,) + codes_like()]
+    for _ in range(nq - 1):
+        qsets.append(([b.clone() for b in base],) + codes_like())
+    reps = auto_reps(q_bytes)
+    us = timer.us_per_launch([lambda i=i: rx.rx_quant_fp8(qsets[i % nq][0], fmt, block,
+                                                          qsets[i % nq][1], qsets[i % nq][2])
+                              for i in range(reps)])
+    kern["quant_fp8"] = entry(q_bytes, us, reps, wname, "quant_fp8", target=0.8)
+    # flat reduce of the same message (the full-precision leg)
+    f_bytes = (n + 1) * count * e
+    flat_out = [torch.empty(count, dtype=tdt, device=dev) for _ in range(nq)]
+    reps = auto_reps(f_bytes)
+    us = timer.us_per_launch([lambda i=i: rx.rx_reduce_flat(qsets[i % nq][0], flat_out[i % nq])
+                              for i in range(reps)])
+    kern["reduce_flat"] = entry(f_bytes, us, reps, wname, "reduce_flat", target=0.8)
+    rx.rx_quant_fp8(base, fmt, block, qsets[0][1], qsets[0][2])
+    codes0, scales0 = qsets[0][1], qsets[0][2]
+    del flat_out
+    for s in qsets[1:]:
+        del s
+    qsets = None
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    # DRR: codes + scales in, requantized codes + scales (+ hp) out
+    in_bytes = n * (count + 4 * nb)
+    out_q = count + 4 * nb
+    d_set = in_bytes + out_q + count * e
+    nd = nsets_for(d_set, torch)
+    dsets = []
+    for j in range(nd):
+        c = codes0 if j == 0 else [x.clone() for x in codes0]
+        s = scales0 if j == 0 else [x.clone() for x in scales0]
+        dsets.append((c, s, torch.empty(count, dtype=torch.uint8, device=dev),
+                      torch.empty(nb, dtype=torch.float32, device=dev),
+                      torch.empty(count, dtype=tdt, device=dev)))
+    hp_name = "drr_requant_bf16_out" if tdt == torch.bfloat16 else "drr_requant_fp32_out"
+    for name, with_hp in (("drr_requant", False), (hp_name, True)):
+        nbytes = in_bytes + out_q + (count * e if with_hp else 0)
+        reps = auto_reps(nbytes)
+        us = timer.us_per_launch(
+            [lambda i=i, h=with_hp: rx.rx_dequant_reduce_requant(
+                dsets[i % nd][0], dsets[i % nd][1], fmt, block, rx.RX_DRR_REQUANT,
+                dsets[i % nd][2], dsets[i % nd][3], dsets[i % nd][4] if h else None)
+             for i in range(reps)])
+        kern[name] = entry(nbytes, us, reps, wname,
+                           "drr_requant_hp" if with_hp else "drr_requant", target=0.8)
+    # separate dequantization of the requantized message (N = 1, SUM), with
+    # its own rotation: requantized codes + scales in, the message dtype out
+    rx.rx_dequant_reduce_requant(codes0, scales0, fmt, block, rx.RX_DRR_REQUANT,
+                                 dsets[0][2], dsets[0][3])
+    dq_bytes = out_q + count * e
+    nq2 = nsets_for(dq_bytes, torch)
+    qsets2 = [(dsets[0][2], dsets[0][3], dsets[0][4])]
+    for _ in range(nq2 - 1):
+        qsets2.append((dsets[0][2].clone(), dsets[0][3].clone(),
+                       torch.empty(count, dtype=tdt, device=dev)))
+    reps = auto_reps(dq_bytes)
+    us = timer.us_per_launch([lambda i=i: rx.rx_dequant_reduce_requant(
+        [qsets2[i % nq2][0]], [qsets2[i % nq2][1]], fmt, block, rx.RX_DRR_SUM,
+        out_hp=qsets2[i % nq2][2]) for i in range(reps)])
+    kern["dequant_separate"] = entry(dq_bytes, us, reps, wname, "dequant_separate", target=0.8)
+
+    if ceilings:
+        ratio_kind = {
+            "quant_fp8": ("narrow4" if e == 4 else "narrow2"),
+            "reduce_flat": f"reduce{n}",
+            "drr_requant": f"reduce{n}",
+            hp_name: f"reduce{max(1, round(in_bytes / (out_q + count * e)))}",
+            "dequant_separate": "copy",
+        }
+        for name, kind in ratio_kind.items():
+            c = ceilings.get(kind)
+            if c:
+                kern[name]["mixed_ceiling"] = kind
+                kern[name]["frac_of_mixed_ceiling"] = round(kern[name]["GB/s"] / c["GB/s"], 4)
+    out = {"workload": describe(w), "input_sha256": hashes,
+           "cache": f"cold (quant rotates {nq} set(s) of {q_bytes / 2**30:.2f} GiB, DRR {nd} of "
+                    f"{d_set / 2**30:.2f} GiB, dequant {nq2} of {dq_bytes / 2**30:.2f} GiB)",
+           "generate_upload_s": round(gen_s, 1), "kernels": kern}
+    del dsets, qsets2, base, codes0, scales0
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# ceilings and floors
+# ---------------------------------------------------------------------------
+
+def stream_ceilings(torch, rx, timer):
     """Read, write and copy rates of the library's plain 16-byte-per-lane
-    streaming kernels over 1 GiB (4x the Infinity Cache), best over 1, 2, 4
-    and 8 workgroups per CU with and without nontemporal hints: the HBM
-    ceilings a streaming kernel reaches on this GPU. Bytes counted: read +
-    written."""
+    streaming kernels over 1 GiB, and the mixed read/write ceilings (the
+    hot-path kernels' access patterns with XOR in place of their arithmetic:
+    reduce N:1 over N sources, 2:1 and 4:1 narrowing), best over 1, 2, 4
+    and 8 workgroups per CU with and without nontemporal hints. Bytes counted:
+    read + written."""
     nbytes = 1 << 30
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
     dst = torch.empty_like(src)
     sink = torch.empty(rx.rxtest_stream_sink_bytes(8) // 4, dtype=torch.float32, device="cuda:0")
-    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     out = {}
-    for kind, name, moved in ((rx.RXTEST_READ, "read", nbytes), (rx.RXTEST_WRITE, "write", nbytes),
-                              (rx.RXTEST_COPY, "copy", 2 * nbytes)):
-        best = None
+
+    def best(run_for, moved, reps=6):
+        b = None
         for wgs in (1, 2, 4, 8):
             for nt in (False, True):
-                d = sink if kind == rx.RXTEST_READ else dst
-                run = lambda: rx.rxtest_stream(kind, src, d, nbytes, wgs, nt, stream)
-                run(); run()
-                reps = 10
-                torch.cuda.synchronize()
-                a.record(stream)
-                for _ in range(reps):
-                    run()
-                z.record(stream)
-                torch.cuda.synchronize()
-                us = a.elapsed_time(z) * 1000.0 / reps
+                us = timer.us_per_launch([lambda wgs=wgs, nt=nt: run_for(wgs, nt)] * reps)
                 gbs = moved / (us * 1e-6) / 1e9
-                if best is None or gbs > best["GB/s"]:
-                    best = {"GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
-                            "wgs_per_cu": wgs, "nontemporal": nt}
-        out[name] = best
+                if b is None or gbs > b["GB/s"]:
+                    b = {"GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+                         "wgs_per_cu": wgs, "nontemporal": nt}
+        return b
+
+    out["read"] = best(lambda wgs, nt: rx.rxtest_stream(rx.RXTEST_READ, src, sink, nbytes, wgs, nt),
+                       nbytes)
+    out["write"] = best(lambda wgs, nt: rx.rxtest_stream(rx.RXTEST_WRITE, None, dst, nbytes, wgs, nt),
+                        nbytes)
+    out["copy"] = best(lambda wgs, nt: rx.rxtest_stream(rx.RXTEST_COPY, src, dst, nbytes, wgs, nt),
+                       2 * nbytes)
+    if not hasattr(rx, "rxtest_stream_mixed"):
+        del src, dst, sink
+        torch.cuda.empty_cache()
+        return out
+    # mixed: 1 GiB read in total
+    for k in (8, 3, 2):
+        per = nbytes // k // 16 * 16
+        srcs = [src.view(torch.uint8)[j * per:(j + 1) * per] for j in range(k)]
+        out[f"reduce{k}"] = best(lambda wgs, nt, srcs=srcs, per=per: rx.rxtest_stream_mixed(
+            rx.RXTEST_MIXED_REDUCE, srcs, dst.view(torch.uint8)[:per], per, wgs, nt),
+            (k + 1) * per)
+    for kind, k in ((rx.RXTEST_MIXED_NARROW2, 2), (rx.RXTEST_MIXED_NARROW4, 4)):
+        out[f"narrow{k}"] = best(lambda wgs, nt, kind=kind, k=k: rx.rxtest_stream_mixed(
+            kind, [src], dst.view(torch.uint8)[:nbytes // k], nbytes, wgs, nt),
+            nbytes + nbytes // k)
     del src, dst, sink
     torch.cuda.empty_cache()
     return out
 
 
-def launch_floors(torch, rx, in_bytes, reps=256):
+def launch_floors(torch, rx, timer, in_bytes, reps=256):
     """What a plain streaming kernel costs per back-to-back launch at this
     message size, cold (graph replay, each launch on its own slice of a
     1 GiB rotation): a launch with no memory access, a read of in_bytes, and
@@ -502,29 +652,12 @@ def launch_floors(torch, rx, in_bytes, reps=256):
     src = torch.zeros(total // 4, dtype=torch.float32, device="cuda:0")
     dst = torch.zeros_like(src)
     sink = torch.empty(rx.rxtest_stream_sink_bytes(8) // 4, dtype=torch.float32, device="cuda:0")
-    stream = torch.cuda.current_stream()
-    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     per = in_bytes // 4
-
-    def timed(calls):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for c in calls:
-                c()
-        g.replay()
-        torch.cuda.synchronize()
-        a.record(stream)
-        g.replay()
-        z.record(stream)
-        torch.cuda.synchronize()
-        del g
-        return a.elapsed_time(z) * 1000.0 / len(calls)
-
     out = {"bytes": in_bytes}
-    out["empty_us"] = round(timed([lambda: rx.rxtest_stream(rx.RXTEST_EMPTY, None, None, 0, 1)
-                                   for _ in range(reps)]), 3)
+    out["empty_us"] = round(timer.us_per_launch(
+        [lambda: rx.rxtest_stream(rx.RXTEST_EMPTY, None, None, 0, 1)] * reps), 3)
     for kind, name in ((rx.RXTEST_READ, "read_us"), (rx.RXTEST_COPY, "copy_us")):
-        best = None
+        b = None
         for wgs in (1, 2, 4):
             for nt in (False, True):
                 calls = []
@@ -534,9 +667,9 @@ def launch_floors(torch, rx, in_bytes, reps=256):
                     d_ = sink if kind == rx.RXTEST_READ else dst[k * per:(k + 1) * per]
                     calls.append(lambda s_=s_, d_=d_, wgs=wgs, nt=nt:
                                  rx.rxtest_stream(kind, s_, d_, in_bytes, wgs, nt))
-                us = timed(calls)
-                best = us if best is None else min(best, us)
-        out[name] = round(best, 3)
+                us = timer.us_per_launch(calls)
+                b = us if b is None else min(b, us)
+        out[name] = round(b, 3)
     del src, dst, sink
     torch.cuda.empty_cache()
     return out
@@ -561,7 +694,6 @@ def single_launch_us(torch, rx, fn, batches, stream, reps=200):
         z.record(stream)
     torch.cuda.synchronize()
     ts = sorted(a.elapsed_time(z) * 1000.0 for a, z in evs[10:])
-    # the same pair of events with nothing between them
     for a, z in evs:
         rx.rxtest_stream(rx.RXTEST_READ, busy, sink, nbytes, 2, True, stream)
         a.record(stream)
@@ -573,10 +705,16 @@ def single_launch_us(torch, rx, fn, batches, stream, reps=200):
     return round(ts[len(ts) // 2], 3), round(t0[len(t0) // 2], 3)
 
 
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, timed on the host cores
+# ---------------------------------------------------------------------------
+
 def cpu_baseline(w, host, lp_fmt, lp_block, seconds, step_bytes):
-    """The oracle (single-threaded plain C) running the same step on a
-    bounded sample: whole steps while they fit in `seconds`, else a prefix of
-    every rank buffer, scaled to GB/s with the same algorithmic bytes."""
+    """The oracle (plain C) running the same step on the same inputs: one
+    host thread, then `cpu_threads()` threads over windows of whole blocks
+    (the tree step, a single call, runs beside them). The oracle is
+    elementwise and block-local, so the windowed run computes the same bits;
+    that is checked on one step."""
     import numpy as np
 
     import oracle as O
@@ -586,29 +724,72 @@ def cpu_baseline(w, host, lp_fmt, lp_block, seconds, step_bytes):
     dt = O.BF16 if w.dtype == 1 else O.FP32
     cnt = w.count
     sample = "full message"
-    # bound the sample: at most 2^22 elements per rank buffer
-    if cnt > (1 << 22):
+    if cnt > (1 << 22):   # bound the sample
         cnt = 1 << 22
-        sample = f"first {cnt} elements of each rank buffer"
-    srcs = [h[:cnt] for h in host]
+        sample = f"first {cnt:,} elements of each rank buffer"
+    srcs = [np.ascontiguousarray(h[:cnt]) for h in host]
     e = w.elem_bytes
     nb = -(-cnt // lp_block)
     lo, hi = O.tree_chunk(cnt, n, dt, 0)
     sbytes = (n * cnt * e + cnt * e) + 2 * n * (hi - lo) * e + n * (cnt * e + cnt + 4 * nb) + \
         n * (cnt + 4 * nb) + (cnt + 4 * nb) + cnt * e
-    dsts = [np.empty(cnt, dtype=srcs[0].dtype) for _ in range(n)]
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        O.reduce_flat(srcs, dt)
-        O.reduce_scatter_chunk_bcast(srcs, dt, reps % n, dsts)
+
+    def one_thread(i):
+        dsts = [np.zeros(cnt, dtype=srcs[0].dtype) for _ in range(n)]
+        flat = O.reduce_flat(srcs, dt)
+        O.reduce_scatter_chunk_bcast(srcs, dt, i % n, dsts)
         codes, scales = O.quant_fp8(srcs, dt, fmt, lp_block)
-        O.dequant_reduce_requant(codes, scales, fmt, lp_block, O.DRR_REQUANT, dt, True)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    gbs = sbytes * reps / el / 1e9
+        r = O.dequant_reduce_requant(codes, scales, fmt, lp_block, O.DRR_REQUANT, dt, True)
+        return flat, dsts, codes, scales, r
+
+    threads = cpu_threads()
+    unit = lp_block * 8
+    win = -(-(-(-cnt // threads)) // unit) * unit
+    wins = [(a, min(a + win, cnt)) for a in range(0, cnt, win)]
+    pool = ThreadPoolExecutor(threads)
+
+    def many_threads(i):
+        dsts = [np.zeros(cnt, dtype=srcs[0].dtype) for _ in range(n)]
+        flat = np.empty(cnt, dtype=srcs[0].dtype)
+        codes = [np.empty(cnt, np.uint8) for _ in range(n)]
+        scales = [np.empty(nb, np.float32) for _ in range(n)]
+        oc, osc = np.empty(cnt, np.uint8), np.empty(nb, np.float32)
+        ohp = np.empty(cnt, dtype=srcs[0].dtype)
+        tree = pool.submit(O.reduce_scatter_chunk_bcast, srcs, dt, i % n, dsts)
+
+        def stage1(ab):
+            a, b = ab
+            x = [s[a:b] for s in srcs]
+            flat[a:b] = O.reduce_flat(x, dt)
+            c, s = O.quant_fp8(x, dt, fmt, lp_block)
+            for j in range(n):
+                codes[j][a:b] = c[j]
+                scales[j][a // lp_block:-(-b // lp_block)] = s[j]
+            r = O.dequant_reduce_requant(c, s, fmt, lp_block, O.DRR_REQUANT, dt, True)
+            oc[a:b], osc[a // lp_block:-(-b // lp_block)], ohp[a:b] = r
+
+        list(pool.map(stage1, wins))
+        tree.result()
+        return flat, dsts, codes, scales, (oc, osc, ohp)
+
+    def run(fn, budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn(reps)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return reps, el
+
+    a = one_thread(3)
+    b = many_threads(3)
+    same = (np.array_equal(a[0], b[0]) and all(np.array_equal(x, y) for x, y in zip(a[1], b[1]))
+            and all(np.array_equal(x, y) for x, y in zip(a[2], b[2]))
+            and all(np.array_equal(x.view(np.uint32), y.view(np.uint32)) for x, y in zip(a[3], b[3]))
+            and all(np.array_equal(x.view(np.uint8), y.view(np.uint8)) for x, y in zip(a[4], b[4])))
+    r1, e1 = run(one_thread, seconds / 2)
+    rn, en = run(many_threads, seconds / 2)
+    pool.shutdown()
     cpu = "unknown CPU"
     try:
         for line in open("/proc/cpuinfo"):
@@ -617,10 +798,139 @@ def cpu_baseline(w, host, lp_fmt, lp_block, seconds, step_bytes):
                 break
     except OSError:
         pass
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} oracle step(s) over the {sample} ({sbytes} algorithmic bytes "
-                      f"per step), {el:.1f} s on one host core ({cpu}, "
-                      f"{os.cpu_count()} logical CPUs visible)"}
+    g1, gn = sbytes * r1 / e1 / 1e9, sbytes * rn / en / 1e9
+    return {"value": round(gn, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the step over the {sample} ({sbytes:,} algorithmic bytes per step): "
+                      f"{rn} step(s) in {en:.1f} s on {threads} host threads, windows of whole "
+                      f"blocks; {cpu}, {os.cpu_count()} logical CPUs visible",
+            "one_thread": {"value": round(g1, 3), "unit": "GB/s", "cores": 1,
+                           "sample": f"{r1} step(s) in {e1:.1f} s"},
+            "threads_bit_identical_to_one": bool(same)}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this benchmark runs on one GPU only (got --gpus {args.gpus}); "
+              "the multi-GPU collective is out of scope here", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import allreduce_reduction_rx_amd as rx
+    import rxgen as G
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    rx.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    timer = Timer(torch)
+
+    def progress(msg):
+        print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+    progress(f"step workload {args.workload}")
+    s = step_workload(args, torch, rx, G, timer)
+    w, n, count = s["w"], s["w"].nsrc, s["w"].count
+    e = w.elem_bytes
+    pk = s["per_kernel"]
+
+    ceil = None
+    if not args.no_ceilings:
+        progress("ceilings")
+        ceil = stream_ceilings(torch, rx, timer)
+        for k in pk.values():
+            k["frac_of_copy_ceiling"] = round(k["GB/s"] / ceil["copy"]["GB/s"], 4)
+    floors = None
+    if n * count * e <= (64 << 20):
+        progress("launch floors")
+        floors = launch_floors(torch, rx, timer, n * count * e)
+
+    configs = {}
+    want = [c for c in args.configs.split(",") if c]
+    if args.workload == "decode":
+        configs["cfg2"] = {"workload": describe(w), "input_sha256": s["hashes"],
+                           "cache": f"cold (rotating {s['nsets']} batches)",
+                           "kernels": {"reduce_flat": dict(pk["reduce_flat"], target_frac=0.4)}}
+    if "cfg1" in want:
+        progress("cfg1")
+        configs["cfg1"] = cfg_flat_small("flat_rank", torch, rx, G, timer)
+        configs["cfg1_uniform"] = cfg_flat_small("flat_uniform", torch, rx, G, timer)
+    if "cfg3" in want:
+        progress("cfg3")
+        configs["cfg3"] = cfg_tree(torch, rx, G, timer)
+    if "cfg4" in want:
+        progress("cfg4")
+        configs["cfg4"] = cfg_lp("lp_fp32", torch, rx, G, timer, ceil)
+    if "cfg5" in want:
+        progress("cfg5")
+        configs["cfg5"] = cfg_lp("lp_bf16", torch, rx, G, timer, ceil)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        progress("cpu baseline")
+        cpu = cpu_baseline(w, s["host"], s["lp_fmt"], s["lp_block"], args.cpu_seconds,
+                           s["step_bytes"])
+
+    dominant = max(s["kernels"], key=lambda k: pk[k]["us"])
+    dk = pk[dominant]
+    value = s["step_bytes"] / (s["step_ms"] * 1e-3) / 1e9
+    e_name = "BF16" if w.dtype == G.BF16 else "FP32"
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(s["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": e_name.lower(),
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: {n} x {count} {e_name} rank buffers "
+                        f"({count * e / 1024:.0f} KiB each), step = flat reduce + tree step "
+                        f"(chunk {s['chunk']}) + FP8 quant ({s['lp_fmt']}, block {s['lp_block']}) + "
+                        f"dequant-reduce-requant with {e_name} output",
+            "nsrc": n, "count": count, "io_dtype": e_name.lower(), "accumulate": "f32",
+            "fp8": s["lp_fmt"], "block": s["lp_block"],
+            "cache": "warm (one batch reused)" if args.warm else
+                     f"cold (rotating {s['nsets']} batches, "
+                     f"{s['nsets'] * s['per_batch_bytes'] / 2**30:.2f} GiB; local allreduce rows "
+                     f"{s['n_ar_sets']} sets, {s['n_ar_sets'] * s['ar_set_bytes'] / 2**30:.2f} GiB)",
+            "step_bytes": s["step_bytes"],
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": dominant,
+            "achieved": dk["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": dk["frac"],
+            "frac_event": dk["frac"], "us_event": dk["us"],
+            "frac_trace": dk.get("frac_trace"), "us_trace": dk.get("us_trace"),
+            "traffic": read_traffic(args.workload, dominant),
+        },
+        "us_at_512KB": ({"event": pk["reduce_flat"]["us"],
+                         "trace": pk["reduce_flat"].get("us_trace")}
+                        if args.workload == "decode" else None),
+        "configs": configs,
+        "kernels": pk,
+        "reduce_flat_us_by_nsrc": s["flat_by_nsrc"],
+        "tree_step_by_rank_us": s["by_rank"],
+        "us_reduce_flat_single_launch": s["us_single"],
+        "us_event_pair_alone": s["us_events"],
+        "launch_floors": floors,
+        "tree_matches_flat": bool(s["tree_ok"]),
+        "stream_ceilings": ceil,
+        "input_sha256": s["hashes"],
+        "wall_s": round(s["wall_s"], 4),
+        "launch": "HIP graph replay",
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":
