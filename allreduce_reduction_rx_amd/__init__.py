@@ -22,7 +22,8 @@ __all__ = [
     "rx_reduce_flat", "rx_reduce_scatter_chunk_bcast", "rx_tree_chunk",
     "rx_quant_fp8", "rx_dequant_reduce_requant", "rx_status_string",
     "rx_lp_reduce_scatter_chunk_bcast", "rx_lp_tree_chunk", "rx_allreduce_local",
-    "rx_allreduce_local_workspace", "RX_ALGO_AUTO", "RX_ALGO_FLAT", "RX_ALGO_TREE",
+    "rx_allreduce_local_workspace", "rx_allreduce_local_noalloc",
+    "RX_NOALLOC_SCRATCH_BYTES", "RX_ALGO_AUTO", "RX_ALGO_FLAT", "RX_ALGO_TREE",
     "RX_ALGO_LOWPREC", "EXPORTED_SYMBOLS",
 ]
 
@@ -30,12 +31,14 @@ RX_FP32, RX_BF16, RX_FP8_E4M3, RX_FP8_E5M2 = 0, 1, 2, 3
 RX_DRR_SUM, RX_DRR_REQUANT = 0, 1
 RX_ALGO_AUTO, RX_ALGO_FLAT, RX_ALGO_TREE, RX_ALGO_LOWPREC = 0, 1, 2, 3
 RX_MAX_SRC = 16
+RX_NOALLOC_SCRATCH_BYTES = 64 << 20
+RX_ERR_SCRATCH = 6
 
 EXPORTED_SYMBOLS = (
     "rx_reduce_flat", "rx_reduce_scatter_chunk_bcast", "rx_tree_chunk",
     "rx_quant_fp8", "rx_dequant_reduce_requant", "rx_status_string",
     "rx_lp_reduce_scatter_chunk_bcast", "rx_lp_tree_chunk", "rx_allreduce_local",
-    "rx_allreduce_local_workspace", "rxtest_block_scale_bits", "rxtest_fp8_encode_bits", "rxtest_fp8_decode", "rxtest_bf16_round_bits",
+    "rx_allreduce_local_workspace", "rx_allreduce_local_noalloc", "rxtest_block_scale_bits", "rxtest_fp8_encode_bits", "rxtest_fp8_decode", "rxtest_bf16_round_bits",
     "rxtest_group_max", "rxtest_stream", "rxtest_stream_sink_bytes", "rxtest_stream_mixed",
 )
 
@@ -85,6 +88,7 @@ def lib() -> ctypes.CDLL:
                                                  _I, _P],
             "rx_lp_tree_chunk": [_SZ, _I, _I, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)],
             "rx_allreduce_local": [_PP, _I, _SZ, _I, _I, _I, _I, _P, _SZ, _P],
+            "rx_allreduce_local_noalloc": [_PP, _I, _SZ, _I, _I, _I, _I, _P],
             "rxtest_fp8_encode_bits": [ctypes.c_uint32, _SZ, _I, _P, _P],
             "rxtest_block_scale_bits": [ctypes.c_uint32, _SZ, _I, _P, _P, _P],
             "rxtest_fp8_decode": [_P, _SZ, _I, _P, _P],
@@ -329,6 +333,23 @@ def rx_allreduce_local(bufs: Sequence, algo: int = RX_ALGO_AUTO, fmt="e4m3", blo
     _check(lib().rx_allreduce_local(_ptr_array([t.data_ptr() for t in bufs]), len(bufs), count,
                                     dt, int(algo), _fp8_code(fmt), block, wptr, wbytes,
                                     _stream(stream)), "rx_allreduce_local")
+
+
+def rx_allreduce_local_noalloc(bufs: Sequence, algo: int = RX_ALGO_AUTO, fmt="e4m3",
+                               block: int = 128, count: Optional[int] = None,
+                               stream=None) -> None:
+    """rx_allreduce_local without a workspace: the low-precision algorithm
+    uses the library's per-device scratch (RX_NOALLOC_SCRATCH_BYTES), so
+    nothing is allocated; calls that overlap on one device race on it."""
+    count = bufs[0].numel() if count is None else count
+    dt = _rx_dtype(bufs[0])
+    for k, t in enumerate(bufs):
+        _gpu(t, f"bufs[{k}]")
+        if t.dtype != bufs[0].dtype or t.numel() < count:
+            raise ValueError(f"bufs[{k}] must be {bufs[0].dtype} with >= {count} elements")
+    _check(lib().rx_allreduce_local_noalloc(_ptr_array([t.data_ptr() for t in bufs]), len(bufs),
+                                            count, dt, int(algo), _fp8_code(fmt), block,
+                                            _stream(stream)), "rx_allreduce_local_noalloc")
 
 
 # ---- test hooks (rx_testhooks.h) -------------------------------------------

@@ -2,6 +2,7 @@
 // packing and launch. Every check runs before the first HIP call, so an
 // invalid call enqueues nothing. The operations are documented in rx.h.
 #include <atomic>
+#include <mutex>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -63,6 +64,15 @@ hipError_t launch_logged(const char* what, const void* fn, dim3 grid, dim3 block
 
 }  // namespace rx
 
+// Scratch of rx_allreduce_local_noalloc: the low-precision algorithm's codes
+// and scales live here instead of in a caller's workspace. One copy per
+// device (the code object's data is instantiated on every device the library
+// runs on), held until the process ends. Host code never passes `scratch`
+// itself to a kernel or a copy (on the host the name stands for a host-side
+// stand-in, not a device address): it uses the address hipGetSymbolAddress
+// returns for the current device, looked up once per device (scratch_ptr).
+static __device__ __align__(256) uint8_t scratch[RX_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr size_t kMaxCount = (size_t)1 << 38;  // elements per buffer
@@ -111,6 +121,164 @@ size_t tree_chunk_len(size_t count, int nsrc, rx_dtype_t dtype)
     return (c + ve - 1) / ve * ve;
 }
 
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];  // per device, set once
+std::mutex g_scratch_mutex;
+
+// This device's scratch address, or nullptr when the device cannot be
+// queried or the lookup fails (reported as RX_ERR_HIP).
+void* scratch_ptr()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p)
+        return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p)
+        return p;
+    void* q = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !q) {
+        fprintf(stderr, "librx: scratch lookup on device %d failed: %s\n", dev, hipGetErrorName(e));
+        return nullptr;
+    }
+    g_scratch_ptr[dev].store(q, std::memory_order_release);
+    return q;
+}
+
+rx_status_t scratch_too_small(size_t need)
+{
+    if (rx::debug_enabled())
+        fprintf(stderr, "librx: the call needs %zu bytes of scratch, the library holds %zu\n",
+                need, (size_t)RX_NOALLOC_SCRATCH_BYTES);
+    return RX_ERR_SCRATCH;
+}
+
+// rx_allreduce_local and rx_allreduce_local_noalloc. With use_scratch the
+// low-precision algorithm's codes and scales go to this device's scratch
+// array (looked up after validation, before the first launch) instead of the
+// caller's workspace; nothing else differs.
+rx_status_t allreduce_local_impl(void* const* bufs, int nsrc, size_t count, rx_dtype_t dtype,
+                                 rx_algo_t algo, rx_dtype_t fp8_dtype, int block,
+                                 void* workspace, size_t workspace_bytes, bool use_scratch,
+                                 hipStream_t stream)
+{
+    if (!bufs)
+        return RX_ERR_NULL;
+    if (nsrc < 1 || nsrc > RX_MAX_SRC || count > kMaxCount || algo < RX_ALGO_AUTO ||
+        algo > RX_ALGO_LOWPREC)
+        return RX_ERR_ARG;
+    if (!hp_type(dtype))
+        return RX_ERR_DTYPE;
+    rx_status_t st = check_ptrs(reinterpret_cast<const void* const*>(bufs), nsrc, true);
+    if (st != RX_OK)
+        return st;
+    const size_t esz = dtype == RX_BF16 ? 2 : 4;
+    if (algo == RX_ALGO_AUTO) {
+        const char* en = getenv("RX_LOW_PRECISION_ENABLE");
+        const bool lp = en && en[0] == '1' && en[1] == '\0' && count * esz >= ((size_t)16 << 20);
+        algo = lp ? RX_ALGO_LOWPREC : RX_ALGO_FLAT;
+    }
+    size_t need = 0;
+    if (algo == RX_ALGO_LOWPREC) {
+        if (!valid_block(block))
+            return RX_ERR_ARG;
+        if ((count / 256 + 1) * (size_t)nsrc >= ((size_t)1 << 32))   // the quantizer's limit
+            return RX_ERR_ARG;
+        if (!fp8_type(fp8_dtype))
+            return RX_ERR_DTYPE;
+        need = rx_allreduce_local_workspace(nsrc, count, block);
+        if (use_scratch) {
+            if (need > workspace_bytes)
+                return scratch_too_small(need);
+        } else {
+            if (!workspace)
+                return RX_ERR_NULL;
+            if (((uintptr_t)workspace & 255u) != 0)
+                return RX_ERR_ALIGN;
+            if (workspace_bytes < need)
+                return RX_ERR_ARG;
+        }
+    }
+    if (use_scratch) {
+        // the set-up runs on every call (also count == 0 and the algorithms
+        // that need no scratch), so a caller can make it happen outside a
+        // stream capture; after the first call on a device it is a lookup
+        workspace = scratch_ptr();
+        if (!workspace)
+            return RX_ERR_HIP;
+    }
+    if (count == 0)
+        return RX_OK;
+    const int dt = dtype == RX_BF16 ? 1 : 0;
+
+    if (algo == RX_ALGO_FLAT || algo == RX_ALGO_TREE) {
+        rx::TreeArgs a = {};
+        for (int j = 0; j < nsrc; ++j) {
+            a.src[j] = bufs[j];
+            a.dst[j] = bufs[j];
+        }
+        if (algo == RX_ALGO_FLAT) {
+            a.lo = 0;
+            a.hi = count;
+            return launched(rx::launch_tree(a, nsrc, dt, stream));
+        }
+        for (int k = 0; k < nsrc; ++k) {
+            rx_tree_chunk(count, nsrc, dtype, k, &a.lo, &a.hi);
+            if (a.lo >= a.hi)
+                continue;
+            rx_status_t r = launched(rx::launch_tree(a, nsrc, dt, stream));
+            if (r != RX_OK)
+                return r;
+        }
+        return RX_OK;
+    }
+
+    // low precision: codes and scales of every rank in the workspace
+    const size_t nb = (count + (size_t)block - 1) / (size_t)block;
+    const int fmt = fp8_dtype == RX_FP8_E5M2 ? 1 : 0;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    void* codes[RX_MAX_SRC];
+    float* scales[RX_MAX_SRC];
+    for (int j = 0; j < nsrc; ++j) {
+        codes[j] = ws + (size_t)j * round256(count);
+        scales[j] = reinterpret_cast<float*>(ws + (size_t)nsrc * round256(count) +
+                                             (size_t)j * round256(nb * sizeof(float)));
+    }
+    rx::QuantArgs q = {};
+    for (int j = 0; j < nsrc; ++j) {
+        q.src[j] = bufs[j];
+        q.codes[j] = codes[j];
+        q.scales[j] = scales[j];
+    }
+    q.count = count;
+    q.nsrc = nsrc;
+    rx_status_t r = launched(rx::launch_quant(q, dt, fmt, block, stream));
+    if (r != RX_OK)
+        return r;
+    // On one device the nsrc ranks' low-precision tree steps (each reducing
+    // and requantizing its chunk) and their dequantizations of the gathered
+    // FP8 message collapse into one pass: reduce, requantize, dequantize, and
+    // write the result into every rank's buffer.
+    rx::DrrArgs d = {};
+    for (int j = 0; j < nsrc; ++j) {
+        d.codes[j] = codes[j];
+        d.scales[j] = scales[j];
+        d.out_hps[j] = bufs[j];
+    }
+    d.lo = 0;
+    d.hi = count;
+    d.block = block;
+    d.hp_bf16 = dt;
+    r = launched(rx::launch_drr(d, nsrc, fmt, true, stream));
+    if (r != RX_OK)
+        return r;
+    return RX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -124,6 +292,7 @@ const char* rx_status_string(rx_status_t s)
     case RX_ERR_DTYPE: return "RX_ERR_DTYPE: dtype not supported by this operation";
     case RX_ERR_ALIGN: return "RX_ERR_ALIGN: buffer misaligned (16 B data, 4 B scales)";
     case RX_ERR_HIP: return "RX_ERR_HIP: the HIP runtime rejected the launch";
+    case RX_ERR_SCRATCH: return "RX_ERR_SCRATCH: the call needs more than the library's scratch";
     }
     return "unknown rx_status_t";
 }
@@ -369,104 +538,17 @@ rx_status_t rx_allreduce_local(void* const* bufs, int nsrc, size_t count,
                                rx_dtype_t fp8_dtype, int block, void* workspace,
                                size_t workspace_bytes, hipStream_t stream)
 {
-    if (!bufs)
-        return RX_ERR_NULL;
-    if (nsrc < 1 || nsrc > RX_MAX_SRC || count > kMaxCount || algo < RX_ALGO_AUTO ||
-        algo > RX_ALGO_LOWPREC)
-        return RX_ERR_ARG;
-    if (!hp_type(dtype))
-        return RX_ERR_DTYPE;
-    rx_status_t st = check_ptrs(reinterpret_cast<const void* const*>(bufs), nsrc, true);
-    if (st != RX_OK)
-        return st;
-    const size_t esz = dtype == RX_BF16 ? 2 : 4;
-    if (algo == RX_ALGO_AUTO) {
-        const char* en = getenv("RX_LOW_PRECISION_ENABLE");
-        const bool lp = en && en[0] == '1' && en[1] == '\0' && count * esz >= ((size_t)16 << 20);
-        algo = lp ? RX_ALGO_LOWPREC : RX_ALGO_FLAT;
-    }
-    size_t need = 0;
-    if (algo == RX_ALGO_LOWPREC) {
-        if (!valid_block(block))
-            return RX_ERR_ARG;
-        if ((count / 256 + 1) * (size_t)nsrc >= ((size_t)1 << 32))   // the quantizer's limit
-            return RX_ERR_ARG;
-        if (!fp8_type(fp8_dtype))
-            return RX_ERR_DTYPE;
-        if (!workspace)
-            return RX_ERR_NULL;
-        if (((uintptr_t)workspace & 255u) != 0)
-            return RX_ERR_ALIGN;
-        need = rx_allreduce_local_workspace(nsrc, count, block);
-        if (workspace_bytes < need)
-            return RX_ERR_ARG;
-    }
-    if (count == 0)
-        return RX_OK;
-    const int dt = dtype == RX_BF16 ? 1 : 0;
+    return allreduce_local_impl(bufs, nsrc, count, dtype, algo, fp8_dtype, block, workspace,
+                                workspace_bytes, false, stream);
+}
 
-    if (algo == RX_ALGO_FLAT || algo == RX_ALGO_TREE) {
-        rx::TreeArgs a = {};
-        for (int j = 0; j < nsrc; ++j) {
-            a.src[j] = bufs[j];
-            a.dst[j] = bufs[j];
-        }
-        if (algo == RX_ALGO_FLAT) {
-            a.lo = 0;
-            a.hi = count;
-            return launched(rx::launch_tree(a, nsrc, dt, stream));
-        }
-        for (int k = 0; k < nsrc; ++k) {
-            rx_tree_chunk(count, nsrc, dtype, k, &a.lo, &a.hi);
-            if (a.lo >= a.hi)
-                continue;
-            rx_status_t r = launched(rx::launch_tree(a, nsrc, dt, stream));
-            if (r != RX_OK)
-                return r;
-        }
-        return RX_OK;
-    }
-
-    // low precision: codes and scales of every rank in the workspace
-    const size_t nb = (count + (size_t)block - 1) / (size_t)block;
-    const int fmt = fp8_dtype == RX_FP8_E5M2 ? 1 : 0;
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    void* codes[RX_MAX_SRC];
-    float* scales[RX_MAX_SRC];
-    for (int j = 0; j < nsrc; ++j) {
-        codes[j] = ws + (size_t)j * round256(count);
-        scales[j] = reinterpret_cast<float*>(ws + (size_t)nsrc * round256(count) +
-                                             (size_t)j * round256(nb * sizeof(float)));
-    }
-    rx::QuantArgs q = {};
-    for (int j = 0; j < nsrc; ++j) {
-        q.src[j] = bufs[j];
-        q.codes[j] = codes[j];
-        q.scales[j] = scales[j];
-    }
-    q.count = count;
-    q.nsrc = nsrc;
-    rx_status_t r = launched(rx::launch_quant(q, dt, fmt, block, stream));
-    if (r != RX_OK)
-        return r;
-    // On one device the nsrc ranks' low-precision tree steps (each reducing
-    // and requantizing its chunk) and their dequantizations of the gathered
-    // FP8 message collapse into one pass: reduce, requantize, dequantize, and
-    // write the result into every rank's buffer.
-    rx::DrrArgs d = {};
-    for (int j = 0; j < nsrc; ++j) {
-        d.codes[j] = codes[j];
-        d.scales[j] = scales[j];
-        d.out_hps[j] = bufs[j];
-    }
-    d.lo = 0;
-    d.hi = count;
-    d.block = block;
-    d.hp_bf16 = dt;
-    r = launched(rx::launch_drr(d, nsrc, fmt, true, stream));
-    if (r != RX_OK)
-        return r;
-    return RX_OK;
+rx_status_t rx_allreduce_local_noalloc(void* const* bufs, int nsrc, size_t count,
+                                       rx_dtype_t dtype, rx_algo_t algo,
+                                       rx_dtype_t fp8_dtype, int block,
+                                       hipStream_t stream)
+{
+    return allreduce_local_impl(bufs, nsrc, count, dtype, algo, fp8_dtype, block, nullptr,
+                                RX_NOALLOC_SCRATCH_BYTES, true, stream);
 }
 
 }  // extern "C"

@@ -14,7 +14,9 @@
  *     caller may free them on return. Every pointer IN them is a device
  *     pointer.
  *   - The caller owns all device memory. The library allocates nothing and
- *     keeps no state beyond a per-device cache of the compute-unit count.
+ *     keeps no state beyond a per-device cache of the compute-unit count,
+ *     and (rx_allreduce_local_noalloc only) one static scratch array per
+ *     device with its address.
  *   - Calls are stream-ordered and asynchronous: they return after enqueueing
  *     on `stream` (0 = the null stream). Synchronize the stream to observe
  *     results.
@@ -58,7 +60,9 @@ typedef enum {
     RX_ERR_ARG = 2,   /* nsrc, rank, block or mode/pointer combination      */
     RX_ERR_DTYPE = 3, /* dtype not supported by this operation              */
     RX_ERR_ALIGN = 4, /* data buffer not 16-B aligned / scales not 4-B      */
-    RX_ERR_HIP = 5    /* the HIP runtime reported an error at launch        */
+    RX_ERR_HIP = 5,   /* the HIP runtime reported an error at launch        */
+    RX_ERR_SCRATCH = 6 /* rx_allreduce_local_noalloc: the call needs more
+                          than RX_NOALLOC_SCRATCH_BYTES of scratch          */
 } rx_status_t;
 
 typedef enum {
@@ -255,6 +259,39 @@ rx_status_t rx_allreduce_local(void* const* bufs, int nsrc, size_t count,
                                rx_dtype_t dtype, rx_algo_t algo,
                                rx_dtype_t fp8_dtype, int block, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * rx_allreduce_local for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, algorithms and results as rx_allreduce_local,
+ * without the workspace: the low-precision algorithm keeps every rank's FP8
+ * codes and scales in a scratch array inside the library instead.
+ *
+ *   - The scratch holds RX_NOALLOC_SCRATCH_BYTES per device, allocated when
+ *     the library's device code is loaded on that device and held until the
+ *     process ends. A low-precision call whose
+ *     rx_allreduce_local_workspace(nsrc, count, block) exceeds it returns
+ *     RX_ERR_SCRATCH and enqueues nothing (e.g. 8 ranks of up to 8,134,400
+ *     elements fit with blocks of 128: 31 MiB of FP32 per rank; 8 ranks of
+ *     16 MiB BF16 do not). FLAT and TREE use no scratch and have no limit.
+ *   - This entry point calls no hipMalloc, hipFree or other allocating
+ *     routine. On its first call on a device (any algorithm, also with
+ *     count == 0) it looks up that device's scratch address once
+ *     (hipGetSymbolAddress, RX_ERR_HIP if that fails); make that first call
+ *     outside a stream capture. Every later call uses the kept address.
+ *   - Nothing in the scratch has to start at zero: the quantizer writes
+ *     every code and scale the second pass reads. Its contents after a call
+ *     are unspecified.
+ *   - Every call on one device shares that device's scratch: calls that
+ *     overlap in time on one device (different streams or host threads
+ *     without ordering between them) race on it and give undefined results.
+ *     Calls ordered on one stream are safe.
+ */
+#define RX_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+rx_status_t rx_allreduce_local_noalloc(void* const* bufs, int nsrc, size_t count,
+                                       rx_dtype_t dtype, rx_algo_t algo,
+                                       rx_dtype_t fp8_dtype, int block,
+                                       hipStream_t stream);
 
 /* Workspace bytes rx_allreduce_local needs for the low-precision algorithm
  * (codes and scales of every rank, each array 256-B aligned); 0 on invalid

@@ -12,7 +12,7 @@ import pytest
 import allreduce_reduction_rx_amd as rx
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, NULL, ARG, DTYPE, ALIGN = 0, 1, 2, 3, 4
+OK, NULL, ARG, DTYPE, ALIGN, HIP, SCRATCH = 0, 1, 2, 3, 4, 5, 6
 FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
 
 
@@ -44,7 +44,7 @@ def ptrs(*vals):
 
 
 def test_status_strings():
-    for s in range(6):
+    for s in range(7):
         assert rx.rx_status_string(s).startswith("RX_")
 
 
@@ -180,6 +180,34 @@ def test_allreduce_local_validation():
     # nothing to do: no launch
     assert f(bufs, 2, 0, F32, LP, E4, 128, ws, need, None) == OK
     assert f(bufs, 2, 0, F32, AUTO, E4, 128, None, 0, None) == OK
+
+
+def test_allreduce_local_noalloc_validation():
+    """The allocation-free variant validates like rx_allreduce_local and
+    rejects a low-precision call whose codes and scales exceed the library's
+    scratch with RX_ERR_SCRATCH, before any HIP call (so before the scratch
+    address lookup, which needs a device)."""
+    L = rx.lib()
+    f = L.rx_allreduce_local_noalloc
+    bufs = ptrs(*[FAKE + (1 << 26) * j for j in range(8)])
+    F32, BF, E4, E5 = rx.RX_FP32, rx.RX_BF16, rx.RX_FP8_E4M3, rx.RX_FP8_E5M2
+    FLAT, LP = rx.RX_ALGO_FLAT, rx.RX_ALGO_LOWPREC
+    cap = rx.RX_NOALLOC_SCRATCH_BYTES
+    assert cap == 64 << 20
+    assert f(None, 8, 1000, F32, FLAT, E4, 128, None) == NULL
+    assert f(bufs, 0, 1000, F32, FLAT, E4, 128, None) == ARG
+    assert f(bufs, 8, 1000, F32, 9, E4, 128, None) == ARG
+    assert f(bufs, 8, 1000, E5, FLAT, E4, 128, None) == DTYPE
+    assert f(ptrs(FAKE, FAKE + 2), 2, 1000, F32, FLAT, E4, 128, None) == ALIGN
+    assert f(bufs, 8, 1000, F32, LP, E4, 96, None) == ARG
+    assert f(bufs, 8, 1000, F32, LP, BF, 128, None) == DTYPE
+    # largest low-precision count that fits, and the next one
+    fit = 8_134_400
+    assert rx.rx_allreduce_local_workspace(8, fit, 128) <= cap
+    assert rx.rx_allreduce_local_workspace(8, fit + 1, 128) > cap
+    assert f(bufs, 8, fit + 1, F32, LP, E4, 128, None) == SCRATCH
+    assert f(bufs, 8, 8 << 20, BF, LP, E5, 256, None) == SCRATCH   # 8 x 16 MiB BF16
+    assert "scratch" in rx.rx_status_string(SCRATCH)
 
 
 def test_one_hip_runtime_per_process():
