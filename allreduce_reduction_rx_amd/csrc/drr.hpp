@@ -183,6 +183,98 @@ __device__ __forceinline__ void store_hp(void* out, bool bf16, size_t c, size_t 
 // per rank (the low-precision tree step's push); kDrrRequantAll -> only the
 // dequantized result, into N buffers out_hps[j] (every rank's final values
 // in a one-device allreduce).
+// One wave tile of k_drr. WHOLE: every chunk of the tile lies inside the
+// range (all tiles but a ragged last one); that instance has no per-lane
+// bounds branches around its loads and stores.
+template <int F, int N, bool REQUANT, int CPC, int U, int OUT, bool WHOLE>
+__device__ __forceinline__ void drr_tile(const DrrArgs& a, uint32_t t, int lane, size_t c0,
+                                         size_t count, int bshift, int lpb)
+{
+    size_t c[U], e[U], b[U];
+    bool whole[U], valid[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        c[u] = c0 + ((size_t)t * U + u) * kWave + lane;  // this lane's chunk u
+        e[u] = c[u] * CPC;
+        whole[u] = WHOLE || e[u] + CPC <= count;
+        valid[u] = WHOLE || e[u] < count;
+        b[u] = e[u] >> bshift;
+    }
+
+    Chunk<CPC> x[N][U];
+    float sc[N][U];
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+        const uint8_t* cp = static_cast<const uint8_t*>(a.codes[r]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            x[r][u] = load_chunk<CPC>(cp, c[u], e[u], count, whole[u]);
+            sc[r][u] = valid[u] ? a.scales[r][b[u]] : 0.0f;
+        }
+    }
+
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float S[CPC];
+        dequant<F, CPC>(x[0][u].w, sc[0][u], S);
+#pragma unroll
+        for (int r = 1; r < N; ++r) {
+            float d[CPC];
+            dequant<F, CPC>(x[r][u].w, sc[r][u], d);
+#pragma unroll
+            for (int k = 0; k < CPC; ++k)
+                S[k] = S[k] + d[k];
+        }
+
+        if constexpr (!REQUANT) {
+            store_hp<CPC>(a.out_hp, a.hp_bf16 != 0, c[u], e[u], count, whole[u], S);
+            continue;
+        }
+
+        // Requantize the FP32 sum with the same block size and format.
+        float m = __builtin_fabsf(S[0]);
+#pragma unroll
+        for (int k = 1; k < CPC; ++k)
+            m = __builtin_fmaxf(m, __builtin_fabsf(S[k]));
+        const float A = bits_f32(group_max_rt(__builtin_bit_cast(uint32_t, m), lpb));
+        float s2, r2;
+        block_scale<F>(A, s2, r2);
+        uint32_t q[CPC / 4];
+#pragma unroll
+        for (int p = 0; p < CPC / 4; ++p)
+            q[p] = f32x4_to_fp8<F>(clamp_fmax<F>(S[4 * p + 0] * r2), clamp_fmax<F>(S[4 * p + 1] * r2),
+                                   clamp_fmax<F>(S[4 * p + 2] * r2), clamp_fmax<F>(S[4 * p + 3] * r2));
+        if constexpr (OUT == kDrrRequantPush) {
+            // push the chunk to every destination (one per rank: nout == N,
+            // so the loop unrolls and the pointers load once)
+#pragma unroll
+            for (int j = 0; j < N; ++j)
+                store_codes<CPC>(static_cast<uint8_t*>(a.out_codes[j]), c[u], e[u], count, whole[u], q);
+            if (valid[u] && (lane % lpb) == 0) {
+#pragma unroll
+                for (int j = 0; j < N; ++j)
+                    store_scale<CPC == 4 && U == 1>(a.out_scales[j] + b[u], s2);
+            }
+        } else if constexpr (OUT == kDrrRequant) {
+            store_codes<CPC>(static_cast<uint8_t*>(a.out_codes[0]), c[u], e[u], count, whole[u], q);
+            if (valid[u] && (lane % lpb) == 0)
+                store_scale<CPC == 4 && U == 1>(a.out_scales[0] + b[u], s2);
+        }
+
+        if constexpr (OUT == kDrrRequantAll) {
+            float h[CPC];
+            dequant<F, CPC>(q, s2, h);
+#pragma unroll
+            for (int j = 0; j < N; ++j)
+                store_hp<CPC>(a.out_hps[j], a.hp_bf16 != 0, c[u], e[u], count, whole[u], h);
+        } else if (a.out_hp) {
+            float h[CPC];
+            dequant<F, CPC>(q, s2, h);
+            store_hp<CPC>(a.out_hp, a.hp_bf16 != 0, c[u], e[u], count, whole[u], h);
+        }
+    }
+}
+
 template <int F, int N, bool REQUANT, int CPC, int U, int OUT>
 __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
 {
@@ -200,89 +292,10 @@ __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
     const int bshift = __builtin_ctz((unsigned)a.block);
 
     for (uint32_t t = wave; t < ntiles; t += nwaves) {
-        size_t c[U], e[U], b[U];
-        bool whole[U], valid[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            c[u] = c0 + ((size_t)t * U + u) * kWave + lane;  // this lane's chunk u
-            e[u] = c[u] * CPC;
-            whole[u] = e[u] + CPC <= count;
-            valid[u] = e[u] < count;
-            b[u] = e[u] >> bshift;
-        }
-
-        Chunk<CPC> x[N][U];
-        float sc[N][U];
-#pragma unroll
-        for (int r = 0; r < N; ++r) {
-            const uint8_t* cp = static_cast<const uint8_t*>(a.codes[r]);
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                x[r][u] = load_chunk<CPC>(cp, c[u], e[u], count, whole[u]);
-                sc[r][u] = valid[u] ? a.scales[r][b[u]] : 0.0f;
-            }
-        }
-
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float S[CPC];
-            dequant<F, CPC>(x[0][u].w, sc[0][u], S);
-#pragma unroll
-            for (int r = 1; r < N; ++r) {
-                float d[CPC];
-                dequant<F, CPC>(x[r][u].w, sc[r][u], d);
-#pragma unroll
-                for (int k = 0; k < CPC; ++k)
-                    S[k] = S[k] + d[k];
-            }
-
-            if constexpr (!REQUANT) {
-                store_hp<CPC>(a.out_hp, a.hp_bf16 != 0, c[u], e[u], count, whole[u], S);
-                continue;
-            }
-
-            // Requantize the FP32 sum with the same block size and format.
-            float m = __builtin_fabsf(S[0]);
-#pragma unroll
-            for (int k = 1; k < CPC; ++k)
-                m = __builtin_fmaxf(m, __builtin_fabsf(S[k]));
-            const float A = bits_f32(group_max_rt(__builtin_bit_cast(uint32_t, m), lpb));
-            float s2, r2;
-            block_scale<F>(A, s2, r2);
-            uint32_t q[CPC / 4];
-#pragma unroll
-            for (int p = 0; p < CPC / 4; ++p)
-                q[p] = f32x4_to_fp8<F>(clamp_fmax<F>(S[4 * p + 0] * r2), clamp_fmax<F>(S[4 * p + 1] * r2),
-                                       clamp_fmax<F>(S[4 * p + 2] * r2), clamp_fmax<F>(S[4 * p + 3] * r2));
-            if constexpr (OUT == kDrrRequantPush) {
-                // push the chunk to every destination (one per rank: nout == N,
-                // so the loop unrolls and the pointers load once)
-#pragma unroll
-                for (int j = 0; j < N; ++j)
-                    store_codes<CPC>(static_cast<uint8_t*>(a.out_codes[j]), c[u], e[u], count, whole[u], q);
-                if (valid[u] && (lane % lpb) == 0) {
-#pragma unroll
-                    for (int j = 0; j < N; ++j)
-                        store_scale<CPC == 4 && U == 1>(a.out_scales[j] + b[u], s2);
-                }
-            } else if constexpr (OUT == kDrrRequant) {
-                store_codes<CPC>(static_cast<uint8_t*>(a.out_codes[0]), c[u], e[u], count, whole[u], q);
-                if (valid[u] && (lane % lpb) == 0)
-                    store_scale<CPC == 4 && U == 1>(a.out_scales[0] + b[u], s2);
-            }
-
-            if constexpr (OUT == kDrrRequantAll) {
-                float h[CPC];
-                dequant<F, CPC>(q, s2, h);
-#pragma unroll
-                for (int j = 0; j < N; ++j)
-                    store_hp<CPC>(a.out_hps[j], a.hp_bf16 != 0, c[u], e[u], count, whole[u], h);
-            } else if (a.out_hp) {
-                float h[CPC];
-                dequant<F, CPC>(q, s2, h);
-                store_hp<CPC>(a.out_hp, a.hp_bf16 != 0, c[u], e[u], count, whole[u], h);
-            }
-        }
+        if (a.lo + ((size_t)t + 1) * kTile <= count)
+            drr_tile<F, N, REQUANT, CPC, U, OUT, true>(a, t, lane, c0, count, bshift, lpb);
+        else
+            drr_tile<F, N, REQUANT, CPC, U, OUT, false>(a, t, lane, c0, count, bshift, lpb);
     }
 }
 
