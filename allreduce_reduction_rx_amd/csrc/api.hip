@@ -192,7 +192,9 @@ rx_status_t allreduce_local_impl(void* const* bufs, int nsrc, size_t count, rx_d
             return RX_ERR_DTYPE;
         need = rx_allreduce_local_workspace(nsrc, count, block);
         if (use_scratch) {
-            if (need > workspace_bytes)
+            // only the two-pass form (blocks beyond the one-pass limit)
+            // keeps codes and scales in the scratch
+            if (!rx::allreduce_lp_fits(dtype == RX_BF16 ? 1 : 0, block) && need > workspace_bytes)
                 return scratch_too_small(need);
         } else {
             if (!workspace)
@@ -237,9 +239,20 @@ rx_status_t allreduce_local_impl(void* const* bufs, int nsrc, size_t count, rx_d
         return RX_OK;
     }
 
-    // low precision: codes and scales of every rank in the workspace
-    const size_t nb = (count + (size_t)block - 1) / (size_t)block;
     const int fmt = fp8_dtype == RX_FP8_E5M2 ? 1 : 0;
+    if (rx::allreduce_lp_fits(dt, block)) {
+        // a block lies in one wave's lanes: every rank's quantization, the
+        // reduction, the requantization and every rank's dequantization in
+        // one pass, the codes kept in registers (the workspace is not used)
+        rx::AllreduceLpArgs l = {};
+        for (int j = 0; j < nsrc; ++j)
+            l.buf[j] = bufs[j];
+        l.count = count;
+        return launched(rx::launch_allreduce_lp(l, nsrc, dt, fmt, block, stream));
+    }
+
+    // larger blocks: codes and scales of every rank in the workspace
+    const size_t nb = (count + (size_t)block - 1) / (size_t)block;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     void* codes[RX_MAX_SRC];
     float* scales[RX_MAX_SRC];

@@ -46,6 +46,12 @@ struct DrrArgs {
     int xcd_ranges;              // 1: each XCD takes a contiguous range of tiles
 };
 
+struct AllreduceLpArgs {
+    void* buf[kMaxSrc];          // the ranks' buffers, read and overwritten
+    size_t count;                // elements per buffer
+    int xcd_ranges;              // 1: each XCD takes a contiguous range of tiles
+};
+
 // Launch geometry helper: number of compute units of the current device
 // (cached per device on first use).
 int device_cu_count();
@@ -83,5 +89,10 @@ hipError_t launch_reduce_flat(const FlatArgs& a, int nsrc, int dtype, hipStream_
 hipError_t launch_tree(const TreeArgs& a, int nsrc, int dtype, hipStream_t s);
 hipError_t launch_quant(const QuantArgs& a, int src_dtype, int fmt, int block, hipStream_t s);
 hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStream_t s);
+// One-pass low-precision allreduce of the ranks' buffers (block <= 64
+// 16-byte vectors: allreduce_lp_fits), block 32..512.
+bool allreduce_lp_fits(int dtype, int block);
+hipError_t launch_allreduce_lp(const AllreduceLpArgs& a, int nsrc, int dtype, int fmt, int block,
+                               hipStream_t s);
 
 }  // namespace rx

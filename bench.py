@@ -564,6 +564,23 @@ def cfg_lp(wname, torch, rx, G, timer, ceilings):
         out_hp=qsets2[i % nq2][2]) for i in range(reps)])
     kern["dequant_separate"] = entry(dq_bytes, us, reps, wname, "dequant_separate", target=0.8)
 
+    del qsets2
+    dsets = None
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    # the whole one-device low-precision allreduce, in place (one pass: every
+    # buffer read once and written once), on buffers of zeros so repeated
+    # in-place sums stay finite; no workspace (the one-pass form needs none)
+    ar_bytes = 2 * n * count * e
+    na = nsets_for(n * count * e, torch)
+    ar = [[torch.zeros(count, dtype=tdt, device=dev) for _ in range(n)] for _ in range(na)]
+    reps = auto_reps(ar_bytes)
+    us = timer.us_per_launch([lambda i=i: rx.rx_allreduce_local_noalloc(
+        ar[i % na], rx.RX_ALGO_LOWPREC, fmt, block) for i in range(reps)])
+    kern["allreduce_local_lowprec"] = entry(ar_bytes, us, reps, wname, "allreduce_local_lowprec",
+                                            target=0.8)
+    del ar
+
     if ceilings:
         ratio_kind = {
             "quant_fp8": ("narrow4" if e == 4 else "narrow2"),
@@ -571,6 +588,7 @@ def cfg_lp(wname, torch, rx, G, timer, ceilings):
             "drr_requant": f"reduce{n}",
             hp_name: f"reduce{max(1, round(in_bytes / (out_q + count * e)))}",
             "dequant_separate": "copy",
+            "allreduce_local_lowprec": "copy",
         }
         for name, kind in ratio_kind.items():
             c = ceilings.get(kind)
@@ -579,9 +597,10 @@ def cfg_lp(wname, torch, rx, G, timer, ceilings):
                 kern[name]["frac_of_mixed_ceiling"] = round(kern[name]["GB/s"] / c["GB/s"], 4)
     out = {"workload": describe(w), "input_sha256": hashes,
            "cache": f"cold (quant rotates {nq} set(s) of {q_bytes / 2**30:.2f} GiB, DRR {nd} of "
-                    f"{d_set / 2**30:.2f} GiB, dequant {nq2} of {dq_bytes / 2**30:.2f} GiB)",
+                    f"{d_set / 2**30:.2f} GiB, dequant {nq2} of {dq_bytes / 2**30:.2f} GiB, "
+                    f"allreduce {na} of {n * count * e / 2**30:.2f} GiB)",
            "generate_upload_s": round(gen_s, 1), "kernels": kern}
-    del dsets, qsets2, base, codes0, scales0
+    del base, codes0, scales0
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return out

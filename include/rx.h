@@ -231,12 +231,15 @@ typedef enum {
  *                   FP32 left fold into all of them.
  *   RX_ALGO_TREE    rx_reduce_scatter_chunk_bcast for every rank k in turn
  *                   ("Core feature 1", DDA Tree); same result as FLAT.
- *   RX_ALGO_LOWPREC rx_quant_fp8 of every buffer into the workspace, then
- *                   what every rank's rx_lp_reduce_scatter_chunk_bcast and
- *                   its dequantization of the gathered FP8 message compute
- *                   ("Core feature 2"), which on one device is one pass:
+ *   RX_ALGO_LOWPREC every rank's rx_quant_fp8, then what every rank's
+ *                   rx_lp_reduce_scatter_chunk_bcast and its dequantization
+ *                   of the gathered FP8 message compute ("Core feature 2"):
  *                   every buffer receives dequant(requant(FP32 sum of the
- *                   dequantized inputs)).
+ *                   dequantized inputs)). All of it is block-local, so on one
+ *                   device it runs as one pass that keeps the codes in
+ *                   registers when a block spans at most 64 16-byte vectors
+ *                   (FP32 blocks up to 256, BF16 up to 512); larger blocks
+ *                   quantize into the workspace first, then run one pass.
  *   RX_ALGO_AUTO    RX_ALGO_LOWPREC when the environment variable
  *                   RX_LOW_PRECISION_ENABLE is "1" and a buffer is >= 16 MiB
  *                   (the article's activation switch and threshold),
@@ -248,8 +251,9 @@ typedef enum {
  * fp8_dtype, block: low-precision format and block size (as rx_quant_fp8);
  *                   checked only when the low-precision algorithm runs.
  * workspace       : device memory of at least rx_allreduce_local_workspace()
- *                   bytes, 256-B aligned; needed only by the low-precision
- *                   algorithm (NULL otherwise); its contents on return are
+ *                   bytes, 256-B aligned; required by the low-precision
+ *                   algorithm (NULL otherwise), written only for blocks
+ *                   beyond the one-pass limit; its contents on return are
  *                   unspecified.
  * Errors: RX_ERR_NULL when the low-precision algorithm runs without a
  * workspace, RX_ERR_ARG when it is too small, as well as the errors of the
@@ -264,16 +268,19 @@ rx_status_t rx_allreduce_local(void* const* bufs, int nsrc, size_t count,
  * rx_allreduce_local for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc. Same arguments, algorithms and results as rx_allreduce_local,
- * without the workspace: the low-precision algorithm keeps every rank's FP8
- * codes and scales in a scratch array inside the library instead.
+ * without the workspace: where the low-precision algorithm needs one (blocks
+ * beyond its one-pass limit: FP32 blocks of 512 or 1024, BF16 blocks of
+ * 1024), it keeps every rank's FP8 codes and scales in a scratch array
+ * inside the library instead.
  *
  *   - The scratch holds RX_NOALLOC_SCRATCH_BYTES per device, allocated when
  *     the library's device code is loaded on that device and held until the
- *     process ends. A low-precision call whose
+ *     process ends. A two-pass low-precision call whose
  *     rx_allreduce_local_workspace(nsrc, count, block) exceeds it returns
- *     RX_ERR_SCRATCH and enqueues nothing (e.g. 8 ranks of up to 8,134,400
- *     elements fit with blocks of 128: 31 MiB of FP32 per rank; 8 ranks of
- *     16 MiB BF16 do not). FLAT and TREE use no scratch and have no limit.
+ *     RX_ERR_SCRATCH and enqueues nothing (e.g. 8 ranks of up to 8,355,840
+ *     elements fit with blocks of 1024: 31 MiB of FP32 per rank). FLAT,
+ *     TREE and the one-pass low-precision form use no scratch and have no
+ *     such limit.
  *   - This entry point calls no hipMalloc, hipFree or other allocating
  *     routine. On its first call on a device (any algorithm, also with
  *     count == 0) it looks up that device's scratch address once

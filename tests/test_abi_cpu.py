@@ -201,12 +201,14 @@ def test_allreduce_local_noalloc_validation():
     assert f(ptrs(FAKE, FAKE + 2), 2, 1000, F32, FLAT, E4, 128, None) == ALIGN
     assert f(bufs, 8, 1000, F32, LP, E4, 96, None) == ARG
     assert f(bufs, 8, 1000, F32, LP, BF, 128, None) == DTYPE
-    # largest low-precision count that fits, and the next one
-    fit = 8_134_400
-    assert rx.rx_allreduce_local_workspace(8, fit, 128) <= cap
-    assert rx.rx_allreduce_local_workspace(8, fit + 1, 128) > cap
-    assert f(bufs, 8, fit + 1, F32, LP, E4, 128, None) == SCRATCH
-    assert f(bufs, 8, 8 << 20, BF, LP, E5, 256, None) == SCRATCH   # 8 x 16 MiB BF16
+    # largest two-pass low-precision count that fits (blocks of 1024 are
+    # beyond the one-pass limit), and the next one
+    fit = 8_355_840
+    assert rx.rx_allreduce_local_workspace(8, fit, 1024) <= cap
+    assert rx.rx_allreduce_local_workspace(8, fit + 1, 1024) > cap
+    assert f(bufs, 8, fit + 1, F32, LP, E4, 1024, None) == SCRATCH
+    assert f(bufs, 8, fit + 1, F32, LP, E4, 512, None) == SCRATCH
+    assert f(bufs, 8, 8 << 20, BF, LP, E5, 1024, None) == SCRATCH   # 8 x 16 MiB BF16
     assert "scratch" in rx.rx_status_string(SCRATCH)
 
 

@@ -801,6 +801,33 @@ def test_allreduce_local(dtype, algo):
             assert bits_equal(got, ref[j]), f"count={count} rank={j}: " + first_mismatch(got, ref[j])
 
 
+@pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
+@pytest.mark.parametrize("fmt", [O.E4M3, O.E5M2])
+def test_allreduce_local_lowprec_every_block(dtype, fmt):
+    """The low-precision allreduce for every block size: blocks of at most 64
+    16-byte vectors run the one-pass kernel (codes in registers), larger ones
+    quantize into the workspace first; ragged counts, 1..16 ranks, and a rank
+    of zeros (degenerate blocks, s = r = 1)."""
+    for block in (32, 64, 128, 256, 512, 1024):
+        for n, count in ((8, 70001), (3, 4096 + 17), (16, 1000), (1, 513)):
+            log(f"allreduce_local lowprec dtype={dtype} fmt={fmt} block={block} n={n} count={count}")
+            srcs = [G.fill(count, dtype, G.NORMAL_OUTLIER, seed=9100 + block + n, rank=r)
+                    for r in range(n)]
+            if n == 3:
+                srcs[1][:] = 0
+            ts = [to_gpu(x) for x in srcs]
+            ws = torch.empty(rx.rx_allreduce_local_workspace(n, count, block), dtype=torch.uint8,
+                             device=DEV)
+            rx.rx_allreduce_local(ts, rx.RX_ALGO_LOWPREC, FMTS[fmt], block, ws)
+            sync()
+            ref = [x.copy() for x in srcs]
+            O.allreduce_local(ref, dtype, O.ALGO_LOWPREC, fmt, block)
+            for j in range(n):
+                got = to_host(ts[j])
+                assert bits_equal(got, ref[j]), (f"block={block} n={n} rank={j}: "
+                                                 + first_mismatch(got, ref[j]))
+
+
 @pytest.mark.parametrize("n", [1, 3, 16])
 def test_allreduce_local_rank_counts(n):
     """Every algorithm with other rank counts, ragged length."""

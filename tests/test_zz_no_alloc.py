@@ -2,7 +2,9 @@
 rx_allreduce_local, for callers that cannot allocate) against
 rx_allreduce_local with a caller workspace, through the C ABI: bit for bit,
 for every algorithm, on two calls in a row, the second with a smaller input
-(the scratch keeps the first call's contents)."""
+(the scratch keeps the first call's contents). Blocks of 1024 take the
+two-pass low-precision form, whose codes and scales live in the scratch;
+blocks of 128 / 256 the one-pass form."""
 import numpy as np
 import pytest
 import torch
@@ -28,7 +30,8 @@ def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
 
-@pytest.mark.parametrize("dtype,fmt,block", [(G.FP32, "e4m3", 128), (G.BF16, "e5m2", 256)])
+@pytest.mark.parametrize("dtype,fmt,block", [(G.FP32, "e4m3", 1024), (G.BF16, "e5m2", 1024),
+                                             (G.FP32, "e4m3", 128), (G.BF16, "e5m2", 256)])
 @pytest.mark.parametrize("algo", [rx.RX_ALGO_LOWPREC, rx.RX_ALGO_FLAT, rx.RX_ALGO_TREE])
 def test_noalloc_matches_workspace_variant(dtype, fmt, block, algo):
     n = 8
@@ -49,10 +52,10 @@ def test_noalloc_matches_workspace_variant(dtype, fmt, block, algo):
 
 
 def test_noalloc_oversize_rejected_and_nothing_written():
-    n, count = 8, 8_134_401          # one element beyond the scratch
+    n, count = 8, 8_355_841          # one element beyond the scratch (blocks of 1024)
     bufs = [torch.full((count,), 1.5, dtype=torch.float32, device=DEV) for _ in range(n)]
     with pytest.raises(rx.RxError) as e:
-        rx.rx_allreduce_local_noalloc(bufs, rx.RX_ALGO_LOWPREC, "e4m3", 128)
+        rx.rx_allreduce_local_noalloc(bufs, rx.RX_ALGO_LOWPREC, "e4m3", 1024)
     assert e.value.status == rx.RX_ERR_SCRATCH
     torch.cuda.synchronize()
     assert all(bool((t == 1.5).all()) for t in bufs)
