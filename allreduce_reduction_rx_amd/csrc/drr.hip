@@ -63,6 +63,20 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     // pushes to N destinations 3-8% and the FP32-output layout 2% faster;
     // no gain for the other large layouts, which keep the plain order.
     arg.xcd_ranges = (small || medium || r == kDrrRequantPush || (cpc == 4 && u == 4)) ? 1 : 0;
+    if (small && blk.x == (unsigned)kWave) {
+        // Decode-size launches (one tile per 64-thread workgroup): each XCD
+        // takes a contiguous range of tiles that covers whole 128-byte lines
+        // of block scales (32 blocks), so that no line of scales is written
+        // in part by one XCD and in part by another. 8 x 32K-code chunks
+        // pushed to 8 destinations (E5M2/256, 128 tiles: 4 XCDs x 32):
+        // 2.64 -> 2.48 us, FETCH_SIZE 170 -> 157 KiB.
+        const size_t tiles_per_line = (size_t)32 * (size_t)a.block / tile > 0
+                                      ? (size_t)32 * (size_t)a.block / tile : 1;
+        const size_t lines = (tiles + tiles_per_line - 1) / tiles_per_line;
+        const size_t range = (lines + kXcds - 1) / kXcds * tiles_per_line;
+        arg.xcd_ranges = (int)range;
+        grid = dim3((unsigned)(kXcds * range));
+    }
     void* params[] = {&arg};
     const DrrFn fn = cpc == 4 ? (u == 4 ? drr_fns_4x4().fn[fmt][r][nsrc - 1] : drr_fns_4x1().fn[fmt][r][nsrc - 1])
                    : cpc == 8 ? drr_fns_8x2().fn[fmt][r][nsrc - 1] : drr_fns_16x1().fn[fmt][r][nsrc - 1];

@@ -281,17 +281,27 @@ __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
     const int lane = lane_id();
     const uint32_t wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t waves_per_wg = blockDim.x / kWave;
-    const uint32_t wg = a.xcd_ranges ? xcd_contiguous(blockIdx.x, gridDim.x) : blockIdx.x;
-    const uint32_t wave = wg * waves_per_wg + wave_in_wg;
-    const uint32_t nwaves = gridDim.x * waves_per_wg;
     const size_t count = a.hi;                                    // end of the range
     constexpr size_t kTile = (size_t)kWave * CPC * U;             // codes per wave tile
     const uint32_t ntiles = (uint32_t)((a.hi - a.lo + kTile - 1) / kTile);
+    uint32_t wave, step;
+    if (a.xcd_ranges > 1) {
+        // one tile per 64-thread workgroup; XCD x takes tiles [x R, x R + R)
+        // (R = xcd_ranges, a whole number of 128-byte lines of block scales,
+        // so no XCD leaves a line of scales partly written); workgroups past
+        // the last tile do nothing
+        wave = (blockIdx.x % kXcds) * (uint32_t)a.xcd_ranges + blockIdx.x / kXcds;
+        step = ntiles;
+    } else {
+        const uint32_t wg = a.xcd_ranges ? xcd_contiguous(blockIdx.x, gridDim.x) : blockIdx.x;
+        wave = wg * waves_per_wg + wave_in_wg;
+        step = gridDim.x * waves_per_wg;
+    }
     const size_t c0 = a.lo / CPC;                                 // lo is a block multiple
     const int lpb = a.block / CPC;                                // lanes per block: <= 64
     const int bshift = __builtin_ctz((unsigned)a.block);
 
-    for (uint32_t t = wave; t < ntiles; t += nwaves) {
+    for (uint32_t t = wave; t < ntiles; t += step) {
         if (a.lo + ((size_t)t + 1) * kTile <= count)
             drr_tile<F, N, REQUANT, CPC, U, OUT, true>(a, t, lane, c0, count, bshift, lpb);
         else

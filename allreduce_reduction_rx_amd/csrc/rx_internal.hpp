@@ -43,7 +43,9 @@ struct DrrArgs {
     int nout;                    // REQUANT: destinations that receive the result
     int block;                   // elements per scale block
     int hp_bf16;                 // out_hp element type: 1 = BF16, 0 = FP32
-    int xcd_ranges;              // 1: each XCD takes a contiguous range of tiles
+    int xcd_ranges;              // 0: plain order; 1: each XCD takes a contiguous
+                                 // range of workgroups; R > 1: one tile per 64-thread
+                                 // workgroup, XCD x takes tiles [x R, x R + R)
 };
 
 struct AllreduceLpArgs {
