@@ -79,7 +79,7 @@ def parse():
                    help="comma list of the per-config measurements to run beside the "
                         "step ('' = none); cfg2 is the decode step workload")
     p.add_argument("--kernel-reps", type=int, default=0,
-                   help="launches per kernel-only timing (0 = auto)")
+                   help="launches per timed measurement, everywhere (0 = auto; for profiler runs)")
     p.add_argument("--warm", action="store_true",
                    help="reuse one batch every step (cache-warm; labelled)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -164,13 +164,34 @@ def cpu_threads():
 class Timer:
     """Back-to-back launches captured in one HIP graph, timed with HIP events
     on the stream the graph replays on (torch's current stream, which is the
-    stream the binding launches on)."""
+    stream the binding launches on).
+
+    With RX_BENCH_PHASE_LOG=<path> in the environment, every timed
+    measurement appends one JSON line {"phase", "t0_ns", "t1_ns"} (host
+    CLOCK_MONOTONIC, the device idle at both ends), so that a profiler's
+    per-dispatch records can be attributed to the measurement they belong
+    to."""
 
     def __init__(self, torch):
         self.torch = torch
         self.stream = torch.cuda.current_stream()
         self.a = torch.cuda.Event(enable_timing=True)
         self.z = torch.cuda.Event(enable_timing=True)
+        path = os.environ.get("RX_BENCH_PHASE_LOG")
+        self.log = open(path, "a") if path else None
+
+    def phase(self, name, run):
+        """run() as the measurement `name` (logged when the log is on)."""
+        if self.log is None:
+            return run()
+        self.torch.cuda.synchronize()
+        t0 = time.clock_gettime_ns(time.CLOCK_MONOTONIC)
+        out = run()
+        self.torch.cuda.synchronize()
+        t1 = time.clock_gettime_ns(time.CLOCK_MONOTONIC)
+        self.log.write(json.dumps({"phase": name, "t0_ns": t0, "t1_ns": t1}) + "\n")
+        self.log.flush()
+        return out
 
     def capture(self, calls):
         g = self.torch.cuda.CUDAGraph()
@@ -189,17 +210,28 @@ class Timer:
         torch.cuda.synchronize()
         return self.a.elapsed_time(self.z) / reps_inner
 
-    def us_per_launch(self, calls):
+    def us_per_launch(self, calls, name=None):
         g = self.capture(calls)
-        g.replay()
-        us = self.timed(g.replay, len(calls)) * 1000.0
+
+        def run():
+            g.replay()
+            return self.timed(g.replay, len(calls)) * 1000.0
+
+        us = self.phase(name, run) if name else run()
         del g
         return us
 
 
+REPS_OVERRIDE = 0   # --kernel-reps: launches per measurement everywhere (0 = auto)
+
+
+def nreps(default):
+    return REPS_OVERRIDE or default
+
+
 def auto_reps(nbytes, lo=8, hi=2000):
     """Enough launches for ~50 ms of HBM traffic at 4 TB/s."""
-    return max(lo, min(hi, int(0.05 / max(1e-9, nbytes / 4e12))))
+    return nreps(max(lo, min(hi, int(0.05 / max(1e-9, nbytes / 4e12)))))
 
 
 def nsets_for(bytes_per_set, torch, cap=1024):
@@ -275,7 +307,12 @@ def step_workload(args, torch, rx, G, timer):
     bytes_k["lp_flat_sum"] = n * (count + 4 * nb) + count * e
     bytes_k["allreduce_local_flat"] = 2 * n * count * e
     bytes_k["allreduce_local_tree"] = 2 * n * count * e
-    bytes_k["allreduce_local_lowprec"] = (n * (count * e + count + 4 * nb)
+    # the low-precision allreduce is one pass (every buffer read and written
+    # once) when a block spans at most 64 16-byte vectors, else a quantize
+    # pass into the workspace and a reduce pass
+    one_pass = lp_block <= (256 if w.dtype == G.FP32 else 512)
+    bytes_k["allreduce_local_lowprec"] = (2 * n * count * e if one_pass else
+                                          n * (count * e + count + 4 * nb)
                                           + n * (count + 4 * nb) + n * count * e)
     per_batch_bytes = (n * count * e + count * e + n * count * e + n * (count + 4 * nb)
                        + count + 4 * nb + count * e + n * (count + 4 * nb))
@@ -349,15 +386,16 @@ def step_workload(args, torch, rx, G, timer):
     if args.warmup:
         g_warm.replay()
     t_wall = time.perf_counter()
-    step_ms = timer.timed(g_steps.replay, args.steps)
+    step_ms = timer.phase(f"{wname}/step", lambda: timer.timed(g_steps.replay, args.steps))
     wall_s = time.perf_counter() - t_wall
     del g_warm, g_steps
 
     # ---- per-kernel timing: back-to-back launches of one kernel ----
     per_kernel = {}
     for name, fn in kernels_timed:
-        reps = args.kernel_reps or auto_reps(bytes_k[name], lo=50)
-        us = timer.us_per_launch([lambda i=i: fn(batches[i % nsets], i) for i in range(reps)])
+        reps = auto_reps(bytes_k[name], lo=50)
+        us = timer.us_per_launch([lambda i=i: fn(batches[i % nsets], i) for i in range(reps)],
+                                 f"{wname}/{name}")
         per_kernel[name] = entry(bytes_k[name], us, reps, wname, name)
 
     # ---- the tree step for each rank on its own ----
@@ -367,7 +405,7 @@ def step_workload(args, torch, rx, G, timer):
         by_rank.append(round(timer.us_per_launch(
             [lambda i=i, k=k: rx.rx_reduce_scatter_chunk_bcast(batches[i % nsets].srcs, k,
                                                                batches[i % nsets].tree_dsts)
-             for i in range(reps)]), 3))
+             for i in range(reps)], f"{wname}/tree_step@rank{k}"), 3))
 
     # ---- the flat reduce over the first k rank buffers, k = 1..N ----
     flat_by_nsrc = []
@@ -376,7 +414,7 @@ def step_workload(args, torch, rx, G, timer):
         flat_by_nsrc.append(round(timer.us_per_launch(
             [lambda i=i, k=k: rx.rx_reduce_flat(batches[i % nsets].srcs[:k],
                                                 batches[i % nsets].flat_out)
-             for i in range(reps)]), 3))
+             for i in range(reps)], f"{wname}/reduce_flat@nsrc{k}"), 3))
 
     # ---- invariant spot check of batch 0: the tree chunk equals the flat
     # result on that chunk ----
@@ -416,7 +454,7 @@ def describe(w):
     return s
 
 
-def cfg_flat_small(wname, torch, rx, G, timer, reps=2000):
+def cfg_flat_small(wname, torch, rx, G, timer):
     """cfg1: the pages' rank-id example and its U[-1,1) companion."""
     import numpy as np
     dev = torch.device("cuda:0")
@@ -425,7 +463,8 @@ def cfg_flat_small(wname, torch, rx, G, timer, reps=2000):
     srcs = upload(host, torch, dev)
     dst = torch.empty(w.count, dtype=torch.float32, device=dev)
     nbytes = (w.nsrc + 1) * w.count * w.elem_bytes
-    us = timer.us_per_launch([lambda: rx.rx_reduce_flat(srcs, dst)] * reps)
+    reps = nreps(2000)
+    us = timer.us_per_launch([lambda: rx.rx_reduce_flat(srcs, dst)] * reps, f"{wname}/reduce_flat")
     rx.rx_reduce_flat(srcs, dst)
     torch.cuda.synchronize()
     d = {"workload": describe(w), "input_sha256": sha256_buffers(host),
@@ -451,13 +490,13 @@ def cfg_tree(torch, rx, G, timer):
         sets.append(([b.clone() for b in base], [torch.empty_like(base[0]) for _ in range(n)]))
     lo, hi = rx.rx_tree_chunk(count, n, w.dtype, 0)
     nbytes = 2 * n * (hi - lo) * e
-    reps = 1000
+    reps = nreps(1000)
     by_rank = []
     for k in range(n):
         by_rank.append(timer.us_per_launch(
             [lambda i=i, k=k: rx.rx_reduce_scatter_chunk_bcast(sets[i % nsets][0], k,
                                                                sets[i % nsets][1])
-             for i in range(reps)]))
+             for i in range(reps)], f"tree/tree_step@rank{k}"))
     med = sorted(by_rank)[n // 2]
     tree = entry(nbytes, med, reps, "tree", "tree_step", target=0.4)
     tree["us_by_rank"] = [round(x, 3) for x in by_rank]
@@ -466,7 +505,7 @@ def cfg_tree(torch, rx, G, timer):
     freps = auto_reps(fbytes, lo=100)
     flat_out = [torch.empty_like(base[0]) for _ in range(nsets)]
     us = timer.us_per_launch([lambda i=i: rx.rx_reduce_flat(sets[i % nsets][0], flat_out[i % nsets])
-                              for i in range(freps)])
+                              for i in range(freps)], "tree/reduce_flat")
     out = {"workload": describe(w) + f", chunk {hi - lo:,}", "input_sha256": hashes,
            "cache": f"cold (rotating {nsets} sets, {nsets * set_bytes / 2**30:.2f} GiB)",
            "kernels": {"tree_step": tree,
@@ -507,14 +546,14 @@ def cfg_lp(wname, torch, rx, G, timer, ceilings):
     reps = auto_reps(q_bytes)
     us = timer.us_per_launch([lambda i=i: rx.rx_quant_fp8(qsets[i % nq][0], fmt, block,
                                                           qsets[i % nq][1], qsets[i % nq][2])
-                              for i in range(reps)])
+                              for i in range(reps)], f"{wname}/quant_fp8")
     kern["quant_fp8"] = entry(q_bytes, us, reps, wname, "quant_fp8", target=0.8)
     # flat reduce of the same message (the full-precision leg)
     f_bytes = (n + 1) * count * e
     flat_out = [torch.empty(count, dtype=tdt, device=dev) for _ in range(nq)]
     reps = auto_reps(f_bytes)
     us = timer.us_per_launch([lambda i=i: rx.rx_reduce_flat(qsets[i % nq][0], flat_out[i % nq])
-                              for i in range(reps)])
+                              for i in range(reps)], f"{wname}/reduce_flat")
     kern["reduce_flat"] = entry(f_bytes, us, reps, wname, "reduce_flat", target=0.8)
     rx.rx_quant_fp8(base, fmt, block, qsets[0][1], qsets[0][2])
     codes0, scales0 = qsets[0][1], qsets[0][2]
@@ -545,7 +584,7 @@ def cfg_lp(wname, torch, rx, G, timer, ceilings):
             [lambda i=i, h=with_hp: rx.rx_dequant_reduce_requant(
                 dsets[i % nd][0], dsets[i % nd][1], fmt, block, rx.RX_DRR_REQUANT,
                 dsets[i % nd][2], dsets[i % nd][3], dsets[i % nd][4] if h else None)
-             for i in range(reps)])
+             for i in range(reps)], f"{wname}/" + ("drr_requant_hp" if with_hp else "drr_requant"))
         kern[name] = entry(nbytes, us, reps, wname,
                            "drr_requant_hp" if with_hp else "drr_requant", target=0.8)
     # separate dequantization of the requantized message (N = 1, SUM), with
@@ -561,7 +600,7 @@ def cfg_lp(wname, torch, rx, G, timer, ceilings):
     reps = auto_reps(dq_bytes)
     us = timer.us_per_launch([lambda i=i: rx.rx_dequant_reduce_requant(
         [qsets2[i % nq2][0]], [qsets2[i % nq2][1]], fmt, block, rx.RX_DRR_SUM,
-        out_hp=qsets2[i % nq2][2]) for i in range(reps)])
+        out_hp=qsets2[i % nq2][2]) for i in range(reps)], f"{wname}/dequant_separate")
     kern["dequant_separate"] = entry(dq_bytes, us, reps, wname, "dequant_separate", target=0.8)
 
     del qsets2
@@ -576,7 +615,8 @@ def cfg_lp(wname, torch, rx, G, timer, ceilings):
     ar = [[torch.zeros(count, dtype=tdt, device=dev) for _ in range(n)] for _ in range(na)]
     reps = auto_reps(ar_bytes)
     us = timer.us_per_launch([lambda i=i: rx.rx_allreduce_local_noalloc(
-        ar[i % na], rx.RX_ALGO_LOWPREC, fmt, block) for i in range(reps)])
+        ar[i % na], rx.RX_ALGO_LOWPREC, fmt, block) for i in range(reps)],
+        f"{wname}/allreduce_local_lowprec")
     kern["allreduce_local_lowprec"] = entry(ar_bytes, us, reps, wname, "allreduce_local_lowprec",
                                             target=0.8)
     del ar
@@ -623,22 +663,24 @@ def stream_ceilings(torch, rx, timer):
     sink = torch.empty(rx.rxtest_stream_sink_bytes(8) // 4, dtype=torch.float32, device="cuda:0")
     out = {}
 
-    def best(run_for, moved, reps=6):
+    def best(kind, run_for, moved, reps=None):
+        reps = nreps(6) if reps is None else reps
         b = None
         for wgs in (1, 2, 4, 8):
             for nt in (False, True):
-                us = timer.us_per_launch([lambda wgs=wgs, nt=nt: run_for(wgs, nt)] * reps)
+                us = timer.us_per_launch([lambda wgs=wgs, nt=nt: run_for(wgs, nt)] * reps,
+                                         f"ceiling/{kind}@wgs{wgs}nt{int(nt)}")
                 gbs = moved / (us * 1e-6) / 1e9
                 if b is None or gbs > b["GB/s"]:
                     b = {"GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
                          "wgs_per_cu": wgs, "nontemporal": nt}
         return b
 
-    out["read"] = best(lambda wgs, nt: rx.rxtest_stream(rx.RXTEST_READ, src, sink, nbytes, wgs, nt),
+    out["read"] = best("read", lambda wgs, nt: rx.rxtest_stream(rx.RXTEST_READ, src, sink, nbytes, wgs, nt),
                        nbytes)
-    out["write"] = best(lambda wgs, nt: rx.rxtest_stream(rx.RXTEST_WRITE, None, dst, nbytes, wgs, nt),
+    out["write"] = best("write", lambda wgs, nt: rx.rxtest_stream(rx.RXTEST_WRITE, None, dst, nbytes, wgs, nt),
                         nbytes)
-    out["copy"] = best(lambda wgs, nt: rx.rxtest_stream(rx.RXTEST_COPY, src, dst, nbytes, wgs, nt),
+    out["copy"] = best("copy", lambda wgs, nt: rx.rxtest_stream(rx.RXTEST_COPY, src, dst, nbytes, wgs, nt),
                        2 * nbytes)
     if not hasattr(rx, "rxtest_stream_mixed"):
         del src, dst, sink
@@ -648,11 +690,11 @@ def stream_ceilings(torch, rx, timer):
     for k in (8, 3, 2):
         per = nbytes // k // 16 * 16
         srcs = [src.view(torch.uint8)[j * per:(j + 1) * per] for j in range(k)]
-        out[f"reduce{k}"] = best(lambda wgs, nt, srcs=srcs, per=per: rx.rxtest_stream_mixed(
+        out[f"reduce{k}"] = best(f"reduce{k}", lambda wgs, nt, srcs=srcs, per=per: rx.rxtest_stream_mixed(
             rx.RXTEST_MIXED_REDUCE, srcs, dst.view(torch.uint8)[:per], per, wgs, nt),
             (k + 1) * per)
     for kind, k in ((rx.RXTEST_MIXED_NARROW2, 2), (rx.RXTEST_MIXED_NARROW4, 4)):
-        out[f"narrow{k}"] = best(lambda wgs, nt, kind=kind, k=k: rx.rxtest_stream_mixed(
+        out[f"narrow{k}"] = best(f"narrow{k}", lambda wgs, nt, kind=kind, k=k: rx.rxtest_stream_mixed(
             kind, [src], dst.view(torch.uint8)[:nbytes // k], nbytes, wgs, nt),
             nbytes + nbytes // k)
     del src, dst, sink
@@ -660,12 +702,13 @@ def stream_ceilings(torch, rx, timer):
     return out
 
 
-def launch_floors(torch, rx, timer, in_bytes, reps=256):
+def launch_floors(torch, rx, timer, in_bytes, reps=None):
     """What a plain streaming kernel costs per back-to-back launch at this
     message size, cold (graph replay, each launch on its own slice of a
     1 GiB rotation): a launch with no memory access, a read of in_bytes, and
     a copy of in_bytes (best of 1/2/4 workgroups per CU, with and without
     nontemporal hints)."""
+    reps = nreps(256) if reps is None else reps
     total = 1 << 30
     slices = total // in_bytes
     src = torch.zeros(total // 4, dtype=torch.float32, device="cuda:0")
@@ -674,7 +717,7 @@ def launch_floors(torch, rx, timer, in_bytes, reps=256):
     per = in_bytes // 4
     out = {"bytes": in_bytes}
     out["empty_us"] = round(timer.us_per_launch(
-        [lambda: rx.rxtest_stream(rx.RXTEST_EMPTY, None, None, 0, 1)] * reps), 3)
+        [lambda: rx.rxtest_stream(rx.RXTEST_EMPTY, None, None, 0, 1)] * reps, "floor/empty"), 3)
     for kind, name in ((rx.RXTEST_READ, "read_us"), (rx.RXTEST_COPY, "copy_us")):
         b = None
         for wgs in (1, 2, 4):
@@ -686,7 +729,7 @@ def launch_floors(torch, rx, timer, in_bytes, reps=256):
                     d_ = sink if kind == rx.RXTEST_READ else dst[k * per:(k + 1) * per]
                     calls.append(lambda s_=s_, d_=d_, wgs=wgs, nt=nt:
                                  rx.rxtest_stream(kind, s_, d_, in_bytes, wgs, nt))
-                us = timer.us_per_launch(calls)
+                us = timer.us_per_launch(calls, f"floor/{name[:-3]}@wgs{wgs}nt{int(nt)}")
                 b = us if b is None else min(b, us)
         out[name] = round(b, 3)
     del src, dst, sink
@@ -694,12 +737,13 @@ def launch_floors(torch, rx, timer, in_bytes, reps=256):
     return out
 
 
-def single_launch_us(torch, rx, fn, batches, stream, reps=200):
+def single_launch_us(torch, rx, fn, batches, stream, reps=None):
     """Median µs of one launch on its own (the GPU-side dispatch included),
     bracketed by its own HIP events. Each launch is queued behind a 512 MiB
     streaming read, so the host has enqueued the events and the launch before
     the GPU reaches them and no host-side call overhead is timed; the read
     also leaves the caches cold. Rotates over the cold batches."""
+    reps = nreps(200) if reps is None else reps
     nbytes = 512 << 20
     busy = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(0.0)
     sink = torch.empty(rx.rxtest_stream_sink_bytes(2) // 4, dtype=torch.float32, device="cuda:0")
@@ -830,7 +874,9 @@ def cpu_baseline(w, host, lp_fmt, lp_block, seconds, step_bytes):
 # ---------------------------------------------------------------------------
 
 def main():
+    global REPS_OVERRIDE
     args = parse()
+    REPS_OVERRIDE = args.kernel_reps
     if args.gpus != 1:
         print(f"bench.py: this benchmark runs on one GPU only (got --gpus {args.gpus}); "
               "the multi-GPU collective is out of scope here", file=sys.stderr)
