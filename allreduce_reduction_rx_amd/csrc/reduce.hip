@@ -1,91 +1,18 @@
-// reduce.hip -- DDA flat local reduce and DDA tree per-rank step (gfx950).
+// reduce.hip -- DDA flat local reduce (gfx950).
 //
 // DDA flat: each rank reads all peers' buffers directly and reduces locally
 // (RCCLX article, code-journey.com, "Core feature 1: Direct Data Access
-// (DDA)", DDA Flat item). DDA tree: reduce-scatter then all-gather with
-// direct access (same section, DDA Tree item); one rank reduces its chunk
-// and pushes it to every destination. Sums are FP32 ("Core feature 2", table
-// row "Compute precision"), folded in source order 0..N-1.
+// (DDA)", DDA Flat item). Sums are FP32 ("Core feature 2", table row
+// "Compute precision"), folded in source order 0..N-1.
 //
-// Both are HBM-bound streams: 16-byte nontemporal loads of every source (all
-// N issued before the first add), FP32 adds, 16-byte nontemporal stores into
-// every destination. N is a template parameter, so the source loop unrolls
-// and the pointer table is read with scalar loads from the kernarg segment.
-#include <array>
-#include <utility>
-
-#include "rx_device.hpp"
-#include "rx_internal.hpp"
+// An HBM-bound stream: 16-byte nontemporal loads of every source (all N
+// issued before the first add), FP32 adds, 16-byte stores. N is a template
+// parameter, so the source loop unrolls and the pointer table is read with
+// scalar loads from the kernarg segment.
+#include "reduce_common.hpp"
 
 namespace rx {
 namespace {
-
-template <int DT> struct Elem;
-template <> struct Elem<0> { static constexpr int kVE = 4; };  // FP32: 4 per 16 B
-template <> struct Elem<1> { static constexpr int kVE = 8; };  // BF16: 8 per 16 B
-
-// Fold vector `v` (16 bytes) of N sources; returns the narrowed 16 bytes.
-// NT: nontemporal source loads (data read once).
-template <int DT, int N, bool NT>
-__device__ __forceinline__ u32x4 fold_vec(const void* const* src, size_t v)
-{
-    u32x4 x[N];
-#pragma unroll
-    for (int r = 0; r < N; ++r)
-        x[r] = NT ? ld16_stream(src[r], v) : ld16(src[r], v);
-    u32x4 out;
-    if constexpr (DT == 0) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float acc = bits_f32(x[0][k]);
-#pragma unroll
-            for (int r = 1; r < N; ++r)
-                acc = acc + bits_f32(x[r][k]);
-            out[k] = __builtin_bit_cast(uint32_t, acc);
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float lo = bf16_lo(x[0][k]);
-            float hi = bf16_hi(x[0][k]);
-#pragma unroll
-            for (int r = 1; r < N; ++r) {
-                lo = lo + bf16_lo(x[r][k]);
-                hi = hi + bf16_hi(x[r][k]);
-            }
-            out[k] = pack_bf16(lo, hi);
-        }
-    }
-    return out;
-}
-
-// One element i (tail of a count that is not a multiple of 16 bytes).
-template <int DT, int N>
-__device__ __forceinline__ float fold_vec_tail(const void* const* src, size_t i)
-{
-    float acc;
-    if constexpr (DT == 0) {
-        acc = static_cast<const float*>(src[0])[i];
-#pragma unroll
-        for (int r = 1; r < N; ++r)
-            acc = acc + static_cast<const float*>(src[r])[i];
-    } else {
-        acc = bits_f32((uint32_t)static_cast<const uint16_t*>(src[0])[i] << 16);
-#pragma unroll
-        for (int r = 1; r < N; ++r)
-            acc = acc + bits_f32((uint32_t)static_cast<const uint16_t*>(src[r])[i] << 16);
-    }
-    return acc;
-}
-
-template <int DT>
-__device__ __forceinline__ void store_elem(void* dst, size_t i, float v)
-{
-    if constexpr (DT == 0)
-        static_cast<float*>(dst)[i] = v;
-    else
-        static_cast<uint16_t*>(dst)[i] = (uint16_t)(pack_bf16(v, 0.0f) & 0xFFFFu);
-}
 
 // Decode-size messages: one 16-byte output vector per thread.
 template <int DT, int N>
@@ -135,133 +62,7 @@ __global__ __launch_bounds__(256) void k_reduce_flat_tiles(FlatArgs a)
         store_elem<DT>(a.dst, i, fold_vec_tail<DT, N>(a.src, i));
 }
 
-// Ragged end of a chunk (hi not a multiple of the vector): element-wise.
-template <int DT, int N>
-__device__ __forceinline__ void tree_tail(const TreeArgs& a, size_t v1, size_t gid)
-{
-    constexpr int VE = Elem<DT>::kVE;
-    const size_t i = v1 * VE + gid;
-    if (i >= a.lo && i < a.hi) {
-        float z = fold_vec_tail<DT, N>(a.src, i);
-#pragma unroll
-        for (int j = 0; j < N; ++j)
-            store_elem<DT>(a.dst[j], i, z);
-    }
-}
-
-// Two lanes per 16-byte vector: the two half-waves fold the same 32 vectors
-// (their loads share cache lines) and each writes half of the N
-// destinations, so twice the threads share the stores. Nontemporal source
-// loads and destination stores (cached ones measured 15-20% slower at
-// 8 x 4 MiB). TAIL: the chunk ends in a partial vector; the instance
-// without it carries no tail code (0.1 us per decode-size launch).
-template <int DT, int N, bool TAIL>
-__global__ __launch_bounds__(256) void k_tree(TreeArgs a)
-{
-    constexpr int VE = Elem<DT>::kVE;
-    constexpr int H = (N + 1) / 2;        // destinations of the first half-wave
-    const size_t v0 = a.lo / VE;          // lo is 16-B aligned (or == hi)
-    const size_t v1 = a.hi / VE;
-    const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    const int lane = lane_id();
-    const int half = lane / (kWave / 2);
-    const int first = half ? H : 0;
-    const int cnt = half ? N - H : H;
-    // wave w takes vectors 32w .. 32w + 31, both halves the same ones
-    const size_t vv = (gid / kWave) * (kWave / 2) + (size_t)(lane % (kWave / 2));
-    for (size_t v = v0 + vv; v < v1; v += stride / 2) {
-        u32x4 y = fold_vec<DT, N, true>(a.src, v);
-#pragma unroll
-        for (int j = 0; j < H; ++j)
-            if (j < cnt)
-                st16_stream(a.dst[first + j], v, y);
-    }
-    if constexpr (TAIL)
-        tree_tail<DT, N>(a, v1 > v0 ? v1 : v0, gid);
-}
-
-// Small chunks (up to one 64-thread workgroup of half-vector lanes per CU):
-// each lane folds one 8-byte half of a 16-byte vector over all N sources and
-// stores it into all N destinations; no load is issued twice (8 x 512 KiB
-// messages, chunk 64 KiB: 2.26 us against 2.30 us for two lanes per vector).
-template <int DT, int N, bool TAIL>
-__global__ __launch_bounds__(256) void k_tree_half(TreeArgs a)
-{
-    constexpr int VE = Elem<DT>::kVE;
-    const size_t v0 = a.lo / VE;
-    const size_t v1 = a.hi / VE;
-    const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t h = 2 * v0 + gid; h < 2 * v1; h += stride) {
-        u32x2 x[N];
-#pragma unroll
-        for (int r = 0; r < N; ++r)
-            x[r] = __builtin_nontemporal_load(static_cast<const u32x2*>(a.src[r]) + h);
-        u32x2 y;
-        if constexpr (DT == 0) {
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                float acc = bits_f32(x[0][k]);
-#pragma unroll
-                for (int r = 1; r < N; ++r)
-                    acc = acc + bits_f32(x[r][k]);
-                y[k] = __builtin_bit_cast(uint32_t, acc);
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                float lo = bf16_lo(x[0][k]);
-                float hi = bf16_hi(x[0][k]);
-#pragma unroll
-                for (int r = 1; r < N; ++r) {
-                    lo = lo + bf16_lo(x[r][k]);
-                    hi = hi + bf16_hi(x[r][k]);
-                }
-                y[k] = pack_bf16(lo, hi);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < N; ++j)
-            __builtin_nontemporal_store(y, static_cast<u32x2*>(a.dst[j]) + h);
-    }
-    if constexpr (TAIL)
-        tree_tail<DT, N>(a, v1 > v0 ? v1 : v0, gid);
-}
-
-// Large BF16 chunks: the tile scheme of k_reduce_flat_tiles, N destinations.
-template <int DT, int N>
-__global__ __launch_bounds__(256) void k_tree_tiles(TreeArgs a)
-{
-    constexpr int VE = Elem<DT>::kVE;
-    constexpr int U = N <= 8 ? 2 : 1;
-    const int lane = lane_id();
-    const uint32_t wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const size_t wave = (size_t)blockIdx.x * (blockDim.x / kWave) + wave_in_wg;
-    const size_t nwaves = (size_t)gridDim.x * (blockDim.x / kWave);
-    const size_t v0 = a.lo / VE;
-    const size_t v1 = a.hi / VE;
-    const size_t ntiles = (v1 - v0 + (size_t)U * kWave - 1) / ((size_t)U * kWave);
-    for (size_t t = wave; t < ntiles; t += nwaves) {
-        const size_t base = v0 + t * U * kWave + lane;
-        u32x4 y[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (base + u * kWave < v1)
-                y[u] = fold_vec<DT, N, true>(a.src, base + u * kWave);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (base + u * kWave < v1) {
-#pragma unroll
-                for (int j = 0; j < N; ++j)
-                    st16_stream(a.dst[j], base + u * kWave, y[u]);
-            }
-    }
-    tree_tail<DT, N>(a, v1 > v0 ? v1 : v0, (size_t)blockIdx.x * blockDim.x + threadIdx.x);
-}
-
 using FlatFn = void (*)(FlatArgs);
-using TreeFn = void (*)(TreeArgs);
 
 template <int DT, int... I>
 constexpr std::array<FlatFn, sizeof...(I)> flat_table(std::integer_sequence<int, I...>)
@@ -273,54 +74,17 @@ constexpr std::array<FlatFn, sizeof...(I)> flat_tiles_table(std::integer_sequenc
 {
     return {{&k_reduce_flat_tiles<DT, I + 1>...}};
 }
-template <int DT, bool TAIL, int... I>
-constexpr std::array<TreeFn, sizeof...(I)> tree_table(std::integer_sequence<int, I...>)
-{
-    return {{&k_tree<DT, I + 1, TAIL>...}};
-}
-template <int DT, bool TAIL, int... I>
-constexpr std::array<TreeFn, sizeof...(I)> tree_half_table(std::integer_sequence<int, I...>)
-{
-    return {{&k_tree_half<DT, I + 1, TAIL>...}};
-}
-template <int DT, int... I>
-constexpr std::array<TreeFn, sizeof...(I)> tree_tiles_table(std::integer_sequence<int, I...>)
-{
-    return {{&k_tree_tiles<DT, I + 1>...}};
-}
-
 const std::array<FlatFn, kMaxSrc> kFlat[2] = {
     flat_table<0>(std::make_integer_sequence<int, kMaxSrc>{}),
     flat_table<1>(std::make_integer_sequence<int, kMaxSrc>{})};
 const std::array<FlatFn, kMaxSrc> kFlatTiles[2] = {
     flat_tiles_table<0>(std::make_integer_sequence<int, kMaxSrc>{}),
     flat_tiles_table<1>(std::make_integer_sequence<int, kMaxSrc>{})};
-// [dtype][tail][nsrc - 1]
-const std::array<TreeFn, kMaxSrc> kTree[2][2] = {
-    {tree_table<0, false>(std::make_integer_sequence<int, kMaxSrc>{}),
-     tree_table<0, true>(std::make_integer_sequence<int, kMaxSrc>{})},
-    {tree_table<1, false>(std::make_integer_sequence<int, kMaxSrc>{}),
-     tree_table<1, true>(std::make_integer_sequence<int, kMaxSrc>{})}};
-const std::array<TreeFn, kMaxSrc> kTreeHalf[2][2] = {
-    {tree_half_table<0, false>(std::make_integer_sequence<int, kMaxSrc>{}),
-     tree_half_table<0, true>(std::make_integer_sequence<int, kMaxSrc>{})},
-    {tree_half_table<1, false>(std::make_integer_sequence<int, kMaxSrc>{}),
-     tree_half_table<1, true>(std::make_integer_sequence<int, kMaxSrc>{})}};
-const std::array<TreeFn, kMaxSrc> kTreeTiles[2] = {
-    tree_tiles_table<0>(std::make_integer_sequence<int, kMaxSrc>{}),
-    tree_tiles_table<1>(std::make_integer_sequence<int, kMaxSrc>{})};
-
 // One thread per 16-byte output vector. Large messages run one 256-thread
 // workgroup per CU with a grid-stride
 // loop: on MI355X a narrow window of in-flight addresses measured up to 20%
 // faster than filling every CU with 8 workgroups.
 LaunchPolicy policy_flat() { return {128u, 256u, 1u}; }
-// Decode-size chunks run 64-thread workgroups (at 8 x 4 MiB, 2.98 us
-// against 3.06 us with 128 threads).
-LaunchPolicy policy_tree() { return {64u, 256u, 1u}; }
-
-bool small_job(size_t threads) { return threads < kSmallThreadsPerCu * (size_t)device_cu_count(); }
-
 }  // namespace
 
 hipError_t launch_reduce_flat(const FlatArgs& a, int nsrc, int dtype, hipStream_t s)
@@ -335,28 +99,6 @@ hipError_t launch_reduce_flat(const FlatArgs& a, int nsrc, int dtype, hipStream_
     const FlatFn fn = small ? kFlat[dtype][nsrc - 1] : kFlatTiles[dtype][nsrc - 1];
     return launch_logged(small ? "k_reduce_flat" : "k_reduce_flat_tiles", (const void*)fn, grid,
                          block, params, s);
-}
-
-hipError_t launch_tree(const TreeArgs& a, int nsrc, int dtype, hipStream_t s)
-{
-    const int ve = dtype == 0 ? 4 : 8;
-    const size_t nvec = (a.hi - a.lo) / ve;
-    const bool small = small_job(nvec);
-    const int tail = a.hi % (size_t)ve != 0 ? 1 : 0;   // lo is a vector multiple
-    // small chunks: half-vector lanes while they fit one 64-thread workgroup
-    // per CU, two lanes per vector above that
-    const bool half = small && 2 * nvec <= (size_t)64 * (size_t)device_cu_count();
-    dim3 grid, block;
-    launch_geometry(small ? 2 * nvec : nvec, small, policy_tree(), grid, block);
-    TreeArgs arg = a;
-    void* params[] = {&arg};
-    // large chunks: tiles measured 5% faster for BF16 and 5% slower for FP32
-    const bool tiles = !small && dtype != 0;
-    const TreeFn fn = tiles ? kTreeTiles[dtype][nsrc - 1]
-                    : half  ? kTreeHalf[dtype][tail][nsrc - 1]
-                            : kTree[dtype][tail][nsrc - 1];
-    return launch_logged(tiles ? "k_tree_tiles" : half ? "k_tree_half" : "k_tree", (const void*)fn,
-                         grid, block, params, s);
 }
 
 }  // namespace rx
