@@ -28,15 +28,17 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     const bool small = (len + 1023) / 1024 < kSmallTilesPerCu * cus / 2;
     const bool all = requant && a.out_hps[0] != nullptr;   // every rank's buffer
     const bool fp32_out = (a.out_hp != nullptr || all) && !a.hp_bf16;
+    const bool codes_only = requant && !all && a.out_hp == nullptr;
     // chunk layout (codes per lane per chunk, chunks per lane); block / CPC <= 64
     int cpc = 16, u = 1;
     if (small) {
         if (a.block <= 256) cpc = 4;
     } else if (fp32_out) {
         if (a.block <= 256) { cpc = 4; u = 4; }
-    } else if (a.block <= 512 && !(a.nout > 1 && a.out_hp == nullptr)) {
-        // codes-only pushes to N destinations keep 16 x 1: 16-byte code
-        // stores measured 1-3% faster there
+    } else if (a.block <= 512 && !codes_only) {
+        // codes only (one destination or a push to N) keep 16 x 1: 16-byte
+        // code stores measured 7-13% faster at 8 x 4M..64M codes with one
+        // destination and 1-3% with N
         cpc = 8;
         u = 2;
     }
@@ -54,6 +56,15 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
                         tiles < (size_t)16 * 2 * (256 / kWave) * cus;
     if (medium)
         pol.max_wgs_per_cu = 4;
+    // Codes only, one destination (16 x 1): below 32 tiles per CU four
+    // workgroups per CU in plain order; above, two per CU with each XCD a
+    // contiguous range (8 x 4M codes E4M3/128: 7.1 us against 8.2 us with
+    // two per CU; 8 x 16M: 25.4 us, 8 x 64M: 100.7 us against 105.1 us in
+    // plain order).
+    const bool single_codes = !small && r == kDrrRequant && cpc == 16;
+    const bool few = single_codes && tiles < (size_t)32 * cus;
+    if (few)
+        pol.max_wgs_per_cu = 4;
     dim3 grid, blk;
     launch_geometry(tiles * kWave, small, pol, grid, blk);
     DrrArgs arg = a;
@@ -62,7 +73,8 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     // destination) meet in one L2. Measured: decode-size 8% faster; large
     // pushes to N destinations 3-8% and the FP32-output layout 2% faster;
     // no gain for the other large layouts, which keep the plain order.
-    arg.xcd_ranges = (small || medium || r == kDrrRequantPush || (cpc == 4 && u == 4)) ? 1 : 0;
+    arg.xcd_ranges = (small || medium || r == kDrrRequantPush || (cpc == 4 && u == 4) ||
+                      (single_codes && !few)) ? 1 : 0;
     if (small && blk.x == (unsigned)kWave) {
         // Decode-size launches (one tile per 64-thread workgroup): each XCD
         // takes a contiguous range of tiles that covers whole 128-byte lines

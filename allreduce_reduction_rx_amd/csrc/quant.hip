@@ -210,27 +210,34 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a)
 
 using QuantFn = void (*)(QuantArgs);
 
-template <int DT, int F, bool SMALL, int... L>
+// U: loads per lane of the large variants (4 or 8); 0 for the decode-size
+// variant (the loads per block).
+template <int DT, int F, int U, int... L>
 constexpr std::array<QuantFn, sizeof...(L)> quant_row(std::integer_sequence<int, L...>)
 {
-    return {{&k_quant<DT, F, (32 << L), SMALL ? loads_per_block<DT, (32 << L)>() : 4, SMALL>...}};
+    return {{&k_quant<DT, F, (32 << L), U ? U : loads_per_block<DT, (32 << L)>(), U == 0>...}};
 }
 
-template <bool SMALL>
+template <int U>
 struct QuantTable {
     // [src dtype][fmt][log2(block) - 5]
     std::array<QuantFn, 6> fn[2][2] = {
-        {quant_row<0, 0, SMALL>(std::make_integer_sequence<int, 6>{}),
-         quant_row<0, 1, SMALL>(std::make_integer_sequence<int, 6>{})},
-        {quant_row<1, 0, SMALL>(std::make_integer_sequence<int, 6>{}),
-         quant_row<1, 1, SMALL>(std::make_integer_sequence<int, 6>{})}};
+        {quant_row<0, 0, U>(std::make_integer_sequence<int, 6>{}),
+         quant_row<0, 1, U>(std::make_integer_sequence<int, 6>{})},
+        {quant_row<1, 0, U>(std::make_integer_sequence<int, 6>{}),
+         quant_row<1, 1, U>(std::make_integer_sequence<int, 6>{})}};
 };
-const QuantTable<false> kQuantLarge;
-const QuantTable<true> kQuantSmall;
+const QuantTable<0> kQuantSmall;
+const QuantTable<4> kQuantLarge;
+const QuantTable<8> kQuantHuge;
 
-// One wave per tile (64 threads per work item). Large messages: 256-thread
-// workgroups, at most 2 per CU (a narrow HBM access window measured best on
-// MI355X); decode-size messages: one tile per wave over every CU.
+// One wave per tile (64 threads per work item), 256-thread workgroups.
+// Messages of at least 16 tiles of 8 loads per wave at two workgroups per CU:
+// U = 8, at most 2 workgroups per CU (a narrow HBM access window); below
+// that U = 4 and 4 per CU. Measured on MI355X: 8 x 16M FP32 E4M3/128 114.3 us
+// (U = 4, 2 per CU: 116.3), 8 x 256M BF16 E5M2/256 1139 us (1152); 8 x 2M
+// FP32 16.0 us (17.3), 8 x 8M BF16 35.7 us (37.3). Decode-size messages: one
+// tile per wave over every CU.
 LaunchPolicy policy_quant() { return {256u, 256u, 2u}; }
 
 }  // namespace
@@ -241,19 +248,26 @@ hipError_t launch_quant(const QuantArgs& a, int src_dtype, int fmt, int block, h
     const size_t vec_elems = src_dtype == 0 ? 4 : 8;
     const size_t cus = (size_t)device_cu_count();
     const size_t large_tiles = (a.count + 4 * 64 * vec_elems - 1) / (4 * 64 * vec_elems) * (size_t)a.nsrc;
+    const size_t huge_tiles = (a.count + 8 * 64 * vec_elems - 1) / (8 * 64 * vec_elems) * (size_t)a.nsrc;
     const bool small = large_tiles < kSmallTilesPerCu * cus;
+    const bool huge = huge_tiles >= (size_t)16 * 8 * cus;
     // loads per tile of the chosen variant
     size_t lanes_per_block = (size_t)block / vec_elems;
-    size_t u = small ? (lanes_per_block <= 64 ? 1 : lanes_per_block / 64) : 4;
+    size_t u = small ? (lanes_per_block <= 64 ? 1 : lanes_per_block / 64) : huge ? 8 : 4;
     const size_t tile_elems = u * 64 * vec_elems;
     const size_t tiles = (a.count + tile_elems - 1) / tile_elems * (size_t)a.nsrc;
+    LaunchPolicy pol = policy_quant();
+    if (!small && !huge)
+        pol.max_wgs_per_cu = 4;
     dim3 grid, blk;
-    launch_geometry(tiles * kWave, small, policy_quant(), grid, blk);
+    launch_geometry(tiles * kWave, small, pol, grid, blk);
     QuantArgs arg = a;
     void* params[] = {&arg};
-    QuantFn fn = small ? kQuantSmall.fn[src_dtype][fmt][lb] : kQuantLarge.fn[src_dtype][fmt][lb];
-    return launch_logged(small ? "k_quant (decode size)" : "k_quant", (const void*)fn, grid, blk,
-                         params, s);
+    QuantFn fn = small ? kQuantSmall.fn[src_dtype][fmt][lb]
+               : huge  ? kQuantHuge.fn[src_dtype][fmt][lb]
+                       : kQuantLarge.fn[src_dtype][fmt][lb];
+    return launch_logged(small ? "k_quant (decode size)" : huge ? "k_quant (8 loads per lane)" : "k_quant",
+                         (const void*)fn, grid, blk, params, s);
 }
 
 }  // namespace rx

@@ -247,6 +247,23 @@ def test_quant_large_variant_ragged(dtype, fmt, block):
     assert bits_equal(gs[0], rs[0]), first_mismatch(gs[0], rs[0])
 
 
+@pytest.mark.parametrize("dtype,fmt,block", [(O.FP32, O.E4M3, 128), (O.BF16, O.E5M2, 1024),
+                                             (O.FP32, O.E5M2, 1024)])
+def test_quant_eight_loads_ragged(dtype, fmt, block):
+    # at least 16 tiles of 8 loads per wave at two 256-thread workgroups per
+    # CU on a 256-CU MI355X: the 8-loads-per-lane kernel (blocks of one and
+    # of several loads), ragged tail and partial last block of every source
+    n = 8
+    count = (8 if dtype == O.FP32 else 16) * (1 << 20) + 5
+    log(f"quant 8 loads per lane dtype={dtype} fmt={fmt} block={block}")
+    srcs = [G.fill(count, dtype, G.NORMAL_OUTLIER, seed=3600 + block, rank=r) for r in range(n)]
+    gc, gs = _quant_gpu(srcs, dtype, fmt, block, count)
+    rc, rs = O.quant_fp8(srcs, dtype, fmt, block)
+    for j in range(n):
+        assert bits_equal(gc[j], rc[j]), f"codes src={j}: " + first_mismatch(gc[j], rc[j])
+        assert bits_equal(gs[j], rs[j]), f"scales src={j}: " + first_mismatch(gs[j], rs[j])
+
+
 def test_quant_degenerate_blocks():
     # zero blocks, tiny blocks (FMAX / A overflows), huge values, -0
     count, block = 1024, 128
@@ -307,12 +324,29 @@ def test_drr_shapes(fmt, block, n):
                     assert bits_equal(g, r), f"{name} count={count}: " + first_mismatch(g, r)
 
 
+@pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 256), (O.E4M3, 1024)])
+def test_drr_codes_only_two_per_cu(fmt, block):
+    # code-only output with at least 32 tiles of 1024 codes per CU on a
+    # 256-CU MI355X: 16 x 1 layout, two workgroups per CU, each XCD a
+    # contiguous range of tiles; ragged tail and partial last block
+    n, count = 3, 8 * (1 << 20) + 7
+    srcs = [G.fill(count, O.FP32, G.LAPLACE, seed=4600 + block, rank=r) for r in range(n)]
+    codes, scales = O.quant_fp8(srcs, O.FP32, fmt, block)
+    log(f"drr codes only fmt={fmt} block={block} count={count}")
+    got = _drr_gpu(codes, scales, fmt, block, O.DRR_REQUANT, O.FP32, False, count)
+    ref = O.dequant_reduce_requant(codes, scales, fmt, block, O.DRR_REQUANT, O.FP32, False)
+    for name, g, r in zip(("codes", "scales", "hp"), got, ref):
+        assert (g is None) == (r is None)
+        if g is not None:
+            assert bits_equal(g, r), f"{name}: " + first_mismatch(g, r)
+
+
 @pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 256), (O.E4M3, 32),
                                        (O.E5M2, 512), (O.E4M3, 1024)])
 def test_drr_large_variant_ragged(fmt, block):
     # > 1024 tiles of 1024 codes: the grid-stride kernels in every chunk
-    # layout (16 codes x 1, 8 x 2 for BF16 / code-only output, 4 x 4 for FP32
-    # output), ragged tail and partial last block
+    # layout (16 codes x 1 for code-only output, 8 x 2 for BF16 output, 4 x 4
+    # for FP32 output), ragged tail and partial last block
     n, count = 4, (1 << 21) + 7
     srcs = [G.fill(count, O.FP32, G.LAPLACE, seed=4500 + block, rank=r) for r in range(n)]
     codes, scales = O.quant_fp8(srcs, O.FP32, fmt, block)
