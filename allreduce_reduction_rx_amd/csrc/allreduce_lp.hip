@@ -23,44 +23,67 @@
 namespace rx {
 namespace {
 
-// Widen a 16-byte vector to kVE floats (exact).
-template <int DT>
-__device__ __forceinline__ void widen_vec(const u32x4& x, float* f)
+// A lane's share of one buffer: LB = 16 or 8 bytes.
+template <int LB>
+struct LaneVec;
+template <>
+struct LaneVec<16> {
+    using T = u32x4;
+};
+template <>
+struct LaneVec<8> {
+    using T = u32x2;
+};
+
+// Widen a lane's LB bytes to VE floats (exact).
+template <int DT, int W, typename V>
+__device__ __forceinline__ void widen_lane(const V& x, float* f)
 {
-    if constexpr (DT == 0) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) f[k] = bits_f32(x[k]);
-    } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < W; ++k) {
+        if constexpr (DT == 0) {
+            f[k] = bits_f32(x[k]);
+        } else {
             f[2 * k] = bf16_lo(x[k]);
             f[2 * k + 1] = bf16_hi(x[k]);
         }
     }
 }
 
-// Elements [e, count) of a partial vector, the rest zero (neutral for the
-// block absmax; never stored).
-template <int DT>
-__device__ __forceinline__ u32x4 load_tail(const void* src, size_t e, size_t count)
+// Elements [e, count) of a partial lane vector, the rest zero (neutral for
+// the block absmax; never stored). Every element is loaded from an index
+// clamped to count - 1 (in bounds, count >= 1) and masked afterwards, so the
+// loads carry no branches and are all in flight before the first use.
+template <int DT, int W, typename V>
+__device__ __forceinline__ V load_tail(const void* src, size_t e, size_t count)
 {
-    u32x4 x = {0u, 0u, 0u, 0u};
+    V x = {};
     if constexpr (DT == 0) {
         const uint32_t* p = static_cast<const uint32_t*>(src);
+        uint32_t w[W];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (e + k < count) x[k] = p[e + k];
+        for (int k = 0; k < W; ++k)
+            w[k] = p[e + k < count ? e + k : count - 1];
+#pragma unroll
+        for (int k = 0; k < W; ++k)
+            x[k] = e + k < count ? w[k] : 0u;
     } else {
         const uint16_t* p = static_cast<const uint16_t*>(src);
+        uint32_t h[2 * W];
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (e + k < count) x[k / 2] |= (uint32_t)p[e + k] << (16 * (k & 1));
+        for (int k = 0; k < 2 * W; ++k)
+            h[k] = p[e + k < count ? e + k : count - 1];
+#pragma unroll
+        for (int k = 0; k < 2 * W; ++k)
+            x[k / 2] |= (e + k < count ? h[k] : 0u) << (16 * (k & 1));
     }
     return x;
 }
 
 // dequant(quant(f)) of the VE values of one lane, for a block whose absmax
-// over its LPB lanes is taken here: out[k] = fl32(decode(code_k) * s).
+// over its LPB lanes is taken here: out[k] = fl32(decode(code_k) * s). The
+// codes are converted and decoded two at a time (both conversions work
+// element by element, so the pairing does not change any result).
 template <int F, int LPB, int VE>
 __device__ __forceinline__ void quant_dequant(const float* f, float* out)
 {
@@ -72,23 +95,28 @@ __device__ __forceinline__ void quant_dequant(const float* f, float* out)
     float s, r;
     block_scale<F>(A, s, r);
 #pragma unroll
-    for (int q = 0; q < VE / 4; ++q) {
-        const uint32_t w = f32x4_to_fp8<F>(clamp_fmax<F>(f[4 * q] * r), clamp_fmax<F>(f[4 * q + 1] * r),
-                                           clamp_fmax<F>(f[4 * q + 2] * r), clamp_fmax<F>(f[4 * q + 3] * r));
-        float d[4];
-        fp8x4_to_f32<F>(w, d);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            out[4 * q + k] = d[k] * s;
+    for (int q = 0; q < VE / 2; ++q) {
+        const float y0 = clamp_fmax<F>(f[2 * q] * r);
+        const float y1 = clamp_fmax<F>(f[2 * q + 1] * r);
+        f32x2 d;
+        if constexpr (F == kE4M3)
+            d = __builtin_amdgcn_cvt_pk_f32_fp8(__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false), false);
+        else
+            d = __builtin_amdgcn_cvt_pk_f32_bf8(__builtin_amdgcn_cvt_pk_bf8_f32(y0, y1, 0, false), false);
+        out[2 * q] = d[0] * s;
+        out[2 * q + 1] = d[1] * s;
     }
 }
 
-// One wave per tile of 64 vectors of every rank (lane l: vector tile * 64 +
-// l); a block spans LPB = BLOCK / VE <= 64 lanes of one tile.
-template <int DT, int F, int BLOCK, int N>
+// One wave per tile of 64 lane vectors of every rank (lane l: lane vector
+// tile * 64 + l of LB bytes); a block spans LPB = BLOCK / VE <= 64 lanes of
+// one tile.
+template <int DT, int F, int BLOCK, int N, int LB>
 __global__ __launch_bounds__(256) void k_allreduce_lp(AllreduceLpArgs a)
 {
-    constexpr int VE = DT == 0 ? 4 : 8;
+    using V = typename LaneVec<LB>::T;
+    constexpr int W = LB / 4;                      // 32-bit words per lane vector
+    constexpr int VE = DT == 0 ? W : 2 * W;        // elements per lane vector
     constexpr int LPB = BLOCK / VE;
     static_assert(LPB >= 1 && LPB <= kWave, "a block lies in the lanes of one wave");
     constexpr size_t kTileElems = (size_t)kWave * VE;
@@ -104,28 +132,29 @@ __global__ __launch_bounds__(256) void k_allreduce_lp(AllreduceLpArgs a)
         const size_t v = t * kWave + lane;
         const size_t e = v * VE;
         const bool full = (t + 1) * kTileElems <= a.count;   // uniform
-        u32x4 x[N];
+        V x[N];
         if (full) {
 #pragma unroll
             for (int r = 0; r < N; ++r)
-                x[r] = ld16_stream(a.buf[r], v);
+                x[r] = __builtin_nontemporal_load(static_cast<const V*>(a.buf[r]) + v);
         } else {
+            // the one partial tile: element loads of every rank, no branches
 #pragma unroll
             for (int r = 0; r < N; ++r)
-                x[r] = e + VE <= a.count ? ld16(a.buf[r], v) : load_tail<DT>(a.buf[r], e, a.count);
+                x[r] = load_tail<DT, W, V>(a.buf[r], e, a.count);
         }
 
         // every rank's block quantized and dequantized, folded in rank order
         float S[VE];
         {
             float f[VE];
-            widen_vec<DT>(x[0], f);
+            widen_lane<DT, W>(x[0], f);
             quant_dequant<F, LPB, VE>(f, S);
         }
 #pragma unroll
         for (int r = 1; r < N; ++r) {
             float f[VE], d[VE];
-            widen_vec<DT>(x[r], f);
+            widen_lane<DT, W>(x[r], f);
             quant_dequant<F, LPB, VE>(f, d);
 #pragma unroll
             for (int k = 0; k < VE; ++k)
@@ -134,22 +163,22 @@ __global__ __launch_bounds__(256) void k_allreduce_lp(AllreduceLpArgs a)
         // the requantized sum, dequantized: every rank's result
         float h[VE];
         quant_dequant<F, LPB, VE>(S, h);
-        u32x4 y;
-        if constexpr (DT == 0) {
+        V y;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) y[k] = __builtin_bit_cast(uint32_t, h[k]);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) y[k] = pack_bf16(h[2 * k], h[2 * k + 1]);
+        for (int k = 0; k < W; ++k) {
+            if constexpr (DT == 0)
+                y[k] = __builtin_bit_cast(uint32_t, h[k]);
+            else
+                y[k] = pack_bf16(h[2 * k], h[2 * k + 1]);
         }
         if (full) {
 #pragma unroll
             for (int r = 0; r < N; ++r)
-                st16_stream(a.buf[r], v, y);
+                __builtin_nontemporal_store(y, static_cast<V*>(a.buf[r]) + v);
         } else if (e + VE <= a.count) {
 #pragma unroll
             for (int r = 0; r < N; ++r)
-                st16(a.buf[r], v, y);
+                static_cast<V*>(a.buf[r])[v] = y;
         } else {
 #pragma unroll
             for (int r = 0; r < N; ++r) {
@@ -170,14 +199,15 @@ __global__ __launch_bounds__(256) void k_allreduce_lp(AllreduceLpArgs a)
 
 using LpFn = void (*)(AllreduceLpArgs);
 
-template <int DT, int F, int BLOCK, int... I>
+template <int DT, int F, int BLOCK, int LB, int... I>
 constexpr std::array<LpFn, sizeof...(I)> lp_row(std::integer_sequence<int, I...>)
 {
-    return {{&k_allreduce_lp<DT, F, BLOCK, I + 1>...}};
+    return {{&k_allreduce_lp<DT, F, BLOCK, I + 1, LB>...}};
 }
 
-// Rows by block size (32, 64, ...): blocks of at most 64 vectors, FP32
-// 32..256 and BF16 32..512 (larger blocks use the two-pass path).
+// Rows by block size (32, 64, ...): blocks of at most 64 lane vectors, with
+// 16-byte lanes FP32 32..256 and BF16 32..512 (larger blocks use the
+// two-pass path).
 template <int DT, int F>
 struct LpTable {
     static constexpr int kRows = DT == 0 ? 4 : 5;
@@ -189,12 +219,12 @@ LpTable<DT, F> make_lp_table()
 {
     const auto seq = std::make_integer_sequence<int, kMaxSrc>{};
     LpTable<DT, F> t{};
-    t.row[0] = lp_row<DT, F, 32>(seq);
-    t.row[1] = lp_row<DT, F, 64>(seq);
-    t.row[2] = lp_row<DT, F, 128>(seq);
-    t.row[3] = lp_row<DT, F, 256>(seq);
+    t.row[0] = lp_row<DT, F, 32, 16>(seq);
+    t.row[1] = lp_row<DT, F, 64, 16>(seq);
+    t.row[2] = lp_row<DT, F, 128, 16>(seq);
+    t.row[3] = lp_row<DT, F, 256, 16>(seq);
     if constexpr (DT == 1)
-        t.row[4] = lp_row<DT, F, 512>(seq);
+        t.row[4] = lp_row<DT, F, 512, 16>(seq);
     return t;
 }
 
@@ -203,13 +233,42 @@ const LpTable<0, 1> kLpF32E5 = make_lp_table<0, 1>();
 const LpTable<1, 0> kLpB16E4 = make_lp_table<1, 0>();
 const LpTable<1, 1> kLpB16E5 = make_lp_table<1, 1>();
 
-// Decode-size messages: one tile per wave in 64-thread workgroups over every
-// CU, each XCD a contiguous range. Large ones: four 64-thread workgroups per
-// CU (one wave per SIMD), grid-stride; measured on MI355X against 2-16 per
-// CU and 128/256-thread workgroups: 8 x 512 MiB BF16 E5M2/256 1487 us
-// (two 256-thread workgroups: 1942 us; five or three 64-thread ones: 1691,
-// 1879 us), 8 x 64 MiB FP32 E4M3/128 180 us (207 us).
-LaunchPolicy policy_lp() { return {64u, 64u, 4u}; }
+// 8-byte lanes (4 BF16 elements), for decode-size BF16 messages: twice the
+// waves, each with half the per-element work. Blocks 32..256.
+template <int F>
+struct LpNarrowTable {
+    std::array<LpFn, kMaxSrc> row[4];
+};
+
+template <int F>
+LpNarrowTable<F> make_lp_narrow_table()
+{
+    const auto seq = std::make_integer_sequence<int, kMaxSrc>{};
+    LpNarrowTable<F> t{};
+    t.row[0] = lp_row<1, F, 32, 8>(seq);
+    t.row[1] = lp_row<1, F, 64, 8>(seq);
+    t.row[2] = lp_row<1, F, 128, 8>(seq);
+    t.row[3] = lp_row<1, F, 256, 8>(seq);
+    return t;
+}
+
+const LpNarrowTable<0> kLpB16E4Narrow = make_lp_narrow_table<0>();
+const LpNarrowTable<1> kLpB16E5Narrow = make_lp_narrow_table<1>();
+
+// Launch shape by the number of 16-byte-lane tiles T (measured on MI355X,
+// 8 ranks, HBM-cold rotating buffers):
+//  - T <= 2 per CU, BF16, blocks <= 256: 8-byte lanes, one tile per wave in
+//    256-thread workgroups, each XCD a contiguous range (8 x 512 KiB
+//    E5M2/256: 4.2 us against 4.8 us with 16-byte lanes);
+//  - T <= 16 per CU: 256-thread workgroups, at most 2 per CU (8 x 2 MiB FP32
+//    E4M3/128: 6.9 us against 9.5 us; 8 x 4 MiB BF16: 14.8 against 15.3);
+//  - larger: four 64-thread workgroups per CU (one wave per SIMD),
+//    grid-stride: 8 x 512 MiB BF16 E5M2/256 1480 us (two 256-thread
+//    workgroups per CU: 1942 us; five or three 64-thread ones: 1691,
+//    1879 us), 8 x 64 MiB FP32 E4M3/128 180 us (207 us).
+LaunchPolicy policy_lp_narrow() { return {256u, 256u, 0u}; }
+LaunchPolicy policy_lp_medium() { return {256u, 256u, 2u}; }
+LaunchPolicy policy_lp_large() { return {64u, 64u, 4u}; }
 
 }  // namespace
 
@@ -224,17 +283,26 @@ hipError_t launch_allreduce_lp(const AllreduceLpArgs& a, int nsrc, int dtype, in
     if (!allreduce_lp_fits(dtype, block))
         return hipErrorInvalidValue;
     const int lb = __builtin_ctz((unsigned)block) - 5;
+    const size_t cus = (size_t)device_cu_count();
     const size_t ve = dtype == 0 ? 4 : 8;
-    const size_t tiles = (a.count + 64 * ve - 1) / (64 * ve);
-    const bool small = tiles < kSmallTilesPerCu * (size_t)device_cu_count();
+    const size_t tiles = (a.count + 64 * ve - 1) / (64 * ve);     // 16-byte-lane tiles
+    const bool narrow = dtype == 1 && block <= 256 && tiles <= 2 * cus;
+    const bool medium = !narrow && tiles <= 16 * cus;
     dim3 grid, blk;
-    launch_geometry(tiles * kWave, small, policy_lp(), grid, blk);
     AllreduceLpArgs arg = a;
-    arg.xcd_ranges = small ? 1 : 0;
+    arg.xcd_ranges = narrow ? 1 : 0;
+    LpFn fn;
+    if (narrow) {
+        const size_t tiles8 = (a.count + 64 * 4 - 1) / (64 * 4);
+        launch_geometry(tiles8 * kWave, true, policy_lp_narrow(), grid, blk);
+        fn = fmt == 0 ? kLpB16E4Narrow.row[lb][nsrc - 1] : kLpB16E5Narrow.row[lb][nsrc - 1];
+    } else {
+        launch_geometry(tiles * kWave, false, medium ? policy_lp_medium() : policy_lp_large(), grid, blk);
+        fn = dtype == 0 ? (fmt == 0 ? kLpF32E4.row[lb][nsrc - 1] : kLpF32E5.row[lb][nsrc - 1])
+                        : (fmt == 0 ? kLpB16E4.row[lb][nsrc - 1] : kLpB16E5.row[lb][nsrc - 1]);
+    }
     void* params[] = {&arg};
-    const LpFn fn = dtype == 0 ? (fmt == 0 ? kLpF32E4.row[lb][nsrc - 1] : kLpF32E5.row[lb][nsrc - 1])
-                               : (fmt == 0 ? kLpB16E4.row[lb][nsrc - 1] : kLpB16E5.row[lb][nsrc - 1]);
-    return launch_logged(small ? "k_allreduce_lp (decode size)" : "k_allreduce_lp",
+    return launch_logged(narrow ? "k_allreduce_lp (8-byte lanes)" : medium ? "k_allreduce_lp (medium)" : "k_allreduce_lp",
                          (const void*)fn, grid, blk, params, s);
 }
 

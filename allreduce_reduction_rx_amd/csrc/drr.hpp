@@ -66,12 +66,20 @@ __device__ __forceinline__ Chunk<CPC> load_chunk(const uint8_t* p, size_t c, siz
         } else {
             x.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p) + c);
         }
-    } else {  // codes [e, count) byte by byte, the rest code 0 (decodes to +0)
+    } else {
+        // codes [e, count) byte by byte, the rest code 0 (decodes to +0):
+        // each byte loaded from an index clamped to count - 1 (in bounds,
+        // count >= 1) and masked afterwards, so the loads carry no branches
+        // and are all in flight before the first use
+        uint32_t b[CPC];
+#pragma unroll
+        for (int k = 0; k < CPC; ++k)
+            b[k] = p[e + k < count ? e + k : count - 1];
 #pragma unroll
         for (int q = 0; q < CPC / 4; ++q) x.w[q] = 0u;
 #pragma unroll
         for (int k = 0; k < CPC; ++k)
-            if (e + k < count) x.w[k / 4] |= (uint32_t)p[e + k] << (8 * (k & 3));
+            x.w[k / 4] |= (e + k < count ? b[k] : 0u) << (8 * (k & 3));
     }
     return x;
 }
@@ -208,7 +216,9 @@ __device__ __forceinline__ void drr_tile(const DrrArgs& a, uint32_t t, int lane,
         const uint8_t* cp = static_cast<const uint8_t*>(a.codes[r]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            x[r][u] = load_chunk<CPC>(cp, c[u], e[u], count, whole[u]);
+            // the partial last tile loads byte by byte in every lane (no
+            // branches, one wait for all sources)
+            x[r][u] = load_chunk<CPC>(cp, c[u], e[u], count, WHOLE);
             sc[r][u] = valid[u] ? a.scales[r][b[u]] : 0.0f;
         }
     }

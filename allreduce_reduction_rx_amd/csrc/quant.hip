@@ -64,22 +64,33 @@ __device__ __forceinline__ void widen(const u32x4& x, float* f)
     }
 }
 
-// Partial vector at the end of a ragged source: elements [e, count) loaded
-// one by one, the rest zero (zero is neutral for the absmax).
+// Partial vector at the end of a ragged source: elements [e, count), the
+// rest zero (zero is neutral for the absmax). Every element is loaded from
+// an index clamped to count - 1 (in bounds, count >= 1) and masked
+// afterwards, so the loads carry no branches and are all in flight before
+// the first use.
 template <int DT>
 __device__ __forceinline__ u32x4 load_partial(const void* src, size_t e, size_t count)
 {
     u32x4 x = {0u, 0u, 0u, 0u};
     if constexpr (DT == 0) {
         const uint32_t* p = static_cast<const uint32_t*>(src);
+        uint32_t w[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            if (e + k < count) x[k] = p[e + k];
+            w[k] = p[e + k < count ? e + k : count - 1];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            x[k] = e + k < count ? w[k] : 0u;
     } else {
         const uint16_t* p = static_cast<const uint16_t*>(src);
+        uint32_t h[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            if (e + k < count) x[k / 2] |= (uint32_t)p[e + k] << (16 * (k & 1));
+            h[k] = p[e + k < count ? e + k : count - 1];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            x[k / 2] |= (e + k < count ? h[k] : 0u) << (16 * (k & 1));
     }
     return x;
 }
@@ -119,14 +130,10 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a)
             for (int u = 0; u < U; ++u)
                 x[u] = ld16_stream(src, v0 + u * kWave + lane);
         } else {
+            // the partial last tile of a source: element loads, no branches
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const size_t e = (v0 + u * kWave + lane) * VE;
-                if (e + VE <= a.count)
-                    x[u] = ld16(src, v0 + u * kWave + lane);
-                else
-                    x[u] = load_partial<DT>(src, e, a.count);
-            }
+            for (int u = 0; u < U; ++u)
+                x[u] = load_partial<DT>(src, (v0 + u * kWave + lane) * VE, a.count);
         }
 
         float f[U][VE];
