@@ -109,14 +109,37 @@ __device__ __forceinline__ float clamp_fmax(float y)
 }
 
 // Block scale and its reciprocal from the block absmax A: s = A / FMAX and
-// r = FMAX / A, each one correctly rounded FP32 division; A == 0, s == 0 or
+// r = FMAX / A, each the correctly rounded FP32 quotient; A == 0, s == 0 or
 // r not finite gives s = r = 1.
+//
+// Both quotients are FMA-corrected products (P. Markstein, "IA-64 and
+// Elementary Functions", Prentice Hall 2000: for a quotient b / d with an
+// approximation y of 1 / d, q0 = b y, e = b - q0 d, exact with an FMA, and
+// q = q0 + e y): 10 instructions instead of two division sequences of 11.
+// s takes y = RN(1 / FMAX), a compile-time constant. r takes the hardware
+// reciprocal of A / 4, refined by one Newton step, and divides FMAX / 4 by
+// A / 4: the quarter scaling is exact wherever the result is not degenerate
+// and keeps the reciprocal normal up to A = FLT_MAX. Checked against IEEE
+// division for every finite A >= 0 with every reciprocal estimate within
+// 1 ulp of the true one (tests/bruteforce/block_scale_sweep.c), and on the
+// GPU against the oracle for every A up to +inf.
 template <int F>
 __device__ __forceinline__ void block_scale(float a, float& s, float& r)
 {
     constexpr float m = Fp8Traits<F>::kMax;
-    float sv = a / m;
-    float rv = m / a;
+    constexpr float inv_m = 1.0f / m;      // RN(1 / FMAX)
+    constexpr float m4 = 0.25f * m;
+    const float q0 = a * inv_m;
+    float sv = __builtin_fmaf(__builtin_fmaf(-q0, m, a), inv_m, q0);
+    const float a4 = 0.25f * a;
+    const float y0 = __builtin_amdgcn_rcpf(a4);
+    const float y1 = __builtin_fmaf(__builtin_fmaf(-a4, y0, 1.0f), y0, y0);
+    const float p0 = m4 * y1;
+    float rv = __builtin_fmaf(__builtin_fmaf(-p0, a4, m4), y1, p0);
+    // A = +inf: the quotients are +inf and 0 (the sequences give NaN)
+    const bool inf = a == __builtin_inff();
+    sv = inf ? a : sv;
+    rv = inf ? 0.0f : rv;
     bool degenerate = (a == 0.0f) | (sv == 0.0f) | !__builtin_isfinite(rv);
     s = degenerate ? 1.0f : sv;
     r = degenerate ? 1.0f : rv;

@@ -122,7 +122,7 @@ rx_status_t rxtest_block_scale_bits(uint32_t first, size_t n, rx_dtype_t fmt,
 {
     if (!s || !r) return RX_ERR_NULL;
     if (fmt != RX_FP8_E4M3 && fmt != RX_FP8_E5M2) return RX_ERR_DTYPE;
-    if ((size_t)first + n > 0x7F800000u) return RX_ERR_ARG;
+    if ((size_t)first + n > 0x80000000u) return RX_ERR_ARG;
     if (n == 0) return RX_OK;
     (void)hipGetLastError();   // drop an earlier call's error
     if (fmt == RX_FP8_E4M3)

@@ -30,9 +30,10 @@ rx_status_t rxtest_bf16_round_bits(uint32_t first, size_t n, uint16_t* out,
                                    hipStream_t stream);
 
 /* s[i], r[i] = the kernels' block scale and reciprocal for the block absmax
- * A = FP32 pattern (first + i): s = A / FMAX, r = FMAX / A (correctly rounded
- * divisions), s = r = 1 for A == 0, s == 0 or r not finite. Patterns must be
- * finite and non-negative: first + n <= 0x7F800000. */
+ * A = FP32 pattern (first + i): s = A / FMAX, r = FMAX / A (the correctly
+ * rounded quotients), s = r = 1 for A == 0, s == 0 or r not finite (so also
+ * for NaN); A = +inf gives s = +inf, r = 0. Patterns must have the sign bit
+ * clear: first + n <= 0x80000000. */
 rx_status_t rxtest_block_scale_bits(uint32_t first, size_t n, rx_dtype_t fmt,
                                     float* s, float* r, hipStream_t stream);
 

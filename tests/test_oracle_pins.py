@@ -406,6 +406,51 @@ def test_block_scale_every_absmax(fmt, scale_sweep):
     assert bad.value == 0, f"{bad.value} wrong scales, first at A bits {first.value:#010x}"
 
 
+@pytest.fixture(scope="module")
+def kernel_scale_sweep():
+    """tests/bruteforce/block_scale_sweep.c built for the host: the kernels'
+    division-free block scale repeated in host FP32 against IEEE division."""
+    import ctypes
+    import shutil
+    import subprocess
+    import tempfile
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    tmp = tempfile.mkdtemp()
+    so = os.path.join(tmp, "libkscalesweep.so")
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bruteforce", "block_scale_sweep.c")
+    r = subprocess.run([gcc, "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+                        "-pthread", src, "-o", so, "-lm"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    L = ctypes.CDLL(so)
+    U64 = ctypes.POINTER(ctypes.c_uint64)
+    L.block_scale_sweep.argtypes = [ctypes.c_float, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                    ctypes.c_int, U64, U64, ctypes.POINTER(ctypes.c_uint32)]
+    L.block_scale_sweep.restype = ctypes.c_int
+    yield L
+    shutil.rmtree(tmp, ignore_errors=True)
+
+
+@pytest.mark.parametrize("fmt", [O.E4M3, O.E5M2])
+def test_kernel_block_scale_arithmetic(fmt, kernel_scale_sweep):
+    # The FMA-corrected quotients the kernels use for s and r, with every
+    # reciprocal estimate within 1 ulp: every 61st A pattern up to +inf, and
+    # every pattern in the ranges where the steps could break down (tiny A,
+    # where s is subnormal and r overflows; A within four binades of
+    # FLT_MAX, where 1 / A is subnormal). The full sweep of all 2^31 patterns
+    # (step 1 over [0, 0x7F800001)) also finds no mismatch; it takes about
+    # 1.5 minutes on 8 threads.
+    import ctypes
+    threads = max(1, min(os.cpu_count() or 1, 16))
+    for lo, hi, step in ((0, 0x7F800001, 61), (0, 0x01000000, 1), (0x7D800000, 0x7F800001, 1)):
+        checked, bad, first = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint32()
+        rc = kernel_scale_sweep.block_scale_sweep(FMAXV[fmt], lo, hi, step, threads, ctypes.byref(checked),
+                                                  ctypes.byref(bad), ctypes.byref(first))
+        assert rc == 0 and checked.value == 3 * (-(-(hi - lo) // step))
+        assert bad.value == 0, f"[{lo:#x}, {hi:#x}) step {step}: {bad.value} mismatches, first A bits {first.value:#010x}"
+
+
 def test_block_scale_degenerate():
     for fmt in (O.E4M3, O.E5M2):
         assert O.block_scale(f32([0.0, -0.0, 0.0]), fmt) == (1.0, 1.0)

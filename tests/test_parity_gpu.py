@@ -635,16 +635,18 @@ def test_fp8_encode_exhaustive(fmt):
 
 @pytest.mark.parametrize("fmt", [O.E4M3, O.E5M2])
 def test_block_scale_exhaustive(fmt):
-    """The kernels' block scale and reciprocal (two correctly rounded FP32
-    divisions, degenerate blocks -> 1) for every finite non-negative FP32
-    block absmax A, including zero, subnormals and the thresholds where
-    A / FMAX underflows or FMAX / A overflows, against the oracle."""
+    """The kernels' block scale and reciprocal (FMA-corrected quotients that
+    must equal the correctly rounded FP32 divisions; degenerate blocks -> 1)
+    for every non-negative FP32 block absmax A up to +inf, including zero,
+    subnormals and the thresholds where A / FMAX underflows or FMAX / A
+    overflows, and NaN patterns, against the oracle."""
     from concurrent.futures import ThreadPoolExecutor
-    end = 0x7F800000
+    end = 0x7F800001                      # through +inf
     s_d = torch.empty(CHUNK, dtype=torch.float32, device=DEV)
     r_d = torch.empty(CHUNK, dtype=torch.float32, device=DEV)
-    for first in range(0, end, CHUNK):
-        n = min(CHUNK, end - first)
+    ranges = [(first, min(CHUNK, end - first)) for first in range(0, end, CHUNK)]
+    ranges += [(0x7F800001, 4096), (0x7FC00000, 4096), (0x7FFFF000, 4096)]   # NaNs
+    for first, n in ranges:
         log(f"block scale sweep fmt={fmt} first={first:#x}")
         rx.rxtest_block_scale_bits(first, n, FMTS[fmt], s_d, r_d)
         sync()
