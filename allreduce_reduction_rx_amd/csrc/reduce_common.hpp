@@ -17,23 +17,56 @@ template <> struct Elem<0> { static constexpr int kVE = 4; };  // FP32: 4 per 16
 template <> struct Elem<1> { static constexpr int kVE = 8; };  // BF16: 8 per 16 B
 
 // Fold vector `v` (16 bytes) of N sources; returns the narrowed 16 bytes.
-// NT: nontemporal source loads (data read once).
-template <int DT, int N, bool NT>
+// NT: nontemporal source loads (data read once). Every element is summed in
+// source order 0..N-1 in both loop orders: SM (source-major) adds each
+// source into all the elements as its load arrives, otherwise one element's
+// sum is completed at a time. The order only changes the instruction
+// schedule; measured on MI355X, source-major is faster for the tree step
+// (8 x 4 MiB BF16: 2.94 against 3.05 us) and element-major for the
+// decode-size flat reduce (8 x 512 KiB: 2.68 against 2.83 us).
+template <int DT, int N, bool NT, bool SM = false>
 __device__ __forceinline__ u32x4 fold_vec(const void* const* src, size_t v)
 {
     u32x4 x[N];
 #pragma unroll
     for (int r = 0; r < N; ++r)
         x[r] = NT ? ld16_stream(src[r], v) : ld16(src[r], v);
+    constexpr int VE = Elem<DT>::kVE;
+    float acc[VE];
     u32x4 out;
-    if constexpr (DT == 0) {
+    if constexpr (SM) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            float acc = bits_f32(x[0][k]);
+            if constexpr (DT == 0) {
+                acc[k] = bits_f32(x[0][k]);
+            } else {
+                acc[2 * k] = bf16_lo(x[0][k]);
+                acc[2 * k + 1] = bf16_hi(x[0][k]);
+            }
+        }
+#pragma unroll
+        for (int r = 1; r < N; ++r) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if constexpr (DT == 0) {
+                    acc[k] = acc[k] + bits_f32(x[r][k]);
+                } else {
+                    acc[2 * k] = acc[2 * k] + bf16_lo(x[r][k]);
+                    acc[2 * k + 1] = acc[2 * k + 1] + bf16_hi(x[r][k]);
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            out[k] = DT == 0 ? __builtin_bit_cast(uint32_t, acc[k]) : pack_bf16(acc[2 * k], acc[2 * k + 1]);
+    } else if constexpr (DT == 0) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float a = bits_f32(x[0][k]);
 #pragma unroll
             for (int r = 1; r < N; ++r)
-                acc = acc + bits_f32(x[r][k]);
-            out[k] = __builtin_bit_cast(uint32_t, acc);
+                a = a + bits_f32(x[r][k]);
+            out[k] = __builtin_bit_cast(uint32_t, a);
         }
     } else {
 #pragma unroll

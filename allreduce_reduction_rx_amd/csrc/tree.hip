@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void k_tree(TreeArgs a)
     // wave w takes vectors 32w .. 32w + 31, both halves the same ones
     const size_t vv = (gid / kWave) * (kWave / 2) + (size_t)(lane % (kWave / 2));
     for (size_t v = v0 + vv; v < v1; v += stride / 2) {
-        u32x4 y = fold_vec<DT, N, true>(a.src, v);
+        u32x4 y = fold_vec<DT, N, true, true>(a.src, v);
 #pragma unroll
         for (int j = 0; j < H; ++j)
             if (j < cnt)
