@@ -40,6 +40,7 @@ EXPORTED_SYMBOLS = (
     "rx_lp_reduce_scatter_chunk_bcast", "rx_lp_tree_chunk", "rx_allreduce_local",
     "rx_allreduce_local_workspace", "rx_allreduce_local_noalloc", "rxtest_block_scale_bits", "rxtest_fp8_encode_bits", "rxtest_fp8_decode", "rxtest_bf16_round_bits",
     "rxtest_group_max", "rxtest_stream", "rxtest_stream_sink_bytes", "rxtest_stream_mixed",
+    "rxtest_copy_streams",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -96,6 +97,7 @@ def lib() -> ctypes.CDLL:
             "rxtest_group_max": [_P, _SZ, _I, _P, _P],
             "rxtest_stream": [_I, _P, _P, _SZ, _I, _I, _P],
             "rxtest_stream_mixed": [_I, _PP, _I, _P, _SZ, _I, _I, _P],
+            "rxtest_copy_streams": [_PP, _PP, _I, _SZ, _SZ, _I, _I, _P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -444,3 +446,22 @@ def rxtest_stream_mixed(kind: int, srcs: Sequence, dst, src_bytes: int, wgs_per_
                                      dst.data_ptr(), src_bytes, wgs_per_cu,
                                      int(bool(nontemporal)), _stream(stream)),
            "rxtest_stream_mixed")
+
+
+def rxtest_copy_streams(srcs: Sequence, dsts: Sequence, offset_bytes: int, nbytes: int,
+                        lanes: int = 1, wg: int = 64, stream=None) -> None:
+    """The tree step's memory pattern without its arithmetic: bytes
+    [offset_bytes, offset_bytes + nbytes) of srcs[j] copied into dsts[j]."""
+    def size(t):
+        return t.numel() * t.element_size()
+    if len(srcs) != len(dsts):
+        raise ValueError("srcs and dsts must have the same length")
+    for name, ts in (("srcs", srcs), ("dsts", dsts)):
+        for k, t in enumerate(ts):
+            _gpu(t, f"{name}[{k}]")
+            if size(t) < offset_bytes + nbytes:
+                raise ValueError(f"{name}[{k}] must hold offset_bytes + nbytes")
+    _check(lib().rxtest_copy_streams(_ptr_array([t.data_ptr() for t in srcs]),
+                                     _ptr_array([t.data_ptr() for t in dsts]), len(srcs),
+                                     offset_bytes, nbytes, lanes, wg, _stream(stream)),
+           "rxtest_copy_streams")

@@ -168,6 +168,62 @@ __global__ __launch_bounds__(256) void k_mixed_narrow(MixedArgs a)
     }
 }
 
+// The tree step's memory pattern without its arithmetic: N streams copied,
+// src[j] -> dst[j] over the same range of 16-byte vectors [v0, v1): N reads
+// and N writes of the range, each stream its own allocation. LANES 1: one
+// lane per vector, its N loads, then its N stores; LANES 2: two lanes per
+// vector, the first half-wave copying streams 0..H-1 and the second H..N-1
+// (H = ceil(N / 2)). Nontemporal loads and stores, as in the tree step.
+struct StreamsArgs {
+    const void* src[kMaxSrc];
+    void* dst[kMaxSrc];
+    size_t v0, v1;
+};
+
+template <int N, int LANES>
+__global__ __launch_bounds__(256) void k_copy_streams(StreamsArgs a)
+{
+    const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    if constexpr (LANES == 1) {
+        for (size_t v = a.v0 + gid; v < a.v1; v += stride) {
+            u32x4 x[N];
+#pragma unroll
+            for (int r = 0; r < N; ++r) x[r] = ld16_stream(a.src[r], v);
+#pragma unroll
+            for (int j = 0; j < N; ++j) st16_stream(a.dst[j], v, x[j]);
+        }
+    } else {
+        constexpr int H = (N + 1) / 2;
+        const int lane = lane_id();
+        const int half = lane / (kWave / 2);
+        const int first = half ? H : 0;
+        const int cnt = half ? N - H : H;
+        const size_t vv = (gid / kWave) * (kWave / 2) + (size_t)(lane % (kWave / 2));
+        for (size_t v = a.v0 + vv; v < a.v1; v += stride / 2) {
+            u32x4 x[H];
+#pragma unroll
+            for (int r = 0; r < H; ++r)
+                if (r < cnt) x[r] = ld16_stream(a.src[first + r], v);
+#pragma unroll
+            for (int j = 0; j < H; ++j)
+                if (j < cnt) st16_stream(a.dst[first + j], v, x[j]);
+        }
+    }
+}
+
+using StreamsFn = void (*)(StreamsArgs);
+
+template <int LANES, int... I>
+constexpr std::array<StreamsFn, sizeof...(I)> streams_table(std::integer_sequence<int, I...>)
+{
+    return {{&k_copy_streams<I + 1, LANES>...}};
+}
+
+const std::array<StreamsFn, kMaxSrc> kCopyStreams[2] = {
+    streams_table<1>(std::make_integer_sequence<int, kMaxSrc>{}),
+    streams_table<2>(std::make_integer_sequence<int, kMaxSrc>{})};
+
 using MixedFn = void (*)(MixedArgs);
 
 template <bool NT, int... I>
@@ -244,6 +300,37 @@ rx_status_t rxtest_stream_mixed(int kind, const void* const* srcs, int nsrc, voi
     const unsigned grid = (unsigned)(rx::device_cu_count() * wgs_per_cu);
     void* params[] = {&a};
     const hipError_t e = hipLaunchKernel((const void*)fn, dim3(grid), dim3(256), params, 0, stream);
+    if (e != hipSuccess)
+        fprintf(stderr, "librx: launch failed: %s\n", hipGetErrorName(e));
+    return e == hipSuccess ? RX_OK : RX_ERR_HIP;
+}
+
+rx_status_t rxtest_copy_streams(const void* const* srcs, void* const* dsts, int n,
+                                size_t offset_bytes, size_t bytes, int lanes, int wg,
+                                hipStream_t stream)
+{
+    if (n < 1 || n > RX_MAX_SRC || (lanes != 1 && lanes != 2) || (wg != 64 && wg != 128 && wg != 256))
+        return RX_ERR_ARG;
+    if (!srcs || !dsts) return RX_ERR_NULL;
+    for (int j = 0; j < n; ++j)
+        if (!srcs[j] || !dsts[j]) return RX_ERR_NULL;
+    for (int j = 0; j < n; ++j)
+        if ((uintptr_t)srcs[j] % 16 || (uintptr_t)dsts[j] % 16) return RX_ERR_ALIGN;
+    if (offset_bytes % 16 || bytes % 16) return RX_ERR_ALIGN;
+    if (bytes == 0) return RX_OK;
+    rx::StreamsArgs a = {};
+    for (int j = 0; j < n; ++j) {
+        a.src[j] = srcs[j];
+        a.dst[j] = dsts[j];
+    }
+    a.v0 = offset_bytes / 16;
+    a.v1 = a.v0 + bytes / 16;
+    const size_t threads = (bytes / 16) * (size_t)lanes;
+    size_t grid = (threads + (size_t)wg - 1) / (size_t)wg;
+    if (grid > 65536) grid = 65536;   // grid-stride beyond
+    void* params[] = {&a};
+    const hipError_t e = hipLaunchKernel((const void*)rx::kCopyStreams[lanes - 1][n - 1],
+                                         dim3((unsigned)grid), dim3((unsigned)wg), params, 0, stream);
     if (e != hipSuccess)
         fprintf(stderr, "librx: launch failed: %s\n", hipGetErrorName(e));
     return e == hipSuccess ? RX_OK : RX_ERR_HIP;

@@ -37,6 +37,13 @@ kernel (captured in a HIP graph), divided by the launch count (`us`,
 hash, its average per-dispatch duration is reported beside it (`us_trace`,
 `frac_trace`): under the profiler each dispatch starts on an idle GPU, so at
 decode size the trace durations run longer than the back-to-back interval.
+
+Floors, timed the same way in the same run: `launch_floors` (an empty
+launch, a read and a copy of the decode message's 4 MiB, on one 1 GiB
+rotation) and the tree step's own memory pattern without its arithmetic
+(`tree_step_pattern_floor`, and cfg3's `pattern_floor`: each rank buffer's
+chunk copied into its own destination, the same 2N streams in the same
+allocations and rotation).
 """
 from __future__ import annotations
 
@@ -56,15 +63,20 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 METRIC = "effective HBM GB/s (% of MI355X peak) per reduce kernel; µs at 512 KB msg"
 ROTATE_BYTES = 2 << 30  # >= 8x the 256 MB Infinity Cache
 
-_REDUCE = ["reduce.hip", "rx_device.hpp"]
-_QUANT = ["quant.hip", "rx_device.hpp"]
-_DRR = ["drr.hpp", "drr.hip", "rx_device.hpp"]
+# the sources each measured kernel is built and launched from (a committed
+# profile's figures are used only while their hash is unchanged)
+_COMMON = ["rx_device.hpp", "rx_internal.hpp", "api.hip"]
+_FLAT = ["reduce.hip", "reduce_common.hpp"] + _COMMON
+_TREE = ["tree.hip", "reduce_common.hpp"] + _COMMON
+_QUANT = ["quant.hip"] + _COMMON
+_DRR = ["drr.hpp", "drr.hip", "drr_16x1.hip", "drr_8x2.hip", "drr_4x4.hip", "drr_4x1.hip"] + _COMMON
+_LP = ["allreduce_lp.hip", "quant.hip", "drr.hpp", "drr.hip"] + _COMMON
 KERNEL_SOURCES = {
-    "reduce_flat": _REDUCE, "tree_step": _REDUCE, "quant_fp8": _QUANT,
+    "reduce_flat": _FLAT, "tree_step": _TREE, "quant_fp8": _QUANT,
     "dequant_reduce_requant": _DRR, "drr_requant": _DRR, "drr_requant_hp": _DRR,
     "lp_tree_step": _DRR, "dequant_separate": _DRR, "lp_flat_sum": _DRR,
-    "allreduce_local_flat": _REDUCE, "allreduce_local_tree": _REDUCE,
-    "allreduce_local_lowprec": _QUANT + _DRR,
+    "allreduce_local_flat": _TREE, "allreduce_local_tree": _TREE,
+    "allreduce_local_lowprec": _LP,
 }
 
 
@@ -407,6 +419,12 @@ def step_workload(args, torch, rx, G, timer):
                                                                batches[i % nsets].tree_dsts)
              for i in range(reps)], f"{wname}/tree_step@rank{k}"), 3))
 
+    # ---- the tree step's memory pattern without its arithmetic ----
+    chunks = [rx.rx_tree_chunk(count, n, w.dtype, k) for k in range(n)]
+    tree_floor = tree_pattern_floor(rx, timer, lambda i: batches[i % nsets].srcs,
+                                    lambda i: batches[i % nsets].tree_dsts, chunks, e,
+                                    per_kernel["tree_step"]["launches"], wname)
+
     # ---- the flat reduce over the first k rank buffers, k = 1..N ----
     flat_by_nsrc = []
     for k in range(1, n + 1):
@@ -434,7 +452,7 @@ def step_workload(args, torch, rx, G, timer):
         "nsets": nsets, "per_batch_bytes": per_batch_bytes, "per_kernel": per_kernel,
         "by_rank": by_rank, "flat_by_nsrc": flat_by_nsrc, "tree_ok": tree_ok,
         "us_single": us_single, "us_events": us_events, "kernels": [k for k, _ in kernels],
-        "n_ar_sets": n_ar, "ar_set_bytes": ar_set_bytes,
+        "n_ar_sets": n_ar, "ar_set_bytes": ar_set_bytes, "tree_floor": tree_floor,
     }
     del batches, ar_bufs, ar_ws, base
     torch.cuda.synchronize()
@@ -501,6 +519,10 @@ def cfg_tree(torch, rx, G, timer):
     tree = entry(nbytes, med, reps, "tree", "tree_step", target=0.4)
     tree["us_by_rank"] = [round(x, 3) for x in by_rank]
     tree["statistic"] = "median over the 8 ranks"
+    chunks = [rx.rx_tree_chunk(count, n, w.dtype, k) for k in range(n)]
+    tree["pattern_floor"] = tree_pattern_floor(rx, timer, lambda i: sets[i % nsets][0],
+                                               lambda i: sets[i % nsets][1], chunks, e, reps, "tree")
+    tree["frac_of_pattern_floor"] = round(tree["pattern_floor"]["us"] / med, 4)
     fbytes = (n + 1) * count * e
     freps = auto_reps(fbytes, lo=100)
     flat_out = [torch.empty_like(base[0]) for _ in range(nsets)]
@@ -700,6 +722,26 @@ def stream_ceilings(torch, rx, timer):
     del src, dst, sink
     torch.cuda.empty_cache()
     return out
+
+
+def tree_pattern_floor(rx, timer, srcs_of, dsts_of, chunks, e, reps, tag):
+    """The tree step's memory pattern without its arithmetic: each rank
+    buffer's chunk copied into its own destination buffer (the same 2N
+    streams in the same allocations and rotation as the tree step, the chunk
+    following the rank as in the tree step's timing); best of one or two
+    lanes per 16-byte vector in 64- or 128-thread workgroups. The floor the
+    tree step's memory pattern sets, measured beside it."""
+    n = len(chunks)
+    best = None
+    for lanes, wg in ((1, 64), (1, 128), (2, 64), (2, 128)):
+        us = timer.us_per_launch(
+            [lambda i=i, lanes=lanes, wg=wg: rx.rxtest_copy_streams(
+                srcs_of(i), dsts_of(i), chunks[i % n][0] * e,
+                (chunks[i % n][1] - chunks[i % n][0]) * e, lanes, wg) for i in range(reps)],
+            f"floor/tree_streams@{tag}_lanes{lanes}wg{wg}")
+        if best is None or us < best[0]:
+            best = (us, lanes, wg)
+    return {"us": round(best[0], 3), "lanes": best[1], "wg": best[2]}
 
 
 def launch_floors(torch, rx, timer, in_bytes, reps=None):
@@ -985,6 +1027,7 @@ def main():
         "kernels": pk,
         "reduce_flat_us_by_nsrc": s["flat_by_nsrc"],
         "tree_step_by_rank_us": s["by_rank"],
+        "tree_step_pattern_floor": s["tree_floor"],
         "us_reduce_flat_single_launch": s["us_single"],
         "us_event_pair_alone": s["us_events"],
         "launch_floors": floors,

@@ -82,6 +82,20 @@ rx_status_t rxtest_stream_mixed(int kind, const void* const* srcs, int nsrc, voi
                                 size_t src_bytes, int wgs_per_cu, int nontemporal,
                                 hipStream_t stream);
 
+/* The tree step's memory pattern without its arithmetic (a floor for it):
+ * for j < n, bytes [offset_bytes, offset_bytes + bytes) of srcs[j] copied to
+ * the same range of dsts[j] -- n read and n write streams, each its own
+ * allocation. lanes 1: one lane per 16-byte vector (n loads, then n
+ * stores); lanes 2: two lanes per vector, each copying half of the streams.
+ * One thread per lane in workgroups of wg threads (64, 128 or 256), grid-
+ * stride beyond 65536 workgroups; nontemporal loads and stores. srcs and
+ * dsts are host arrays of device pointers (16-B aligned) whose buffers hold
+ * at least offset_bytes + bytes; offset_bytes and bytes are multiples of 16;
+ * a destination must not overlap a source. */
+rx_status_t rxtest_copy_streams(const void* const* srcs, void* const* dsts, int n,
+                                size_t offset_bytes, size_t bytes, int lanes, int wg,
+                                hipStream_t stream);
+
 /* Size in bytes of the read kernel's dst for this wgs_per_cu (0 if out of
  * range). */
 size_t rxtest_stream_sink_bytes(int wgs_per_cu);

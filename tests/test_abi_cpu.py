@@ -277,6 +277,19 @@ def test_stream_ceiling_validation():
     assert m(0, ptrs(FAKE, FAKE + 8), 2, FAKE, 1024, 1, 0, None) == ALIGN
     assert m(2, ptrs(FAKE), 1, FAKE, 1000, 1, 0, None) == ALIGN  # bytes % 16
     assert m(0, two, 2, FAKE, 0, 1, 0, None) == OK               # nothing to do
+    c = L.rxtest_copy_streams
+    d2 = ptrs(FAKE + 8192, FAKE + 12288)
+    assert c(two, d2, 0, 0, 1024, 1, 64, None) == ARG            # stream count
+    assert c(ptrs(*[FAKE] * 17), ptrs(*[FAKE] * 17), 17, 0, 1024, 1, 64, None) == ARG
+    assert c(two, d2, 2, 0, 1024, 3, 64, None) == ARG            # lanes
+    assert c(two, d2, 2, 0, 1024, 1, 96, None) == ARG            # workgroup size
+    assert c(None, d2, 2, 0, 1024, 1, 64, None) == NULL
+    assert c(two, None, 2, 0, 1024, 1, 64, None) == NULL
+    assert c(two, ptrs(FAKE, 0), 2, 0, 1024, 1, 64, None) == NULL
+    assert c(two, ptrs(FAKE, FAKE + 8), 2, 0, 1024, 1, 64, None) == ALIGN
+    assert c(two, d2, 2, 8, 1024, 1, 64, None) == ALIGN          # offset % 16
+    assert c(two, d2, 2, 0, 1000, 2, 128, None) == ALIGN         # bytes % 16
+    assert c(two, d2, 2, 16, 0, 2, 256, None) == OK              # nothing to do
 
 
 def test_binding_fails_loudly_without_the_library(tmp_path):

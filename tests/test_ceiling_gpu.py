@@ -84,3 +84,25 @@ def test_stream_mixed(nbytes, wgs, nt):
             want = words[:, 0] ^ words[:, 1] ^ words[:, 2] ^ words[:, 3]
         assert np.array_equal(out.t.cpu().numpy(), want.astype(np.uint32).ravel().view(np.uint8)), k
         assert out.guards_intact()
+
+
+@pytest.mark.parametrize("n", [1, 3, 8, 16])
+@pytest.mark.parametrize("lanes,wg", [(1, 64), (2, 64), (1, 256), (2, 128)])
+def test_copy_streams(n, lanes, wg):
+    """The tree step's memory pattern without arithmetic: each stream's byte
+    range copied into its own destination, nothing else written."""
+    total = (1 << 20) + 4096
+    for off, nbytes in ((0, 16), (4096, 65536 * 16), (48, (1 << 20) - 64), (16, total - 32)):
+        log(f"copy streams n={n} lanes={lanes} wg={wg} off={off} bytes={nbytes}")
+        hosts = [random_bytes(total, 1000 * n + 17 * off + r) for r in range(n)]
+        srcs = [torch.from_numpy(h).to(DEV) for h in hosts]
+        dsts = [Guarded(total, torch.uint8) for _ in range(n)]
+        before = [d.t.clone() for d in dsts]
+        rx.rxtest_copy_streams(srcs, [d.t for d in dsts], off, nbytes, lanes, wg)
+        torch.cuda.synchronize()
+        for j in range(n):
+            got = dsts[j].t.cpu().numpy()
+            want = before[j].cpu().numpy()
+            want[off:off + nbytes] = hosts[j][off:off + nbytes]
+            assert np.array_equal(got, want), f"stream {j}"
+            assert dsts[j].guards_intact()
