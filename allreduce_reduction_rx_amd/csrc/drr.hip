@@ -31,10 +31,17 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     const bool codes_only = requant && !all && a.out_hp == nullptr;
     // chunk layout (codes per lane per chunk, chunks per lane); block / CPC <= 64
     int cpc = 16, u = 1;
+    bool staged = false;
     if (small) {
         if (a.block <= 256) cpc = 4;
     } else if (fp32_out) {
-        if (a.block <= 256) { cpc = 4; u = 4; }
+        // FP32 output from several sources: 16 codes per lane (16-byte code
+        // loads) with the output staged through LDS into contiguous 1 KiB
+        // stores (8 x 16M codes E4M3/128 with FP32 output: 42.1 -> 37.8 us
+        // against 4 x 4); one source keeps 4 x 4, which measured the same
+        // as staging there
+        if (nsrc >= 2) staged = true;
+        else if (a.block <= 256) { cpc = 4; u = 4; }
     } else if (a.block <= 512 && !codes_only) {
         // codes only (one destination or a push to N) keep 16 x 1: 16-byte
         // code stores measured 7-13% faster at 8 x 4M..64M codes with one
@@ -61,7 +68,7 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     // contiguous range (8 x 4M codes E4M3/128: 7.1 us against 8.2 us with
     // two per CU; 8 x 16M: 25.4 us, 8 x 64M: 100.7 us against 105.1 us in
     // plain order).
-    const bool single_codes = !small && r == kDrrRequant && cpc == 16;
+    const bool single_codes = !small && r == kDrrRequant && cpc == 16 && codes_only;
     const bool few = single_codes && tiles < (size_t)32 * cus;
     if (few)
         pol.max_wgs_per_cu = 4;
@@ -73,7 +80,7 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     // destination) meet in one L2. Measured: decode-size 8% faster; large
     // pushes to N destinations 3-8% and the FP32-output layout 2% faster;
     // no gain for the other large layouts, which keep the plain order.
-    arg.xcd_ranges = (small || medium || r == kDrrRequantPush || (cpc == 4 && u == 4) ||
+    arg.xcd_ranges = (small || medium || r == kDrrRequantPush || (cpc == 4 && u == 4) || staged ||
                       (single_codes && !few)) ? 1 : 0;
     if (small && blk.x == (unsigned)kWave) {
         // Decode-size launches (one tile per 64-thread workgroup): each XCD
@@ -90,11 +97,12 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
         grid = dim3((unsigned)(kXcds * range));
     }
     void* params[] = {&arg};
-    const DrrFn fn = cpc == 4 ? (u == 4 ? drr_fns_4x4().fn[fmt][r][nsrc - 1] : drr_fns_4x1().fn[fmt][r][nsrc - 1])
+    const DrrFn fn = staged   ? drr_fns_16x1_staged().fn[fmt][r][nsrc - 1]
+                   : cpc == 4 ? (u == 4 ? drr_fns_4x4().fn[fmt][r][nsrc - 1] : drr_fns_4x1().fn[fmt][r][nsrc - 1])
                    : cpc == 8 ? drr_fns_8x2().fn[fmt][r][nsrc - 1] : drr_fns_16x1().fn[fmt][r][nsrc - 1];
     char what[64] = "k_drr";
     if (debug_enabled())
-        snprintf(what, sizeof what, "k_drr mode %d layout %dx%d", r, cpc, u);
+        snprintf(what, sizeof what, "k_drr mode %d layout %dx%d%s", r, cpc, u, staged ? " staged" : "");
     return launch_logged(what, (const void*)fn, grid, blk, params, s);
 }
 

@@ -30,6 +30,7 @@ const DrrFns& drr_fns_16x1();
 const DrrFns& drr_fns_8x2();
 const DrrFns& drr_fns_4x4();
 const DrrFns& drr_fns_4x1();
+const DrrFns& drr_fns_16x1_staged();
 
 namespace drr_detail {
 
@@ -38,9 +39,12 @@ namespace drr_detail {
 // CPC consecutive codes, chunk u at tile offset (u * 64 + l) * CPC. Every
 // load and store instruction then covers one contiguous run (64 lanes x CPC
 // codes, or their 2- or 4-byte outputs). Layouts used:
-//   CPC 16, U 1: dwordx4 code loads (any block size);
+//   CPC 16, U 1: dwordx4 code loads (any block size); code-only output, and
+//                FP32 output from several sources with the output staged
+//                through LDS (stage_fp32) into contiguous stores;
 //   CPC  8, U 2: BF16 output, 16-byte stores contiguous across the wave;
-//   CPC  4, U 4: FP32 output, 16-byte stores contiguous across the wave;
+//   CPC  4, U 4: FP32 output from one source, 16-byte stores contiguous
+//                across the wave;
 //   CPC  4, U 1: decode-size messages (4x the waves, short serial chains).
 // A block spans block / CPC lanes of one chunk; the launcher only picks
 // layouts with block / CPC <= 64.
@@ -186,6 +190,45 @@ __device__ __forceinline__ void store_hp(void* out, bool bf16, size_t c, size_t 
     }
 }
 
+// FP32 output of a whole 16 x 1 tile staged through LDS: lane l's 16 values
+// become row l of the wave's stage (rows of 5 16-byte slots, one of them
+// padding against bank conflicts); store instruction u then takes floats
+// [256 u + 4 l, +4) of the tile -- row 16 u + l / 4, slot l % 4 -- so each
+// of the tile's four stores writes one contiguous 1 KiB run (nontemporal),
+// where the unstaged 16 x 1 layout writes four strided 16-byte pieces per
+// lane. The stage belongs to one wave; the waits keep the previous tile's
+// reads before this tile's writes and the writes before the reads.
+constexpr int kStageSlots = 64 * 5;
+
+__device__ __forceinline__ void stage_wait()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ void stage_fp32(u32x4* stage, int lane, const float* h, u32x4* piece)
+{
+    stage_wait();
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        stage[lane * 5 + q] = u32x4{__builtin_bit_cast(uint32_t, h[4 * q]), __builtin_bit_cast(uint32_t, h[4 * q + 1]),
+                                    __builtin_bit_cast(uint32_t, h[4 * q + 2]),
+                                    __builtin_bit_cast(uint32_t, h[4 * q + 3])};
+    stage_wait();
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        piece[u] = stage[(u * 16 + lane / 4) * 5 + lane % 4];
+}
+
+// The four staged pieces into one output, whose tile starts at 16-byte
+// vector f0.
+__device__ __forceinline__ void store_staged(void* out, size_t f0, int lane, const u32x4* piece)
+{
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        st16_stream(out, f0 + (size_t)u * kWave + lane, piece[u]);
+}
+
 // OUT (requantization only): kDrrRequant -> out_codes[0] / out_scales[0]
 // (+ out_hp); kDrrRequantPush -> the codes and scales to N destinations, one
 // per rank (the low-precision tree step's push); kDrrRequantAll -> only the
@@ -194,10 +237,15 @@ __device__ __forceinline__ void store_hp(void* out, bool bf16, size_t c, size_t 
 // One wave tile of k_drr. WHOLE: every chunk of the tile lies inside the
 // range (all tiles but a ragged last one); that instance has no per-lane
 // bounds branches around its loads and stores.
-template <int F, int N, bool REQUANT, int CPC, int U, int OUT, bool WHOLE>
+// STAGE (16 x 1 only): the high-precision output is FP32 and whole tiles
+// write it through `stage` (stage_fp32); a partial tile writes it directly.
+template <int F, int N, bool REQUANT, int CPC, int U, int OUT, bool WHOLE, bool STAGE>
 __device__ __forceinline__ void drr_tile(const DrrArgs& a, uint32_t t, int lane, size_t c0,
-                                         size_t count, int bshift, int lpb)
+                                         size_t count, int bshift, int lpb, u32x4* stage)
 {
+    static_assert(!STAGE || (CPC == 16 && U == 1), "staged output: 16 x 1 layout");
+    constexpr bool kStaged = STAGE && WHOLE;
+    const size_t f0 = (c0 + (size_t)t * kWave) * 4;   // staged: the tile's first FP32 vector
     size_t c[U], e[U], b[U];
     bool whole[U], valid[U];
 #pragma unroll
@@ -237,7 +285,13 @@ __device__ __forceinline__ void drr_tile(const DrrArgs& a, uint32_t t, int lane,
         }
 
         if constexpr (!REQUANT) {
-            store_hp<CPC>(a.out_hp, a.hp_bf16 != 0, c[u], e[u], count, whole[u], S);
+            if constexpr (kStaged) {
+                u32x4 piece[4];
+                stage_fp32(stage, lane, S, piece);
+                store_staged(a.out_hp, f0, lane, piece);
+            } else {
+                store_hp<CPC>(a.out_hp, a.hp_bf16 != 0, c[u], e[u], count, whole[u], S);
+            }
             continue;
         }
 
@@ -274,23 +328,42 @@ __device__ __forceinline__ void drr_tile(const DrrArgs& a, uint32_t t, int lane,
         if constexpr (OUT == kDrrRequantAll) {
             float h[CPC];
             dequant<F, CPC>(q, s2, h);
+            if constexpr (kStaged) {
+                u32x4 piece[4];
+                stage_fp32(stage, lane, h, piece);
 #pragma unroll
-            for (int j = 0; j < N; ++j)
-                store_hp<CPC>(a.out_hps[j], a.hp_bf16 != 0, c[u], e[u], count, whole[u], h);
+                for (int j = 0; j < N; ++j)
+                    store_staged(a.out_hps[j], f0, lane, piece);
+            } else {
+#pragma unroll
+                for (int j = 0; j < N; ++j)
+                    store_hp<CPC>(a.out_hps[j], a.hp_bf16 != 0, c[u], e[u], count, whole[u], h);
+            }
         } else if (a.out_hp) {
             float h[CPC];
             dequant<F, CPC>(q, s2, h);
-            store_hp<CPC>(a.out_hp, a.hp_bf16 != 0, c[u], e[u], count, whole[u], h);
+            if constexpr (kStaged) {
+                u32x4 piece[4];
+                stage_fp32(stage, lane, h, piece);
+                store_staged(a.out_hp, f0, lane, piece);
+            } else {
+                store_hp<CPC>(a.out_hp, a.hp_bf16 != 0, c[u], e[u], count, whole[u], h);
+            }
         }
     }
 }
 
-template <int F, int N, bool REQUANT, int CPC, int U, int OUT>
+template <int F, int N, bool REQUANT, int CPC, int U, int OUT, bool STAGE = false>
 __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
 {
     const int lane = lane_id();
     const uint32_t wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t waves_per_wg = blockDim.x / kWave;
+    u32x4* stage = nullptr;
+    if constexpr (STAGE) {
+        __shared__ u32x4 stage_mem[256 / kWave][kStageSlots];   // one region per wave
+        stage = stage_mem[wave_in_wg];
+    }
     const size_t count = a.hi;                                    // end of the range
     constexpr size_t kTile = (size_t)kWave * CPC * U;             // codes per wave tile
     const uint32_t ntiles = (uint32_t)((a.hi - a.lo + kTile - 1) / kTile);
@@ -313,32 +386,32 @@ __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
 
     for (uint32_t t = wave; t < ntiles; t += step) {
         if (a.lo + ((size_t)t + 1) * kTile <= count)
-            drr_tile<F, N, REQUANT, CPC, U, OUT, true>(a, t, lane, c0, count, bshift, lpb);
+            drr_tile<F, N, REQUANT, CPC, U, OUT, true, STAGE>(a, t, lane, c0, count, bshift, lpb, stage);
         else
-            drr_tile<F, N, REQUANT, CPC, U, OUT, false>(a, t, lane, c0, count, bshift, lpb);
+            drr_tile<F, N, REQUANT, CPC, U, OUT, false, STAGE>(a, t, lane, c0, count, bshift, lpb, stage);
     }
 }
 
 
-template <int F, bool R, int CPC, int U, int OUT, int... I>
+template <int F, bool R, int CPC, int U, int OUT, bool STAGE, int... I>
 void fill_row(DrrFn* row, std::integer_sequence<int, I...>)
 {
-    ((row[I] = &k_drr<F, I + 1, R, CPC, U, OUT>), ...);
+    ((row[I] = &k_drr<F, I + 1, R, CPC, U, OUT, STAGE>), ...);
 }
 
-template <int CPC, int U>
+template <int CPC, int U, bool STAGE = false>
 DrrFns make_fns()
 {
     DrrFns t{};
     const auto seq = std::make_integer_sequence<int, kMaxSrc>{};
-    fill_row<0, false, CPC, U, kDrrSum>(t.fn[0][kDrrSum], seq);
-    fill_row<0, true, CPC, U, kDrrRequant>(t.fn[0][kDrrRequant], seq);
-    fill_row<0, true, CPC, U, kDrrRequantPush>(t.fn[0][kDrrRequantPush], seq);
-    fill_row<0, true, CPC, U, kDrrRequantAll>(t.fn[0][kDrrRequantAll], seq);
-    fill_row<1, false, CPC, U, kDrrSum>(t.fn[1][kDrrSum], seq);
-    fill_row<1, true, CPC, U, kDrrRequant>(t.fn[1][kDrrRequant], seq);
-    fill_row<1, true, CPC, U, kDrrRequantPush>(t.fn[1][kDrrRequantPush], seq);
-    fill_row<1, true, CPC, U, kDrrRequantAll>(t.fn[1][kDrrRequantAll], seq);
+    fill_row<0, false, CPC, U, kDrrSum, STAGE>(t.fn[0][kDrrSum], seq);
+    fill_row<0, true, CPC, U, kDrrRequant, STAGE>(t.fn[0][kDrrRequant], seq);
+    fill_row<0, true, CPC, U, kDrrRequantPush, STAGE>(t.fn[0][kDrrRequantPush], seq);
+    fill_row<0, true, CPC, U, kDrrRequantAll, STAGE>(t.fn[0][kDrrRequantAll], seq);
+    fill_row<1, false, CPC, U, kDrrSum, STAGE>(t.fn[1][kDrrSum], seq);
+    fill_row<1, true, CPC, U, kDrrRequant, STAGE>(t.fn[1][kDrrRequant], seq);
+    fill_row<1, true, CPC, U, kDrrRequantPush, STAGE>(t.fn[1][kDrrRequantPush], seq);
+    fill_row<1, true, CPC, U, kDrrRequantAll, STAGE>(t.fn[1][kDrrRequantAll], seq);
     return t;
 }
 
