@@ -264,9 +264,25 @@ __device__ __forceinline__ void drr_tile(const DrrArgs& a, uint32_t t, int lane,
         const uint8_t* cp = static_cast<const uint8_t*>(a.codes[r]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            // the partial last tile loads byte by byte in every lane (no
-            // branches, one wait for all sources)
-            x[r][u] = load_chunk<CPC>(cp, c[u], e[u], count, WHOLE);
+            if constexpr (WHOLE || CPC * U == 4) {
+                // whole tiles; and the decode-size layout's partial tile, byte
+                // by byte in every lane (4 loads per source, no branches, one
+                // wait for all sources)
+                x[r][u] = load_chunk<CPC>(cp, c[u], e[u], count, WHOLE);
+            } else {
+                // a large layout's partial tile: whole chunks load as vectors
+                // and only the chunk that straddles the end byte by byte
+                // (byte loads in every lane would hold CPC x U x N registers
+                // for the whole kernel)
+                if (whole[u])
+                    x[r][u] = load_chunk<CPC>(cp, c[u], e[u], count, true);
+                else if (valid[u])
+                    x[r][u] = load_chunk<CPC>(cp, c[u], e[u], count, false);
+                else {
+#pragma unroll
+                    for (int q = 0; q < CPC / 4; ++q) x[r][u].w[q] = 0u;
+                }
+            }
             sc[r][u] = valid[u] ? a.scales[r][b[u]] : 0.0f;
         }
     }
