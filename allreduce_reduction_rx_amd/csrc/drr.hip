@@ -9,9 +9,9 @@ namespace {
 
 // One wave per tile (64 threads per work item). Large messages: 256-thread
 // workgroups, at most 2 per CU (a narrow HBM access window measured best on
-// MI355X), 4 for the FP32-output layout, whose 4 chunks per lane keep fewer
-// bytes in flight per wave; decode-size messages: one tile per wave over
-// every CU.
+// MI355X), 4 for the one-source FP32-output layout (4 x 4), whose 4-byte
+// code loads keep fewer bytes in flight per wave; decode-size messages: one
+// tile per wave over every CU.
 LaunchPolicy policy_drr() { return {64u, 256u, 2u}; }
 LaunchPolicy policy_drr_fp32_out() { return {64u, 256u, 4u}; }
 // One source (the separate dequantization): each wave reads 1/N of the bytes

@@ -25,9 +25,10 @@ namespace {
 // Quantizer
 // ---------------------------------------------------------------------------
 
-// A wave processes tiles of U loads per lane (U x 1 KiB per tile): U = 4 for
-// large messages (more bytes in flight per wave), U = the loads per block
-// (usually 1) for decode-size messages (4x the waves, shorter serial chains).
+// A wave processes tiles of U loads per lane (U x 1 KiB per tile): U = 4 or 8
+// for large messages (more bytes in flight per wave; launch_quant picks by
+// size), U = the loads per block (usually 1) for decode-size messages (4x the
+// waves, shorter serial chains).
 template <int DT, int F, int BLOCK, int U>
 struct QuantShape {
     static constexpr int kVE = DT == 0 ? 4 : 8;          // elements per 16-B vector

@@ -125,7 +125,7 @@ rx_status_t rx_tree_chunk(size_t count, int nsrc, rx_dtype_t dtype, int rank,
  * types"). The pages do not give the encoding; this library fixes:
  *   block b = elements [b*block, min((b+1)*block, count)) of each source,
  *   A = max |x| over the block,
- *   s = A / FMAX, r = FMAX / A (each one correctly rounded FP32 division),
+ *   s = A / FMAX, r = FMAX / A (each the correctly rounded FP32 quotient),
  *   (A == 0, s == 0 or r not finite: s = r = 1),
  *   code_i = OCP FP8 of fl32(x_i * r), round to nearest even, saturating.
  *
