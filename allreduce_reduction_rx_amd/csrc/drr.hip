@@ -32,26 +32,76 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     // chunk layout (codes per lane per chunk, chunks per lane); block / CPC <= 64
     int cpc = 16, u = 1;
     bool staged = false;
+    const bool hp_out = a.out_hp != nullptr || all;
     if (small) {
         if (a.block <= 256) cpc = 4;
+    } else if (hp_out && nsrc >= 2) {
+        // FP32 or BF16 output from several sources: 16 codes per lane
+        // (16-byte code loads) with the output staged through LDS into
+        // contiguous 1 KiB stores. 8 x 16M codes E4M3/128 with FP32 output:
+        // 42.1 -> 37.8 us against 4 x 4; 8 x 64M codes E5M2/256 with BF16
+        // output: 127.5 -> 120.6 us against 8 x 2
+        staged = true;
     } else if (fp32_out) {
-        // FP32 output from several sources: 16 codes per lane (16-byte code
-        // loads) with the output staged through LDS into contiguous 1 KiB
-        // stores (8 x 16M codes E4M3/128 with FP32 output: 42.1 -> 37.8 us
-        // against 4 x 4); one source keeps 4 x 4, which measured the same
-        // as staging there
-        if (nsrc >= 2) staged = true;
-        else if (a.block <= 256) { cpc = 4; u = 4; }
+        // one source (the separate dequantization): 4 x 4 measured the same
+        // as staging
+        if (a.block <= 256) { cpc = 4; u = 4; }
     } else if (a.block <= 512 && !codes_only) {
-        // codes only (one destination or a push to N) keep 16 x 1: 16-byte
-        // code stores measured 7-13% faster at 8 x 4M..64M codes with one
-        // destination and 1-3% with N
+        // BF16 output from one source; codes only (one destination or a
+        // push to N) keep 16 x 1: 16-byte code stores measured 7-13% faster
+        // at 8 x 4M..64M codes with one destination and 1-3% with N
         cpc = 8;
         u = 2;
     }
     const size_t tile = (size_t)kWave * cpc * u;
     const size_t tiles = (len + tile - 1) / tile;
     const int r = !requant ? kDrrSum : all ? kDrrRequantAll : a.nout > 1 ? kDrrRequantPush : kDrrRequant;
+    if (staged) {
+        // Whole tiles of 1024 codes in the staged kernel, two 256-thread
+        // workgroups per CU, each XCD a contiguous range up to 128 tiles per
+        // CU (8 x 16M codes: 37.8 against 39.1 us in plain order) and plain
+        // order above (8 x 256M codes E5M2/256 with BF16 output: 513 against
+        // 524 us); a ragged remainder (less than one tile) in the unstaged
+        // 16 x 1 kernel, launched after it.
+        const size_t whole = len / tile;
+        hipError_t e = hipSuccess;
+        if (whole) {
+            dim3 grid, blk;
+            launch_geometry(whole * kWave, false, policy_drr(), grid, blk);
+            // every pointer offset to the start of the range: the staged
+            // kernel runs over [0, whole * 1024)
+            DrrArgs arg = a;
+            const size_t esz = a.hp_bf16 ? 2 : 4;
+            const size_t blk0 = a.lo / (size_t)a.block;   // lo is a block multiple
+            for (int j = 0; j < nsrc; ++j) {
+                arg.codes[j] = static_cast<const uint8_t*>(a.codes[j]) + a.lo;
+                arg.scales[j] = a.scales[j] + blk0;
+            }
+            for (int j = 0; j < kMaxSrc; ++j) {
+                if (a.out_codes[j]) arg.out_codes[j] = static_cast<uint8_t*>(a.out_codes[j]) + a.lo;
+                if (a.out_scales[j]) arg.out_scales[j] = a.out_scales[j] + blk0;
+                if (a.out_hps[j]) arg.out_hps[j] = static_cast<uint8_t*>(a.out_hps[j]) + a.lo * esz;
+            }
+            if (a.out_hp) arg.out_hp = static_cast<uint8_t*>(a.out_hp) + a.lo * esz;
+            arg.lo = 0;
+            arg.hi = whole * tile;
+            arg.xcd_ranges = whole <= (size_t)128 * cus ? 1 : 0;
+            void* params[] = {&arg};
+            e = launch_logged("k_drr_staged", (const void*)drr_fns_16x1_staged(a.hp_bf16).fn[fmt][r][nsrc - 1],
+                              grid, blk, params, s);
+            if (e != hipSuccess)
+                return e;
+        }
+        if (len % tile) {
+            DrrArgs arg = a;
+            arg.lo = a.lo + whole * tile;      // a multiple of 1024, so of the block
+            arg.xcd_ranges = 0;
+            void* params[] = {&arg};
+            e = launch_logged("k_drr (ragged remainder)", (const void*)drr_fns_16x1().fn[fmt][r][nsrc - 1],
+                              dim3(1), dim3(kWave), params, s);
+        }
+        return e;
+    }
     LaunchPolicy pol = (cpc == 4 && u == 4) ? policy_drr_fp32_out()
                      : nsrc == 1            ? policy_drr_one_source()
                                             : policy_drr();
@@ -80,7 +130,7 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     // destination) meet in one L2. Measured: decode-size 8% faster; large
     // pushes to N destinations 3-8% and the FP32-output layout 2% faster;
     // no gain for the other large layouts, which keep the plain order.
-    arg.xcd_ranges = (small || medium || r == kDrrRequantPush || (cpc == 4 && u == 4) || staged ||
+    arg.xcd_ranges = (small || medium || r == kDrrRequantPush || (cpc == 4 && u == 4) ||
                       (single_codes && !few)) ? 1 : 0;
     if (small && blk.x == (unsigned)kWave) {
         // Decode-size launches (one tile per 64-thread workgroup): each XCD
@@ -97,12 +147,11 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
         grid = dim3((unsigned)(kXcds * range));
     }
     void* params[] = {&arg};
-    const DrrFn fn = staged   ? drr_fns_16x1_staged().fn[fmt][r][nsrc - 1]
-                   : cpc == 4 ? (u == 4 ? drr_fns_4x4().fn[fmt][r][nsrc - 1] : drr_fns_4x1().fn[fmt][r][nsrc - 1])
+    const DrrFn fn = cpc == 4 ? (u == 4 ? drr_fns_4x4().fn[fmt][r][nsrc - 1] : drr_fns_4x1().fn[fmt][r][nsrc - 1])
                    : cpc == 8 ? drr_fns_8x2().fn[fmt][r][nsrc - 1] : drr_fns_16x1().fn[fmt][r][nsrc - 1];
     char what[64] = "k_drr";
     if (debug_enabled())
-        snprintf(what, sizeof what, "k_drr mode %d layout %dx%d%s", r, cpc, u, staged ? " staged" : "");
+        snprintf(what, sizeof what, "k_drr mode %d layout %dx%d", r, cpc, u);
     return launch_logged(what, (const void*)fn, grid, blk, params, s);
 }
 

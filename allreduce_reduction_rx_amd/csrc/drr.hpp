@@ -30,7 +30,8 @@ const DrrFns& drr_fns_16x1();
 const DrrFns& drr_fns_8x2();
 const DrrFns& drr_fns_4x4();
 const DrrFns& drr_fns_4x1();
-const DrrFns& drr_fns_16x1_staged();
+// Staged 16 x 1 kernels for whole tiles, [hp_bf16]
+const DrrFns& drr_fns_16x1_staged(int hp_bf16);
 
 namespace drr_detail {
 
@@ -40,9 +41,10 @@ namespace drr_detail {
 // load and store instruction then covers one contiguous run (64 lanes x CPC
 // codes, or their 2- or 4-byte outputs). Layouts used:
 //   CPC 16, U 1: dwordx4 code loads (any block size); code-only output, and
-//                FP32 output from several sources with the output staged
-//                through LDS (stage_fp32) into contiguous stores;
-//   CPC  8, U 2: BF16 output, 16-byte stores contiguous across the wave;
+//                (k_drr_staged) FP32 or BF16 output from several sources with
+//                the output staged through LDS into contiguous stores;
+//   CPC  8, U 2: BF16 output from one source, 16-byte stores contiguous
+//                across the wave;
 //   CPC  4, U 4: FP32 output from one source, 16-byte stores contiguous
 //                across the wave;
 //   CPC  4, U 1: decode-size messages (4x the waves, short serial chains).
@@ -190,14 +192,15 @@ __device__ __forceinline__ void store_hp(void* out, bool bf16, size_t c, size_t 
     }
 }
 
-// FP32 output of a whole 16 x 1 tile staged through LDS: lane l's 16 values
-// become row l of the wave's stage (rows of 5 16-byte slots, one of them
-// padding against bank conflicts); store instruction u then takes floats
-// [256 u + 4 l, +4) of the tile -- row 16 u + l / 4, slot l % 4 -- so each
-// of the tile's four stores writes one contiguous 1 KiB run (nontemporal),
-// where the unstaged 16 x 1 layout writes four strided 16-byte pieces per
-// lane. The stage belongs to one wave; the waits keep the previous tile's
-// reads before this tile's writes and the writes before the reads.
+// High-precision output of a whole 16 x 1 tile staged through LDS: lane l's
+// 16 values, as SL = 4 (FP32) or 2 (BF16) 16-byte slots, become row l of the
+// wave's stage (rows of SL + 1 slots, one of them padding against bank
+// conflicts); store instruction u then takes slot u * 64 + l of the tile --
+// row u * 64 / SL + l / SL, slot l % SL -- so each of the tile's SL stores
+// writes one contiguous 1 KiB run (nontemporal), where the unstaged 16 x 1
+// layout writes strided 16-byte pieces. The stage belongs to one wave; the
+// waits keep the previous tile's reads before this tile's writes and the
+// writes before the reads.
 constexpr int kStageSlots = 64 * 5;
 
 __device__ __forceinline__ void stage_wait()
@@ -206,27 +209,50 @@ __device__ __forceinline__ void stage_wait()
     __builtin_amdgcn_wave_barrier();
 }
 
-__device__ __forceinline__ void stage_fp32(u32x4* stage, int lane, const float* h, u32x4* piece)
+template <bool BF16>
+__device__ __forceinline__ void stage_hp(u32x4* stage, int lane, const float* h, u32x4* piece)
 {
+    constexpr int SL = BF16 ? 2 : 4;
     stage_wait();
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        stage[lane * 5 + q] = u32x4{__builtin_bit_cast(uint32_t, h[4 * q]), __builtin_bit_cast(uint32_t, h[4 * q + 1]),
-                                    __builtin_bit_cast(uint32_t, h[4 * q + 2]),
-                                    __builtin_bit_cast(uint32_t, h[4 * q + 3])};
+    for (int q = 0; q < SL; ++q) {
+        u32x4 v;
+        if constexpr (BF16) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] = pack_bf16(h[8 * q + 2 * k], h[8 * q + 2 * k + 1]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] = __builtin_bit_cast(uint32_t, h[4 * q + k]);
+        }
+        stage[lane * (SL + 1) + q] = v;
+    }
     stage_wait();
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-        piece[u] = stage[(u * 16 + lane / 4) * 5 + lane % 4];
+    for (int u = 0; u < SL; ++u)
+        piece[u] = stage[(u * (kWave / SL) + lane / SL) * (SL + 1) + lane % SL];
 }
 
-// The four staged pieces into one output, whose tile starts at 16-byte
-// vector f0.
-__device__ __forceinline__ void store_staged(void* out, size_t f0, int lane, const u32x4* piece)
+// The SL staged pieces into one output, whose tile starts at 16-byte vector
+// v0 (FP32: 4 per 16 codes, BF16: 2).
+template <bool BF16>
+__device__ __forceinline__ void store_staged(void* out, size_t v0, int lane, const u32x4* piece)
 {
+    constexpr int SL = BF16 ? 2 : 4;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-        st16_stream(out, f0 + (size_t)u * kWave + lane, piece[u]);
+    for (int u = 0; u < SL; ++u)
+        st16_stream(out, v0 + (size_t)u * kWave + lane, piece[u]);
+}
+
+// Stage a whole tile's output once and write it to NOUT outputs.
+template <int NOUT, bool BF16>
+__device__ __forceinline__ void staged_out(void* const* outs, size_t c_tile, u32x4* stage, int lane,
+                                           const float* h)
+{
+    u32x4 piece[4];
+    stage_hp<BF16>(stage, lane, h, piece);
+#pragma unroll
+    for (int j = 0; j < NOUT; ++j)
+        store_staged<BF16>(outs[j], c_tile * (BF16 ? 2 : 4), lane, piece);
 }
 
 // OUT (requantization only): kDrrRequant -> out_codes[0] / out_scales[0]
@@ -237,15 +263,10 @@ __device__ __forceinline__ void store_staged(void* out, size_t f0, int lane, con
 // One wave tile of k_drr. WHOLE: every chunk of the tile lies inside the
 // range (all tiles but a ragged last one); that instance has no per-lane
 // bounds branches around its loads and stores.
-// STAGE (16 x 1 only): the high-precision output is FP32 and whole tiles
-// write it through `stage` (stage_fp32); a partial tile writes it directly.
-template <int F, int N, bool REQUANT, int CPC, int U, int OUT, bool WHOLE, bool STAGE>
+template <int F, int N, bool REQUANT, int CPC, int U, int OUT, bool WHOLE>
 __device__ __forceinline__ void drr_tile(const DrrArgs& a, uint32_t t, int lane, size_t c0,
-                                         size_t count, int bshift, int lpb, u32x4* stage)
+                                         size_t count, int bshift, int lpb)
 {
-    static_assert(!STAGE || (CPC == 16 && U == 1), "staged output: 16 x 1 layout");
-    constexpr bool kStaged = STAGE && WHOLE;
-    const size_t f0 = (c0 + (size_t)t * kWave) * 4;   // staged: the tile's first FP32 vector
     size_t c[U], e[U], b[U];
     bool whole[U], valid[U];
 #pragma unroll
@@ -301,13 +322,7 @@ __device__ __forceinline__ void drr_tile(const DrrArgs& a, uint32_t t, int lane,
         }
 
         if constexpr (!REQUANT) {
-            if constexpr (kStaged) {
-                u32x4 piece[4];
-                stage_fp32(stage, lane, S, piece);
-                store_staged(a.out_hp, f0, lane, piece);
-            } else {
-                store_hp<CPC>(a.out_hp, a.hp_bf16 != 0, c[u], e[u], count, whole[u], S);
-            }
+            store_hp<CPC>(a.out_hp, a.hp_bf16 != 0, c[u], e[u], count, whole[u], S);
             continue;
         }
 
@@ -344,42 +359,23 @@ __device__ __forceinline__ void drr_tile(const DrrArgs& a, uint32_t t, int lane,
         if constexpr (OUT == kDrrRequantAll) {
             float h[CPC];
             dequant<F, CPC>(q, s2, h);
-            if constexpr (kStaged) {
-                u32x4 piece[4];
-                stage_fp32(stage, lane, h, piece);
 #pragma unroll
-                for (int j = 0; j < N; ++j)
-                    store_staged(a.out_hps[j], f0, lane, piece);
-            } else {
-#pragma unroll
-                for (int j = 0; j < N; ++j)
-                    store_hp<CPC>(a.out_hps[j], a.hp_bf16 != 0, c[u], e[u], count, whole[u], h);
-            }
+            for (int j = 0; j < N; ++j)
+                store_hp<CPC>(a.out_hps[j], a.hp_bf16 != 0, c[u], e[u], count, whole[u], h);
         } else if (a.out_hp) {
             float h[CPC];
             dequant<F, CPC>(q, s2, h);
-            if constexpr (kStaged) {
-                u32x4 piece[4];
-                stage_fp32(stage, lane, h, piece);
-                store_staged(a.out_hp, f0, lane, piece);
-            } else {
-                store_hp<CPC>(a.out_hp, a.hp_bf16 != 0, c[u], e[u], count, whole[u], h);
-            }
+            store_hp<CPC>(a.out_hp, a.hp_bf16 != 0, c[u], e[u], count, whole[u], h);
         }
     }
 }
 
-template <int F, int N, bool REQUANT, int CPC, int U, int OUT, bool STAGE = false>
+template <int F, int N, bool REQUANT, int CPC, int U, int OUT>
 __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
 {
     const int lane = lane_id();
     const uint32_t wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t waves_per_wg = blockDim.x / kWave;
-    u32x4* stage = nullptr;
-    if constexpr (STAGE) {
-        __shared__ u32x4 stage_mem[256 / kWave][kStageSlots];   // one region per wave
-        stage = stage_mem[wave_in_wg];
-    }
     const size_t count = a.hi;                                    // end of the range
     constexpr size_t kTile = (size_t)kWave * CPC * U;             // codes per wave tile
     const uint32_t ntiles = (uint32_t)((a.hi - a.lo + kTile - 1) / kTile);
@@ -402,32 +398,139 @@ __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
 
     for (uint32_t t = wave; t < ntiles; t += step) {
         if (a.lo + ((size_t)t + 1) * kTile <= count)
-            drr_tile<F, N, REQUANT, CPC, U, OUT, true, STAGE>(a, t, lane, c0, count, bshift, lpb, stage);
+            drr_tile<F, N, REQUANT, CPC, U, OUT, true>(a, t, lane, c0, count, bshift, lpb);
         else
-            drr_tile<F, N, REQUANT, CPC, U, OUT, false, STAGE>(a, t, lane, c0, count, bshift, lpb, stage);
+            drr_tile<F, N, REQUANT, CPC, U, OUT, false>(a, t, lane, c0, count, bshift, lpb);
+    }
+}
+
+// The 16 x 1 layout with the high-precision output (FP32, or BF16 when
+// BF16) staged through LDS, for whole tiles of 1024 codes only: tiles
+// [0, hi / 1024); the launcher passes every pointer already offset to the
+// start of the range (lo == 0 here) and runs the unstaged kernel over a
+// ragged remainder. Lane l owns chunk l of 16 codes (one 16-byte load per
+// source); sums, requantization and code / scale stores as in drr_tile.
+// Launched only for modes with a high-precision output (out_hp, or out_hps
+// for kDrrRequantAll). The range offset and an out_hp check, both removed
+// here, made the compiler schedule the loop 4% slower (8 x 64M codes
+// E5M2/256 with BF16 output: 127.3 against 121.7 us).
+template <int F, int N, bool REQUANT, int OUT, bool BF16>
+__global__ __launch_bounds__(256) void k_drr_staged(DrrArgs a)
+{
+    __shared__ u32x4 stage_mem[256 / kWave][kStageSlots];   // one region per wave
+    const int lane = lane_id();
+    const uint32_t wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t wg = a.xcd_ranges ? xcd_contiguous(blockIdx.x, gridDim.x) : blockIdx.x;
+    const uint32_t wave = wg * (blockDim.x / kWave) + wave_in_wg;
+    const uint32_t step = gridDim.x * (blockDim.x / kWave);
+    const uint32_t ntiles = (uint32_t)(a.hi / ((size_t)kWave * 16));
+    const int lpb = a.block / 16;                                 // lanes per block: <= 64
+    const int bshift = __builtin_ctz((unsigned)a.block);
+    u32x4* stage = stage_mem[wave_in_wg];
+
+    for (uint32_t t = wave; t < ntiles; t += step) {
+        const size_t c_tile = (size_t)t * kWave;
+        const size_t c = c_tile + lane;
+        const size_t e = c * 16;
+        const size_t b = e >> bshift;
+        Chunk<16> x[N];
+        float sc[N];
+#pragma unroll
+        for (int r = 0; r < N; ++r) {
+            x[r] = load_chunk<16>(static_cast<const uint8_t*>(a.codes[r]), c, e, a.hi, true);
+            sc[r] = a.scales[r][b];
+        }
+        float S[16];
+        dequant<F, 16>(x[0].w, sc[0], S);
+#pragma unroll
+        for (int r = 1; r < N; ++r) {
+            float d[16];
+            dequant<F, 16>(x[r].w, sc[r], d);
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                S[k] = S[k] + d[k];
+        }
+        if constexpr (!REQUANT) {
+            staged_out<1, BF16>(&a.out_hp, c_tile, stage, lane, S);
+            continue;
+        }
+        float m = __builtin_fabsf(S[0]);
+#pragma unroll
+        for (int k = 1; k < 16; ++k)
+            m = __builtin_fmaxf(m, __builtin_fabsf(S[k]));
+        const float A = bits_f32(group_max_rt(__builtin_bit_cast(uint32_t, m), lpb));
+        float s2, r2;
+        block_scale<F>(A, s2, r2);
+        uint32_t q[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            q[p] = f32x4_to_fp8<F>(clamp_fmax<F>(S[4 * p + 0] * r2), clamp_fmax<F>(S[4 * p + 1] * r2),
+                                   clamp_fmax<F>(S[4 * p + 2] * r2), clamp_fmax<F>(S[4 * p + 3] * r2));
+        if constexpr (OUT == kDrrRequantPush) {
+#pragma unroll
+            for (int j = 0; j < N; ++j)
+                store_codes<16>(static_cast<uint8_t*>(a.out_codes[j]), c, e, a.hi, true, q);
+            if ((lane % lpb) == 0) {
+#pragma unroll
+                for (int j = 0; j < N; ++j)
+                    store_scale<false>(a.out_scales[j] + b, s2);
+            }
+        } else if constexpr (OUT == kDrrRequant) {
+            store_codes<16>(static_cast<uint8_t*>(a.out_codes[0]), c, e, a.hi, true, q);
+            if ((lane % lpb) == 0)
+                store_scale<false>(a.out_scales[0] + b, s2);
+        }
+        float h[16];
+        dequant<F, 16>(q, s2, h);
+        if constexpr (OUT == kDrrRequantAll)
+            staged_out<N, BF16>(a.out_hps, c_tile, stage, lane, h);
+        else
+            staged_out<1, BF16>(&a.out_hp, c_tile, stage, lane, h);
     }
 }
 
 
-template <int F, bool R, int CPC, int U, int OUT, bool STAGE, int... I>
+template <int F, bool R, int CPC, int U, int OUT, int... I>
 void fill_row(DrrFn* row, std::integer_sequence<int, I...>)
 {
-    ((row[I] = &k_drr<F, I + 1, R, CPC, U, OUT, STAGE>), ...);
+    ((row[I] = &k_drr<F, I + 1, R, CPC, U, OUT>), ...);
 }
 
-template <int CPC, int U, bool STAGE = false>
+template <int CPC, int U>
 DrrFns make_fns()
 {
     DrrFns t{};
     const auto seq = std::make_integer_sequence<int, kMaxSrc>{};
-    fill_row<0, false, CPC, U, kDrrSum, STAGE>(t.fn[0][kDrrSum], seq);
-    fill_row<0, true, CPC, U, kDrrRequant, STAGE>(t.fn[0][kDrrRequant], seq);
-    fill_row<0, true, CPC, U, kDrrRequantPush, STAGE>(t.fn[0][kDrrRequantPush], seq);
-    fill_row<0, true, CPC, U, kDrrRequantAll, STAGE>(t.fn[0][kDrrRequantAll], seq);
-    fill_row<1, false, CPC, U, kDrrSum, STAGE>(t.fn[1][kDrrSum], seq);
-    fill_row<1, true, CPC, U, kDrrRequant, STAGE>(t.fn[1][kDrrRequant], seq);
-    fill_row<1, true, CPC, U, kDrrRequantPush, STAGE>(t.fn[1][kDrrRequantPush], seq);
-    fill_row<1, true, CPC, U, kDrrRequantAll, STAGE>(t.fn[1][kDrrRequantAll], seq);
+    fill_row<0, false, CPC, U, kDrrSum>(t.fn[0][kDrrSum], seq);
+    fill_row<0, true, CPC, U, kDrrRequant>(t.fn[0][kDrrRequant], seq);
+    fill_row<0, true, CPC, U, kDrrRequantPush>(t.fn[0][kDrrRequantPush], seq);
+    fill_row<0, true, CPC, U, kDrrRequantAll>(t.fn[0][kDrrRequantAll], seq);
+    fill_row<1, false, CPC, U, kDrrSum>(t.fn[1][kDrrSum], seq);
+    fill_row<1, true, CPC, U, kDrrRequant>(t.fn[1][kDrrRequant], seq);
+    fill_row<1, true, CPC, U, kDrrRequantPush>(t.fn[1][kDrrRequantPush], seq);
+    fill_row<1, true, CPC, U, kDrrRequantAll>(t.fn[1][kDrrRequantAll], seq);
+    return t;
+}
+
+template <int F, bool R, int OUT, bool BF16, int... I>
+void fill_staged_row(DrrFn* row, std::integer_sequence<int, I...>)
+{
+    ((row[I] = &k_drr_staged<F, I + 1, R, OUT, BF16>), ...);
+}
+
+template <bool BF16>
+DrrFns make_staged_fns()
+{
+    DrrFns t{};
+    const auto seq = std::make_integer_sequence<int, kMaxSrc>{};
+    fill_staged_row<0, false, kDrrSum, BF16>(t.fn[0][kDrrSum], seq);
+    fill_staged_row<0, true, kDrrRequant, BF16>(t.fn[0][kDrrRequant], seq);
+    fill_staged_row<0, true, kDrrRequantPush, BF16>(t.fn[0][kDrrRequantPush], seq);
+    fill_staged_row<0, true, kDrrRequantAll, BF16>(t.fn[0][kDrrRequantAll], seq);
+    fill_staged_row<1, false, kDrrSum, BF16>(t.fn[1][kDrrSum], seq);
+    fill_staged_row<1, true, kDrrRequant, BF16>(t.fn[1][kDrrRequant], seq);
+    fill_staged_row<1, true, kDrrRequantPush, BF16>(t.fn[1][kDrrRequantPush], seq);
+    fill_staged_row<1, true, kDrrRequantAll, BF16>(t.fn[1][kDrrRequantAll], seq);
     return t;
 }
 

@@ -341,6 +341,27 @@ def test_drr_codes_only_two_per_cu(fmt, block):
             assert bits_equal(g, r), f"{name}: " + first_mismatch(g, r)
 
 
+@pytest.mark.parametrize("n", [2, 5, 13, 16])
+def test_drr_staged_output_source_counts(n):
+    # FP32 and BF16 outputs from several sources at large sizes run the 16 x 1
+    # layout with the output staged through LDS: each source count is a
+    # kernel instance of its own; whole tiles through the stage, the ragged
+    # last tile directly
+    count = (1 << 20) + 13
+    for fmt, block in ((O.E4M3, 128), (O.E5M2, 1024)):
+        srcs = [G.fill(count, O.FP32, G.LAPLACE, seed=4700 + n + block, rank=r) for r in range(n)]
+        codes, scales = O.quant_fp8(srcs, O.FP32, fmt, block)
+        for mode, hp_dtype in ((O.DRR_SUM, O.FP32), (O.DRR_SUM, O.BF16), (O.DRR_REQUANT, O.FP32),
+                               (O.DRR_REQUANT, O.BF16)):
+            log(f"drr staged output n={n} fmt={fmt} block={block} mode={mode} hp={hp_dtype}")
+            got = _drr_gpu(codes, scales, fmt, block, mode, hp_dtype, True, count)
+            ref = O.dequant_reduce_requant(codes, scales, fmt, block, mode, hp_dtype, True)
+            for name, g, r in zip(("codes", "scales", "hp"), got, ref):
+                assert (g is None) == (r is None)
+                if g is not None:
+                    assert bits_equal(g, r), f"{name}: " + first_mismatch(g, r)
+
+
 @pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 256), (O.E4M3, 32),
                                        (O.E5M2, 512), (O.E4M3, 1024)])
 def test_drr_large_variant_ragged(fmt, block):
