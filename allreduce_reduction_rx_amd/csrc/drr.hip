@@ -59,10 +59,11 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     if (staged) {
         // Whole tiles of 1024 codes in the staged kernel, two 256-thread
         // workgroups per CU, each XCD a contiguous range up to 128 tiles per
-        // CU (8 x 16M codes: 37.8 against 39.1 us in plain order) and plain
-        // order above (8 x 256M codes E5M2/256 with BF16 output: 513 against
-        // 524 us); a ragged remainder (less than one tile) in the unstaged
-        // 16 x 1 kernel, launched after it.
+        // CU with FP32 output and 512 with BF16 output, plain order above
+        // (FP32: 8 x 16M codes 37.8 against 39.1 us, 8 x 64M 146 against
+        // 152 us; BF16: 8 x 64M 119.8 against 122.1 us, 8 x 256M 513
+        // against 524 us); a ragged remainder (less than one tile) in the
+        // unstaged 16 x 1 kernel, launched after it.
         const size_t whole = len / tile;
         hipError_t e = hipSuccess;
         if (whole) {
@@ -85,7 +86,7 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
             if (a.out_hp) arg.out_hp = static_cast<uint8_t*>(a.out_hp) + a.lo * esz;
             arg.lo = 0;
             arg.hi = whole * tile;
-            arg.xcd_ranges = whole <= (size_t)128 * cus ? 1 : 0;
+            arg.xcd_ranges = whole <= (size_t)(a.hp_bf16 ? 512 : 128) * cus ? 1 : 0;
             void* params[] = {&arg};
             e = launch_logged("k_drr_staged", (const void*)drr_fns_16x1_staged(a.hp_bf16).fn[fmt][r][nsrc - 1],
                               grid, blk, params, s);
@@ -114,12 +115,14 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     if (medium)
         pol.max_wgs_per_cu = 4;
     // Codes only, one destination (16 x 1): below 32 tiles per CU four
-    // workgroups per CU in plain order; above, two per CU with each XCD a
-    // contiguous range (8 x 4M codes E4M3/128: 7.1 us against 8.2 us with
-    // two per CU; 8 x 16M: 25.4 us, 8 x 64M: 100.7 us against 105.1 us in
-    // plain order).
+    // workgroups per CU in plain order; up to 512 per CU, two per CU with
+    // each XCD a contiguous range; above, two per CU in plain order (8 x 4M
+    // codes E4M3/128: 7.1 us against 8.2 us with two per CU; 8 x 16M:
+    // 25.4 us, 8 x 64M: 100.7 us against 105.1 us in plain order; 8 x 256M
+    // E5M2/256: 431.5 us against 437.7 us XCD-contiguous).
     const bool single_codes = !small && r == kDrrRequant && cpc == 16 && codes_only;
     const bool few = single_codes && tiles < (size_t)32 * cus;
+    const bool many = single_codes && tiles > (size_t)512 * cus;
     if (few)
         pol.max_wgs_per_cu = 4;
     dim3 grid, blk;
@@ -131,7 +134,7 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     // pushes to N destinations 3-8% and the FP32-output layout 2% faster;
     // no gain for the other large layouts, which keep the plain order.
     arg.xcd_ranges = (small || medium || r == kDrrRequantPush || (cpc == 4 && u == 4) ||
-                      (single_codes && !few)) ? 1 : 0;
+                      (single_codes && !few && !many)) ? 1 : 0;
     if (small && blk.x == (unsigned)kWave) {
         // Decode-size launches (one tile per 64-thread workgroup): each XCD
         // takes a contiguous range of tiles that covers whole 128-byte lines
