@@ -9,11 +9,11 @@ namespace {
 
 // One wave per tile (64 threads per work item). Large messages: 256-thread
 // workgroups, at most 2 per CU (a narrow HBM access window measured best on
-// MI355X), 4 for the one-source FP32-output layout (4 x 4), whose 4-byte
-// code loads keep fewer bytes in flight per wave; decode-size messages: one
-// tile per wave over every CU.
+// MI355X), also for the one-source FP32-output layout (4 x 4: 16M codes
+// E5M2/256 15.8 us against 16.0 us with 4 per CU, 256M codes 232 against
+// more than 249 us); decode-size messages: one tile per wave over every CU.
 LaunchPolicy policy_drr() { return {64u, 256u, 2u}; }
-LaunchPolicy policy_drr_fp32_out() { return {64u, 256u, 4u}; }
+LaunchPolicy policy_drr_fp32_out() { return {64u, 256u, 2u}; }
 // One source (the separate dequantization): each wave reads 1/N of the bytes
 // of an N-source launch, so more waves keep HBM busy; 4 workgroups per CU
 // measured 14% faster than 2 at 8 x 512 MiB BF16 (6 and 8 slower again).
