@@ -26,9 +26,9 @@ namespace {
 // ---------------------------------------------------------------------------
 
 // A wave processes tiles of U loads per lane (U x 1 KiB per tile): U = 4 or 8
-// for large messages (more bytes in flight per wave; launch_quant picks by
-// size), U = the loads per block (usually 1) for decode-size messages (4x the
-// waves, shorter serial chains).
+// for large messages (8 with the next tile's loads in flight; launch_quant
+// picks by size), U = the loads per block (usually 1) for decode-size
+// messages (4x the waves, shorter serial chains).
 template <int DT, int F, int BLOCK, int U>
 struct QuantShape {
     static constexpr int kVE = DT == 0 ? 4 : 8;          // elements per 16-B vector
@@ -96,16 +96,105 @@ __device__ __forceinline__ u32x4 load_partial(const void* src, size_t e, size_t 
     return x;
 }
 
-// SMALL (decode-size launches, one tile per wave): each XCD takes a
-// contiguous range of tiles and the block scales are stored nontemporal, so
-// that no line of scales is left partly written in several L2s for the
-// end-of-kernel write-back (together 7% faster at 8 x 512 KiB; at large sizes
-// both were slower, up to 13%, and the scale lines fill up in L2 instead).
+// Codes and block scales of one tile (x: the U loads of this lane, vector
+// v0 + u * 64 + lane). full: every element of the tile lies inside the
+// source; otherwise the codes and scales past count are not stored. SMALL:
+// scales stored nontemporal (decode-size launches).
+template <int DT, int F, int BLOCK, int U, bool SMALL>
+__device__ __forceinline__ void quant_tile(const u32x4 (&x)[U], uint8_t* codes, float* scales, size_t v0,
+                                           size_t count, bool full, int lane)
+{
+    using Sh = QuantShape<DT, F, BLOCK, U>;
+    constexpr int VE = Sh::kVE, LPB = Sh::kLPB, UPB = Sh::kUPB;
+    float f[U][VE];
+    float amax[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        widen<DT>(x[u], f[u]);
+        float m = __builtin_fabsf(f[u][0]);
+#pragma unroll
+        for (int k = 1; k < VE; ++k)
+            m = __builtin_fmaxf(m, __builtin_fabsf(f[u][k]));
+        amax[u] = m;
+    }
+
+    // Block absmax across the lanes (and loads) that hold the block.
+    float s[U], r[U];
+    if constexpr (UPB == 1) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float A = bits_f32(group_max<LPB>(__builtin_bit_cast(uint32_t, amax[u])));
+            block_scale<F>(A, s[u], r[u]);
+        }
+    } else {
+#pragma unroll
+        for (int g = 0; g < U / UPB; ++g) {
+            float m = amax[g * UPB];
+#pragma unroll
+            for (int q = 1; q < UPB; ++q)
+                m = __builtin_fmaxf(m, amax[g * UPB + q]);
+            float A = bits_f32(group_max<64>(__builtin_bit_cast(uint32_t, m)));
+            float sg, rg;
+            block_scale<F>(A, sg, rg);
+#pragma unroll
+            for (int q = 0; q < UPB; ++q) {
+                s[g * UPB + q] = sg;
+                r[g * UPB + q] = rg;
+            }
+        }
+    }
+
+    // Encode and store: VE codes per lane per load (4 or 8 bytes).
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        uint32_t w[VE / 4];
+#pragma unroll
+        for (int q = 0; q < VE / 4; ++q) {
+            float y0 = clamp_fmax<F>(f[u][4 * q + 0] * r[u]);
+            float y1 = clamp_fmax<F>(f[u][4 * q + 1] * r[u]);
+            float y2 = clamp_fmax<F>(f[u][4 * q + 2] * r[u]);
+            float y3 = clamp_fmax<F>(f[u][4 * q + 3] * r[u]);
+            w[q] = f32x4_to_fp8<F>(y0, y1, y2, y3);
+        }
+        const size_t vi = v0 + u * kWave + lane;
+        const size_t e = vi * VE;
+        if (full || e + VE <= count) {
+            // contiguous across the wave: stream past the caches
+            if constexpr (VE == 4) {
+                __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(codes) + vi);
+            } else {
+                u32x2 p = {w[0], w[1]};
+                __builtin_nontemporal_store(p, reinterpret_cast<u32x2*>(codes) + vi);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < VE; ++k)
+                if (e + k < count)
+                    codes[e + k] = (uint8_t)(w[k / 4] >> (8 * (k & 3)));
+        }
+        // one lane per block writes the scale
+        const bool leader = UPB == 1 ? (lane % LPB) == 0 : (lane == 0 && u % UPB == 0);
+        if (leader && (full || e < count)) {
+            if constexpr (SMALL)
+                __builtin_nontemporal_store(s[u], scales + e / BLOCK);
+            else
+                scales[e / BLOCK] = s[u];
+        }
+    }
+}
+
+// Any message, tiles that may end past the source (decode-size launches and
+// the ragged ends of large ones). SMALL (decode size, one tile per wave):
+// each XCD takes a contiguous range of tiles and the block scales are stored
+// nontemporal, so that no line of scales is left partly written in several
+// L2s for the end-of-kernel write-back (together 7% faster at 8 x 512 KiB;
+// at large sizes both were slower, up to 13%, and the scale lines fill up in
+// L2 instead).
 template <int DT, int F, int BLOCK, int UL, bool SMALL>
 __global__ __launch_bounds__(256) void k_quant(QuantArgs a)
 {
     using Sh = QuantShape<DT, F, BLOCK, UL>;
-    constexpr int VE = Sh::kVE, U = Sh::kU, LPB = Sh::kLPB, UPB = Sh::kUPB;
+    constexpr int VE = Sh::kVE, U = Sh::kU;
     const int lane = lane_id();
     const uint32_t wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t waves_per_wg = blockDim.x / kWave;
@@ -119,8 +208,6 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a)
         const uint32_t j = t / tiles_per_src;
         const uint32_t tile = t - j * tiles_per_src;
         const void* src = a.src[j];
-        uint8_t* codes = static_cast<uint8_t*>(a.codes[j]);
-        float* scales = a.scales[j];
         const size_t e0 = (size_t)tile * Sh::kTileElems;   // first element of the tile
         const size_t v0 = e0 / VE;
         const bool full = e0 + Sh::kTileElems <= a.count;
@@ -136,117 +223,140 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a)
             for (int u = 0; u < U; ++u)
                 x[u] = load_partial<DT>(src, (v0 + u * kWave + lane) * VE, a.count);
         }
+        quant_tile<DT, F, BLOCK, U, SMALL>(x, static_cast<uint8_t*>(a.codes[j]), a.scales[j], v0, a.count,
+                                           full, lane);
+    }
+}
 
-        float f[U][VE];
-        float amax[U];
+// The U loads of tile t (tile t % tiles_per_src of source t / tiles_per_src).
+template <int DT, int F, int BLOCK, int U>
+__device__ __forceinline__ void load_whole_tile(u32x4 (&x)[U], const QuantArgs& a, uint32_t t,
+                                                uint32_t tiles_per_src, int lane)
+{
+    using Sh = QuantShape<DT, F, BLOCK, U>;
+    const uint32_t j = t / tiles_per_src;
+    const size_t v0 = (size_t)(t - j * tiles_per_src) * Sh::kTileVec;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            widen<DT>(x[u], f[u]);
-            float m = __builtin_fabsf(f[u][0]);
-#pragma unroll
-            for (int k = 1; k < VE; ++k)
-                m = __builtin_fmaxf(m, __builtin_fabsf(f[u][k]));
-            amax[u] = m;
+    for (int u = 0; u < U; ++u)
+        x[u] = ld16_stream(a.src[j], v0 + u * kWave + lane);
+}
+
+template <int DT, int F, int BLOCK, int U>
+__device__ __forceinline__ void quant_whole_tile(const u32x4 (&x)[U], const QuantArgs& a, uint32_t t,
+                                                 uint32_t tiles_per_src, int lane)
+{
+    using Sh = QuantShape<DT, F, BLOCK, U>;
+    const uint32_t j = t / tiles_per_src;
+    const size_t v0 = (size_t)(t - j * tiles_per_src) * Sh::kTileVec;
+    quant_tile<DT, F, BLOCK, U, false>(x, static_cast<uint8_t*>(a.codes[j]), a.scales[j], v0, a.count, true,
+                                       lane);
+}
+
+// Large messages, whole tiles only (count a multiple of the tile; the ragged
+// end of each source goes to k_quant). Without the partial-tile code the
+// kernel ran 6% faster (8 x 16M FP32 E4M3/128: 112.6 -> 106.0 us). PF: the
+// next tile's loads are issued before this tile's arithmetic, into the other
+// of two register buffers; the last tile of a wave is peeled off, so that in
+// the loop every prefetch is unconditional and the compiler waits only for
+// the current tile's loads (8 x 256M BF16 E5M2/256: 1148 -> 1073 us, at one
+// 256-thread workgroup per CU).
+template <int DT, int F, int BLOCK, int U, bool PF>
+__global__ __launch_bounds__(256) void k_quant_whole(QuantArgs a)
+{
+    using Sh = QuantShape<DT, F, BLOCK, U>;
+    const int lane = lane_id();
+    const uint32_t wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t wave = blockIdx.x * (blockDim.x / kWave) + wave_in_wg;
+    const uint32_t nwaves = gridDim.x * (blockDim.x / kWave);
+    const uint32_t tiles_per_src = (uint32_t)(a.count / Sh::kTileElems);
+    const uint32_t total = tiles_per_src * (uint32_t)a.nsrc;
+    uint32_t t = wave;
+    if (t >= total)
+        return;
+    if constexpr (PF) {
+        u32x4 xa[U], xb[U];
+        uint32_t n = (total - t + nwaves - 1) / nwaves;   // tiles of this wave, >= 1
+        load_whole_tile<DT, F, BLOCK, U>(xa, a, t, tiles_per_src, lane);
+        for (;;) {
+            if (n == 1) {
+                quant_whole_tile<DT, F, BLOCK, U>(xa, a, t, tiles_per_src, lane);
+                break;
+            }
+            load_whole_tile<DT, F, BLOCK, U>(xb, a, t + nwaves, tiles_per_src, lane);
+            quant_whole_tile<DT, F, BLOCK, U>(xa, a, t, tiles_per_src, lane);
+            t += nwaves;
+            --n;
+            if (n == 1) {
+                quant_whole_tile<DT, F, BLOCK, U>(xb, a, t, tiles_per_src, lane);
+                break;
+            }
+            load_whole_tile<DT, F, BLOCK, U>(xa, a, t + nwaves, tiles_per_src, lane);
+            quant_whole_tile<DT, F, BLOCK, U>(xb, a, t, tiles_per_src, lane);
+            t += nwaves;
+            --n;
         }
-
-        // Block absmax across the lanes (and loads) that hold the block.
-        float s[U], r[U];
-        if constexpr (UPB == 1) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float A = bits_f32(group_max<LPB>(__builtin_bit_cast(uint32_t, amax[u])));
-                block_scale<F>(A, s[u], r[u]);
-            }
-        } else {
-#pragma unroll
-            for (int g = 0; g < U / UPB; ++g) {
-                float m = amax[g * UPB];
-#pragma unroll
-                for (int q = 1; q < UPB; ++q)
-                    m = __builtin_fmaxf(m, amax[g * UPB + q]);
-                float A = bits_f32(group_max<64>(__builtin_bit_cast(uint32_t, m)));
-                float sg, rg;
-                block_scale<F>(A, sg, rg);
-#pragma unroll
-                for (int q = 0; q < UPB; ++q) {
-                    s[g * UPB + q] = sg;
-                    r[g * UPB + q] = rg;
-                }
-            }
-        }
-
-        // Encode and store: VE codes per lane per load (4 or 8 bytes).
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            uint32_t w[VE / 4];
-#pragma unroll
-            for (int q = 0; q < VE / 4; ++q) {
-                float y0 = clamp_fmax<F>(f[u][4 * q + 0] * r[u]);
-                float y1 = clamp_fmax<F>(f[u][4 * q + 1] * r[u]);
-                float y2 = clamp_fmax<F>(f[u][4 * q + 2] * r[u]);
-                float y3 = clamp_fmax<F>(f[u][4 * q + 3] * r[u]);
-                w[q] = f32x4_to_fp8<F>(y0, y1, y2, y3);
-            }
-            const size_t vi = v0 + u * kWave + lane;
-            const size_t e = vi * VE;
-            if (full || e + VE <= a.count) {
-                // contiguous across the wave: stream past the caches
-                if constexpr (VE == 4) {
-                    __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(codes) + vi);
-                } else {
-                    u32x2 p = {w[0], w[1]};
-                    __builtin_nontemporal_store(p, reinterpret_cast<u32x2*>(codes) + vi);
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < VE; ++k)
-                    if (e + k < a.count)
-                        codes[e + k] = (uint8_t)(w[k / 4] >> (8 * (k & 3)));
-            }
-            // one lane per block writes the scale
-            const bool leader = UPB == 1 ? (lane % LPB) == 0 : (lane == 0 && u % UPB == 0);
-            if (leader && e < a.count) {
-                if constexpr (SMALL)
-                    __builtin_nontemporal_store(s[u], scales + e / BLOCK);
-                else
-                    scales[e / BLOCK] = s[u];
-            }
+    } else {
+        for (; t < total; t += nwaves) {
+            u32x4 x[U];
+            load_whole_tile<DT, F, BLOCK, U>(x, a, t, tiles_per_src, lane);
+            quant_whole_tile<DT, F, BLOCK, U>(x, a, t, tiles_per_src, lane);
         }
     }
 }
 
-
 using QuantFn = void (*)(QuantArgs);
 
-// U: loads per lane of the large variants (4 or 8); 0 for the decode-size
-// variant (the loads per block).
-template <int DT, int F, int U, int... L>
+// Decode-size variant: U = the loads per block.
+template <int DT, int F, int... L>
 constexpr std::array<QuantFn, sizeof...(L)> quant_row(std::integer_sequence<int, L...>)
 {
-    return {{&k_quant<DT, F, (32 << L), U ? U : loads_per_block<DT, (32 << L)>(), U == 0>...}};
+    return {{&k_quant<DT, F, (32 << L), loads_per_block<DT, (32 << L)>(), true>...}};
 }
 
-template <int U>
+template <int DT, int F, int U, bool PF, int... L>
+constexpr std::array<QuantFn, sizeof...(L)> quant_whole_row(std::integer_sequence<int, L...>)
+{
+    return {{&k_quant_whole<DT, F, (32 << L), U, PF>...}};
+}
+
+// [src dtype][fmt][log2(block) - 5]
 struct QuantTable {
-    // [src dtype][fmt][log2(block) - 5]
     std::array<QuantFn, 6> fn[2][2] = {
-        {quant_row<0, 0, U>(std::make_integer_sequence<int, 6>{}),
-         quant_row<0, 1, U>(std::make_integer_sequence<int, 6>{})},
-        {quant_row<1, 0, U>(std::make_integer_sequence<int, 6>{}),
-         quant_row<1, 1, U>(std::make_integer_sequence<int, 6>{})}};
+        {quant_row<0, 0>(std::make_integer_sequence<int, 6>{}), quant_row<0, 1>(std::make_integer_sequence<int, 6>{})},
+        {quant_row<1, 0>(std::make_integer_sequence<int, 6>{}), quant_row<1, 1>(std::make_integer_sequence<int, 6>{})}};
 };
-const QuantTable<0> kQuantSmall;
-const QuantTable<4> kQuantLarge;
-const QuantTable<8> kQuantHuge;
+template <int U, bool PF>
+struct QuantWholeTable {
+    std::array<QuantFn, 6> fn[2][2] = {
+        {quant_whole_row<0, 0, U, PF>(std::make_integer_sequence<int, 6>{}),
+         quant_whole_row<0, 1, U, PF>(std::make_integer_sequence<int, 6>{})},
+        {quant_whole_row<1, 0, U, PF>(std::make_integer_sequence<int, 6>{}),
+         quant_whole_row<1, 1, U, PF>(std::make_integer_sequence<int, 6>{})}};
+};
+const QuantTable kQuantSmall;
+const QuantWholeTable<4, false> kQuantWhole4;
+const QuantWholeTable<8, true> kQuantWhole8Pf;
 
 // One wave per tile (64 threads per work item), 256-thread workgroups.
-// Messages of at least 16 tiles of 8 loads per wave at two workgroups per CU:
-// U = 8, at most 2 workgroups per CU (a narrow HBM access window); below
-// that U = 4 and 4 per CU. Measured on MI355X: 8 x 16M FP32 E4M3/128 114.3 us
-// (U = 4, 2 per CU: 116.3), 8 x 256M BF16 E5M2/256 1139 us (1152); 8 x 2M
-// FP32 16.0 us (17.3), 8 x 8M BF16 35.7 us (37.3). Decode-size messages: one
-// tile per wave over every CU.
 LaunchPolicy policy_quant() { return {256u, 256u, 2u}; }
+
+// Decode-size kernel over any message: one tile (one block's loads) per wave
+// over every CU.
+hipError_t launch_quant_tiles(const QuantArgs& a, int src_dtype, int fmt, int block, hipStream_t s)
+{
+    const int lb = __builtin_ctz((unsigned)block) - 5;
+    const size_t vec_elems = src_dtype == 0 ? 4 : 8;
+    const size_t lanes_per_block = (size_t)block / vec_elems;
+    const size_t u = lanes_per_block <= 64 ? 1 : lanes_per_block / 64;
+    const size_t tile_elems = u * 64 * vec_elems;
+    const size_t tiles = (a.count + tile_elems - 1) / tile_elems * (size_t)a.nsrc;
+    dim3 grid, blk;
+    launch_geometry(tiles * kWave, true, policy_quant(), grid, blk);
+    QuantArgs arg = a;
+    void* params[] = {&arg};
+    return launch_logged("k_quant (decode size)", (const void*)kQuantSmall.fn[src_dtype][fmt][lb], grid, blk,
+                         params, s);
+}
 
 }  // namespace
 
@@ -256,26 +366,48 @@ hipError_t launch_quant(const QuantArgs& a, int src_dtype, int fmt, int block, h
     const size_t vec_elems = src_dtype == 0 ? 4 : 8;
     const size_t cus = (size_t)device_cu_count();
     const size_t large_tiles = (a.count + 4 * 64 * vec_elems - 1) / (4 * 64 * vec_elems) * (size_t)a.nsrc;
-    const size_t huge_tiles = (a.count + 8 * 64 * vec_elems - 1) / (8 * 64 * vec_elems) * (size_t)a.nsrc;
-    const bool small = large_tiles < kSmallTilesPerCu * cus;
-    const bool huge = huge_tiles >= (size_t)16 * 8 * cus;
-    // loads per tile of the chosen variant
-    size_t lanes_per_block = (size_t)block / vec_elems;
-    size_t u = small ? (lanes_per_block <= 64 ? 1 : lanes_per_block / 64) : huge ? 8 : 4;
-    const size_t tile_elems = u * 64 * vec_elems;
-    const size_t tiles = (a.count + tile_elems - 1) / tile_elems * (size_t)a.nsrc;
-    LaunchPolicy pol = policy_quant();
-    if (!small && !huge)
-        pol.max_wgs_per_cu = 4;
+    if (large_tiles < kSmallTilesPerCu * cus)
+        return launch_quant_tiles(a, src_dtype, fmt, block, s);
     dim3 grid, blk;
-    launch_geometry(tiles * kWave, small, pol, grid, blk);
-    QuantArgs arg = a;
-    void* params[] = {&arg};
-    QuantFn fn = small ? kQuantSmall.fn[src_dtype][fmt][lb]
-               : huge  ? kQuantHuge.fn[src_dtype][fmt][lb]
-                       : kQuantLarge.fn[src_dtype][fmt][lb];
-    return launch_logged(small ? "k_quant (decode size)" : huge ? "k_quant (8 loads per lane)" : "k_quant",
-                         (const void*)fn, grid, blk, params, s);
+    // Large messages: whole tiles in k_quant_whole, then the ragged end of
+    // each source (less than one tile) in the decode-size kernel. A tile of
+    // 4 loads per lane is 4 KiB of input. From 4 MiB of input per CU
+    // (1024 such tiles): 8 loads per lane with the next tile prefetched, one
+    // workgroup per CU (8 x 256M BF16 E5M2/256 1080 us against 1157 us for
+    // 4 loads at two per CU; 8 x 64M BF16 259.5 against 265.2 us, FP32
+    // 435.5 against 438.1 us); below: 4 loads per lane, two workgroups per
+    // CU (8 x 16M FP32 E4M3/128 106.4 us against 109.4 us with the
+    // prefetch), four below 64 tiles per CU (8 x 1M FP32 8.8 against
+    // 9.1 us).
+    const bool pf = large_tiles >= (size_t)1024 * cus;
+    const size_t u = pf ? 8 : 4;
+    const size_t tile_elems = u * 64 * vec_elems;
+    const size_t whole = a.count / tile_elems;
+    if (whole) {
+        LaunchPolicy pol = policy_quant();
+        pol.max_wgs_per_cu = pf ? 1 : large_tiles < (size_t)64 * cus ? 4 : 2;
+        launch_geometry(whole * (size_t)a.nsrc * kWave, false, pol, grid, blk);
+        QuantArgs arg = a;
+        arg.count = whole * tile_elems;
+        void* params[] = {&arg};
+        const QuantFn fn = pf ? kQuantWhole8Pf.fn[src_dtype][fmt][lb] : kQuantWhole4.fn[src_dtype][fmt][lb];
+        const hipError_t e = launch_logged(pf ? "k_quant_whole (8 loads, prefetch)" : "k_quant_whole", (const void*)fn,
+                                           grid, blk, params, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    if (a.count % tile_elems == 0)
+        return hipSuccess;
+    // tile_elems is a multiple of the block, so the rest starts on a block
+    QuantArgs rest = a;
+    const size_t done = whole * tile_elems;
+    for (int j = 0; j < a.nsrc; ++j) {
+        rest.src[j] = static_cast<const uint8_t*>(a.src[j]) + done * (src_dtype == 0 ? 4 : 2);
+        rest.codes[j] = static_cast<uint8_t*>(a.codes[j]) + done;
+        rest.scales[j] = a.scales[j] + done / (size_t)block;
+    }
+    rest.count = a.count - done;
+    return launch_quant_tiles(rest, src_dtype, fmt, block, s);
 }
 
 }  // namespace rx

@@ -247,21 +247,37 @@ def test_quant_large_variant_ragged(dtype, fmt, block):
     assert bits_equal(gs[0], rs[0]), first_mismatch(gs[0], rs[0])
 
 
-@pytest.mark.parametrize("dtype,fmt,block", [(O.FP32, O.E4M3, 128), (O.BF16, O.E5M2, 1024),
-                                             (O.FP32, O.E5M2, 1024)])
-def test_quant_eight_loads_ragged(dtype, fmt, block):
-    # at least 16 tiles of 8 loads per wave at two 256-thread workgroups per
-    # CU on a 256-CU MI355X: the 8-loads-per-lane kernel (blocks of one and
-    # of several loads), ragged tail and partial last block of every source
+@pytest.mark.parametrize("dtype,fmt,block,mib", [(O.FP32, O.E4M3, 128, 32), (O.BF16, O.E5M2, 1024, 32),
+                                                 (O.FP32, O.E4M3, 128, 128), (O.BF16, O.E5M2, 1024, 128),
+                                                 (O.FP32, O.E5M2, 1024, 128), (O.BF16, O.E4M3, 32, 128)])
+def test_quant_whole_tiles_ragged(dtype, fmt, block, mib):
+    # 8 sources of mib MiB + 5 elements on a 256-CU MI355X: the whole-tile
+    # kernel with 4 loads per lane (32 MiB) or 8 loads per lane and the next
+    # tile prefetched (128 MiB: 1 GiB of input), blocks of one and of several
+    # loads, then the ragged end of every source (a partial last block) in a
+    # second launch. Every code and scale against the oracle, which runs over
+    # windows of whole blocks in a thread pool.
     n = 8
-    count = (8 if dtype == O.FP32 else 16) * (1 << 20) + 5
-    log(f"quant 8 loads per lane dtype={dtype} fmt={fmt} block={block}")
-    srcs = [G.fill(count, dtype, G.NORMAL_OUTLIER, seed=3600 + block, rank=r) for r in range(n)]
+    count = mib * (1 << 20) // (4 if dtype == O.FP32 else 2) + 5
+    log(f"quant whole tiles dtype={dtype} fmt={fmt} block={block} count={count}")
+    srcs = [G.fill(count, dtype, G.NORMAL_OUTLIER, seed=3600 + block + mib, rank=r) for r in range(n)]
     gc, gs = _quant_gpu(srcs, dtype, fmt, block, count)
-    rc, rs = O.quant_fp8(srcs, dtype, fmt, block)
-    for j in range(n):
-        assert bits_equal(gc[j], rc[j]), f"codes src={j}: " + first_mismatch(gc[j], rc[j])
-        assert bits_equal(gs[j], rs[j]), f"scales src={j}: " + first_mismatch(gs[j], rs[j])
+    win = 8192 * block
+
+    def check(i0):
+        i1 = min(i0 + win, count)
+        b0, b1 = i0 // block, -(-i1 // block)
+        rc, rs = O.quant_fp8([x[i0:i1] for x in srcs], dtype, fmt, block)
+        for j in range(n):
+            if not bits_equal(gc[j][i0:i1], rc[j]):
+                return f"codes src={j} window [{i0}, {i1}): " + first_mismatch(gc[j][i0:i1], rc[j])
+            if not bits_equal(gs[j][b0:b1], rs[j]):
+                return f"scales src={j} window [{i0}, {i1}): " + first_mismatch(gs[j][b0:b1], rs[j])
+        return None
+
+    with ThreadPoolExecutor(_pool_size()) as ex:
+        for res in ex.map(check, range(0, count, win)):
+            assert res is None, res
 
 
 def test_quant_degenerate_blocks():
