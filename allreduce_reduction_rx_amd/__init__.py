@@ -96,7 +96,7 @@ def lib() -> ctypes.CDLL:
             "rxtest_bf16_round_bits": [ctypes.c_uint32, _SZ, _P, _P],
             "rxtest_group_max": [_P, _SZ, _I, _P, _P],
             "rxtest_stream": [_I, _P, _P, _SZ, _I, _I, _P],
-            "rxtest_stream_mixed": [_I, _PP, _I, _P, _SZ, _I, _I, _P],
+            "rxtest_stream_mixed": [_I, _PP, _I, _P, _SZ, _I, _I, _I, _P],
             "rxtest_copy_streams": [_PP, _PP, _I, _SZ, _SZ, _I, _I, _P],
         }
         for name, args in sig.items():
@@ -428,7 +428,7 @@ RXTEST_MIXED_REDUCE, RXTEST_MIXED_NARROW2, RXTEST_MIXED_NARROW4 = 0, 1, 2
 
 
 def rxtest_stream_mixed(kind: int, srcs: Sequence, dst, src_bytes: int, wgs_per_cu: int = 1,
-                        nontemporal: bool = False, stream=None) -> None:
+                        nontemporal: bool = False, prefetch: bool = False, stream=None) -> None:
     """Mixed read/write ceiling kernel: reduce (len(srcs) : 1, dst = XOR of
     the sources) or narrow (one source, dst of src_bytes / 2 or / 4)."""
     def size(t):
@@ -444,7 +444,7 @@ def rxtest_stream_mixed(kind: int, srcs: Sequence, dst, src_bytes: int, wgs_per_
         raise ValueError("dst too small")
     _check(lib().rxtest_stream_mixed(kind, _ptr_array([t.data_ptr() for t in srcs]), len(srcs),
                                      dst.data_ptr(), src_bytes, wgs_per_cu,
-                                     int(bool(nontemporal)), _stream(stream)),
+                                     int(bool(nontemporal)), int(bool(prefetch)), _stream(stream)),
            "rxtest_stream_mixed")
 
 

@@ -45,7 +45,10 @@ __device__ __forceinline__ u32x4 wave_xor(u32x4 v)
 // Wave tiles of kCeilU contiguous 64-vector rows, grid-stride over the waves
 // of the launch. KIND 0: read, XOR into a per-wave sum written once at the
 // end (16 bytes per wave); 1: write a constant pattern; 2: copy; 3: no
-// memory access at all (the launch alone).
+// memory access at all (the launch alone). The loop covers whole tiles only,
+// with no bounds checks inside it (checks inside a tile loop serialise the
+// loads of a wave); the partial last tile, if any, is done after the loop by
+// the wave whose turn it would be.
 template <int KIND, bool NT>
 __global__ __launch_bounds__(256) void k_stream(const void* __restrict__ src, void* __restrict__ dst,
                                                 size_t nvec, u32x4 pattern)
@@ -55,33 +58,33 @@ __global__ __launch_bounds__(256) void k_stream(const void* __restrict__ src, vo
     const size_t lane = threadIdx.x % kWave;
     u32x4 acc = {0u, 0u, 0u, 0u};
     if constexpr (KIND == 3) return;
-    for (size_t t = wave; t * kCeilTile < nvec; t += waves) {
+    const size_t ntiles = nvec / kCeilTile;
+    for (size_t t = wave; t < ntiles; t += waves) {
         const size_t base = t * kCeilTile + lane;
-        if ((t + 1) * kCeilTile <= nvec) {
-            if constexpr (KIND == 0) {
-                u32x4 x[kCeilU];
+        if constexpr (KIND == 0) {
+            u32x4 x[kCeilU];
 #pragma unroll
-                for (int u = 0; u < kCeilU; ++u) x[u] = ld<NT>(src, base + (size_t)u * kWave);
+            for (int u = 0; u < kCeilU; ++u) x[u] = ld<NT>(src, base + (size_t)u * kWave);
 #pragma unroll
-                for (int u = 0; u < kCeilU; ++u) acc ^= x[u];
-            } else if constexpr (KIND == 1) {
+            for (int u = 0; u < kCeilU; ++u) acc ^= x[u];
+        } else if constexpr (KIND == 1) {
 #pragma unroll
-                for (int u = 0; u < kCeilU; ++u) st<NT>(dst, base + (size_t)u * kWave, pattern);
-            } else {
-                u32x4 x[kCeilU];
-#pragma unroll
-                for (int u = 0; u < kCeilU; ++u) x[u] = ld<NT>(src, base + (size_t)u * kWave);
-#pragma unroll
-                for (int u = 0; u < kCeilU; ++u) st<NT>(dst, base + (size_t)u * kWave, x[u]);
-            }
+            for (int u = 0; u < kCeilU; ++u) st<NT>(dst, base + (size_t)u * kWave, pattern);
         } else {
-            for (int u = 0; u < kCeilU; ++u) {
-                const size_t v = base + (size_t)u * kWave;
-                if (v >= nvec) break;
-                if constexpr (KIND == 0) acc ^= ld16(src, v);
-                else if constexpr (KIND == 1) st16(dst, v, pattern);
-                else st16(dst, v, ld16(src, v));
-            }
+            u32x4 x[kCeilU];
+#pragma unroll
+            for (int u = 0; u < kCeilU; ++u) x[u] = ld<NT>(src, base + (size_t)u * kWave);
+#pragma unroll
+            for (int u = 0; u < kCeilU; ++u) st<NT>(dst, base + (size_t)u * kWave, x[u]);
+        }
+    }
+    if (ntiles * kCeilTile < nvec && wave == ntiles % waves) {
+        for (int u = 0; u < kCeilU; ++u) {
+            const size_t v = ntiles * kCeilTile + lane + (size_t)u * kWave;
+            if (v >= nvec) break;
+            if constexpr (KIND == 0) acc ^= ld16(src, v);
+            else if constexpr (KIND == 1) st16(dst, v, pattern);
+            else st16(dst, v, ld16(src, v));
         }
     }
     if constexpr (KIND == 0) {
@@ -98,72 +101,166 @@ __global__ __launch_bounds__(256) void k_stream(const void* __restrict__ src, vo
 //   narrow: one stream read, one written at 1/K of its bytes (16 bytes read
 //           and 16/K written per lane: the quantizer's pattern, K = 4 for
 //           FP32 and 2 for BF16 input).
+// Whole tiles in the loop, the partial last tile after it (as k_stream).
+// PF: each wave loads its next tile into a second register buffer before it
+// writes the current one; the last tile of a wave is peeled off, so that the
+// prefetch in the loop is unconditional.
 struct MixedArgs {
     const void* src[kMaxSrc];
     void* dst;
     size_t nvec;   // 16-byte vectors per source
 };
 
+template <int NSRC>
+struct MixedReduceShape {
+    static constexpr int kU = NSRC <= 8 ? 4 : 2;
+    static constexpr size_t kTile = (size_t)kWave * kU;
+};
+
 template <int NSRC, bool NT>
+__device__ __forceinline__ void mixed_reduce_load(u32x4 (&x)[MixedReduceShape<NSRC>::kU][NSRC], const MixedArgs& a,
+                                                  size_t t, size_t lane)
+{
+    using Sh = MixedReduceShape<NSRC>;
+#pragma unroll
+    for (int u = 0; u < Sh::kU; ++u)
+#pragma unroll
+        for (int r = 0; r < NSRC; ++r)
+            x[u][r] = ld<NT>(a.src[r], t * Sh::kTile + lane + (size_t)u * kWave);
+}
+
+template <int NSRC, bool NT>
+__device__ __forceinline__ void mixed_reduce_store(const u32x4 (&x)[MixedReduceShape<NSRC>::kU][NSRC],
+                                                   const MixedArgs& a, size_t t, size_t lane)
+{
+    using Sh = MixedReduceShape<NSRC>;
+#pragma unroll
+    for (int u = 0; u < Sh::kU; ++u) {
+        u32x4 y = x[u][0];
+#pragma unroll
+        for (int r = 1; r < NSRC; ++r) y ^= x[u][r];
+        st<NT>(a.dst, t * Sh::kTile + lane + (size_t)u * kWave, y);
+    }
+}
+
+template <int NSRC, bool NT, bool PF>
 __global__ __launch_bounds__(256) void k_mixed_reduce(MixedArgs a)
 {
-    constexpr int U = NSRC <= 8 ? 4 : 2;
-    constexpr size_t kTile = (size_t)kWave * U;
+    using Sh = MixedReduceShape<NSRC>;
+    constexpr int U = Sh::kU;
     const size_t waves = (size_t)gridDim.x * (blockDim.x / kWave);
     const size_t wave = (size_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     const size_t lane = threadIdx.x % kWave;
-    for (size_t t = wave; t * kTile < a.nvec; t += waves) {
-        const size_t base = t * kTile + lane;
-        u32x4 y[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const size_t v = base + (size_t)u * kWave;
-            if (v < a.nvec) {
-                u32x4 x[NSRC];
-#pragma unroll
-                for (int r = 0; r < NSRC; ++r) x[r] = ld<NT>(a.src[r], v);
-                y[u] = x[0];
-#pragma unroll
-                for (int r = 1; r < NSRC; ++r) y[u] ^= x[r];
+    const size_t ntiles = a.nvec / Sh::kTile;
+    if constexpr (PF) {
+        if (wave < ntiles) {
+            u32x4 xa[U][NSRC], xb[U][NSRC];
+            size_t t = wave;
+            size_t n = (ntiles - t + waves - 1) / waves;
+            mixed_reduce_load<NSRC, NT>(xa, a, t, lane);
+            for (;;) {
+                if (n == 1) { mixed_reduce_store<NSRC, NT>(xa, a, t, lane); break; }
+                mixed_reduce_load<NSRC, NT>(xb, a, t + waves, lane);
+                mixed_reduce_store<NSRC, NT>(xa, a, t, lane);
+                t += waves;
+                --n;
+                if (n == 1) { mixed_reduce_store<NSRC, NT>(xb, a, t, lane); break; }
+                mixed_reduce_load<NSRC, NT>(xa, a, t + waves, lane);
+                mixed_reduce_store<NSRC, NT>(xb, a, t, lane);
+                t += waves;
+                --n;
             }
         }
-#pragma unroll
+    } else {
+        for (size_t t = wave; t < ntiles; t += waves) {
+            u32x4 x[U][NSRC];
+            mixed_reduce_load<NSRC, NT>(x, a, t, lane);
+            mixed_reduce_store<NSRC, NT>(x, a, t, lane);
+        }
+    }
+    if (ntiles * Sh::kTile < a.nvec && wave == ntiles % waves) {
         for (int u = 0; u < U; ++u) {
-            const size_t v = base + (size_t)u * kWave;
-            if (v < a.nvec) st<NT>(a.dst, v, y[u]);
+            const size_t v = ntiles * Sh::kTile + lane + (size_t)u * kWave;
+            if (v >= a.nvec) break;
+            u32x4 y = ld16(a.src[0], v);
+            for (int r = 1; r < NSRC; ++r) y ^= ld16(a.src[r], v);
+            st16(a.dst, v, y);
         }
     }
 }
 
+// narrow: K = 2 or 4; U loads per lane per tile (8 with the prefetch, as the
+// quantizer's largest variant, 4 without)
+template <int K, bool NT, int U>
+__device__ __forceinline__ void mixed_narrow_load(u32x4 (&x)[U], const MixedArgs& a, size_t t, size_t lane)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        x[u] = ld<NT>(a.src[0], t * kWave * U + lane + (size_t)u * kWave);
+}
+
 template <int K, bool NT>
+__device__ __forceinline__ void narrow_store(const MixedArgs& a, size_t v, const u32x4& x)
+{
+    if constexpr (K == 2) {
+        u32x2 w = {x[0] ^ x[1], x[2] ^ x[3]};
+        if constexpr (NT) __builtin_nontemporal_store(w, static_cast<u32x2*>(a.dst) + v);
+        else static_cast<u32x2*>(a.dst)[v] = w;
+    } else {
+        uint32_t w = x[0] ^ x[1] ^ x[2] ^ x[3];
+        if constexpr (NT) __builtin_nontemporal_store(w, static_cast<uint32_t*>(a.dst) + v);
+        else static_cast<uint32_t*>(a.dst)[v] = w;
+    }
+}
+
+template <int K, bool NT, int U>
+__device__ __forceinline__ void mixed_narrow_store(const u32x4 (&x)[U], const MixedArgs& a, size_t t, size_t lane)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        narrow_store<K, NT>(a, t * kWave * U + lane + (size_t)u * kWave, x[u]);
+}
+
+template <int K, bool NT, bool PF>
 __global__ __launch_bounds__(256) void k_mixed_narrow(MixedArgs a)
 {
-    constexpr int U = 4;
+    constexpr int U = PF ? 8 : 4;
     constexpr size_t kTile = (size_t)kWave * U;
     const size_t waves = (size_t)gridDim.x * (blockDim.x / kWave);
     const size_t wave = (size_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     const size_t lane = threadIdx.x % kWave;
-    for (size_t t = wave; t * kTile < a.nvec; t += waves) {
-        const size_t base = t * kTile + lane;
-        u32x4 x[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const size_t v = base + (size_t)u * kWave;
-            x[u] = v < a.nvec ? ld<NT>(a.src[0], v) : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const size_t v = base + (size_t)u * kWave;
-            if (v >= a.nvec) continue;
-            if constexpr (K == 2) {
-                u32x2 w = {x[u][0] ^ x[u][1], x[u][2] ^ x[u][3]};
-                if constexpr (NT) __builtin_nontemporal_store(w, static_cast<u32x2*>(a.dst) + v);
-                else static_cast<u32x2*>(a.dst)[v] = w;
-            } else {
-                uint32_t w = x[u][0] ^ x[u][1] ^ x[u][2] ^ x[u][3];
-                if constexpr (NT) __builtin_nontemporal_store(w, static_cast<uint32_t*>(a.dst) + v);
-                else static_cast<uint32_t*>(a.dst)[v] = w;
+    const size_t ntiles = a.nvec / kTile;
+    if constexpr (PF) {
+        if (wave < ntiles) {
+            u32x4 xa[U], xb[U];
+            size_t t = wave;
+            size_t n = (ntiles - t + waves - 1) / waves;
+            mixed_narrow_load<K, NT, U>(xa, a, t, lane);
+            for (;;) {
+                if (n == 1) { mixed_narrow_store<K, NT, U>(xa, a, t, lane); break; }
+                mixed_narrow_load<K, NT, U>(xb, a, t + waves, lane);
+                mixed_narrow_store<K, NT, U>(xa, a, t, lane);
+                t += waves;
+                --n;
+                if (n == 1) { mixed_narrow_store<K, NT, U>(xb, a, t, lane); break; }
+                mixed_narrow_load<K, NT, U>(xa, a, t + waves, lane);
+                mixed_narrow_store<K, NT, U>(xb, a, t, lane);
+                t += waves;
+                --n;
             }
+        }
+    } else {
+        for (size_t t = wave; t < ntiles; t += waves) {
+            u32x4 x[U];
+            mixed_narrow_load<K, NT, U>(x, a, t, lane);
+            mixed_narrow_store<K, NT, U>(x, a, t, lane);
+        }
+    }
+    if (ntiles * kTile < a.nvec && wave == ntiles % waves) {
+        for (int u = 0; u < U; ++u) {
+            const size_t v = ntiles * kTile + lane + (size_t)u * kWave;
+            if (v >= a.nvec) break;
+            narrow_store<K, false>(a, v, ld16(a.src[0], v));
         }
     }
 }
@@ -226,17 +323,24 @@ const std::array<StreamsFn, kMaxSrc> kCopyStreams[2] = {
 
 using MixedFn = void (*)(MixedArgs);
 
-template <bool NT, int... I>
+template <bool NT, bool PF, int... I>
 constexpr std::array<MixedFn, sizeof...(I)> mixed_reduce_table(std::integer_sequence<int, I...>)
 {
-    return {{&k_mixed_reduce<I + 1, NT>...}};
+    return {{&k_mixed_reduce<I + 1, NT, PF>...}};
 }
 
-const std::array<MixedFn, kMaxSrc> kMixedReduce[2] = {
-    mixed_reduce_table<false>(std::make_integer_sequence<int, kMaxSrc>{}),
-    mixed_reduce_table<true>(std::make_integer_sequence<int, kMaxSrc>{})};
-const MixedFn kMixedNarrow[2][2] = {{k_mixed_narrow<2, false>, k_mixed_narrow<2, true>},
-                                    {k_mixed_narrow<4, false>, k_mixed_narrow<4, true>}};
+// [prefetch][nontemporal][nsrc - 1]
+const std::array<MixedFn, kMaxSrc> kMixedReduce[2][2] = {
+    {mixed_reduce_table<false, false>(std::make_integer_sequence<int, kMaxSrc>{}),
+     mixed_reduce_table<true, false>(std::make_integer_sequence<int, kMaxSrc>{})},
+    {mixed_reduce_table<false, true>(std::make_integer_sequence<int, kMaxSrc>{}),
+     mixed_reduce_table<true, true>(std::make_integer_sequence<int, kMaxSrc>{})}};
+// [prefetch][K == 4][nontemporal]
+const MixedFn kMixedNarrow[2][2][2] = {
+    {{k_mixed_narrow<2, false, false>, k_mixed_narrow<2, true, false>},
+     {k_mixed_narrow<4, false, false>, k_mixed_narrow<4, true, false>}},
+    {{k_mixed_narrow<2, false, true>, k_mixed_narrow<2, true, true>},
+     {k_mixed_narrow<4, false, true>, k_mixed_narrow<4, true, true>}}};
 
 typedef void (*StreamFn)(const void*, void*, size_t, u32x4);
 const StreamFn kStream[4][2] = {
@@ -279,10 +383,11 @@ rx_status_t rxtest_stream(int kind, const void* src, void* dst, size_t bytes, in
 }
 
 rx_status_t rxtest_stream_mixed(int kind, const void* const* srcs, int nsrc, void* dst,
-                                size_t src_bytes, int wgs_per_cu, int nontemporal,
+                                size_t src_bytes, int wgs_per_cu, int nontemporal, int prefetch,
                                 hipStream_t stream)
 {
     if (kind < 0 || kind > 2 || wgs_per_cu < 1 || wgs_per_cu > 8) return RX_ERR_ARG;
+    if (prefetch != 0 && prefetch != 1) return RX_ERR_ARG;
     if (nsrc < 1 || nsrc > RX_MAX_SRC || (kind != 0 && nsrc != 1)) return RX_ERR_ARG;
     if (!srcs || !dst) return RX_ERR_NULL;
     for (int j = 0; j < nsrc; ++j)
@@ -296,7 +401,8 @@ rx_status_t rxtest_stream_mixed(int kind, const void* const* srcs, int nsrc, voi
     a.dst = dst;
     a.nvec = src_bytes / 16;
     const int nt = nontemporal ? 1 : 0;
-    const rx::MixedFn fn = kind == 0 ? rx::kMixedReduce[nt][nsrc - 1] : rx::kMixedNarrow[kind - 1][nt];
+    const rx::MixedFn fn = kind == 0 ? rx::kMixedReduce[prefetch][nt][nsrc - 1]
+                                     : rx::kMixedNarrow[prefetch][kind - 1][nt];
     const unsigned grid = (unsigned)(rx::device_cu_count() * wgs_per_cu);
     void* params[] = {&a};
     const hipError_t e = hipLaunchKernel((const void*)fn, dim3(grid), dim3(256), params, 0, stream);

@@ -84,6 +84,34 @@ __device__ __forceinline__ u32x4 fold_vec(const void* const* src, size_t v)
     return out;
 }
 
+// Fold 16-byte vectors already loaded (x[r] from source r), in source order
+// 0..N-1 per element; returns the narrowed 16 bytes.
+template <int DT, int N>
+__device__ __forceinline__ u32x4 fold_regs(const u32x4 (&x)[N])
+{
+    u32x4 out;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if constexpr (DT == 0) {
+            float acc = bits_f32(x[0][k]);
+#pragma unroll
+            for (int r = 1; r < N; ++r)
+                acc = acc + bits_f32(x[r][k]);
+            out[k] = __builtin_bit_cast(uint32_t, acc);
+        } else {
+            float lo = bf16_lo(x[0][k]);
+            float hi = bf16_hi(x[0][k]);
+#pragma unroll
+            for (int r = 1; r < N; ++r) {
+                lo = lo + bf16_lo(x[r][k]);
+                hi = hi + bf16_hi(x[r][k]);
+            }
+            out[k] = pack_bf16(lo, hi);
+        }
+    }
+    return out;
+}
+
 // One element i (tail of a count that is not a multiple of 16 bytes).
 template <int DT, int N>
 __device__ __forceinline__ float fold_vec_tail(const void* const* src, size_t i)

@@ -678,25 +678,31 @@ def stream_ceilings(torch, rx, timer):
     streaming kernels over 1 GiB, and the mixed read/write ceilings (the
     hot-path kernels' access patterns with XOR in place of their arithmetic:
     reduce N:1 over N sources, 2:1 and 4:1 narrowing), best over 1, 2, 4
-    and 8 workgroups per CU with and without nontemporal hints. Bytes counted:
-    read + written."""
+    and 8 workgroups per CU with and without nontemporal hints (the mixed ones
+    also with and without the next-tile prefetch). Bytes counted: read +
+    written."""
     nbytes = 1 << 30
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
     dst = torch.empty_like(src)
     sink = torch.empty(rx.rxtest_stream_sink_bytes(8) // 4, dtype=torch.float32, device="cuda:0")
     out = {}
 
-    def best(kind, run_for, moved, reps=None):
+    def best(kind, run_for, moved, reps=None, pfs=(None,)):
         reps = nreps(6) if reps is None else reps
         b = None
         for wgs in (1, 2, 4, 8):
             for nt in (False, True):
-                us = timer.us_per_launch([lambda wgs=wgs, nt=nt: run_for(wgs, nt)] * reps,
-                                         f"ceiling/{kind}@wgs{wgs}nt{int(nt)}")
-                gbs = moved / (us * 1e-6) / 1e9
-                if b is None or gbs > b["GB/s"]:
-                    b = {"GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
-                         "wgs_per_cu": wgs, "nontemporal": nt}
+                for pf in pfs:
+                    tag = f"ceiling/{kind}@wgs{wgs}nt{int(nt)}" + ("" if pf is None else f"pf{int(pf)}")
+                    call = (lambda wgs=wgs, nt=nt: run_for(wgs, nt)) if pf is None else \
+                        (lambda wgs=wgs, nt=nt, pf=pf: run_for(wgs, nt, pf))
+                    us = timer.us_per_launch([call] * reps, tag)
+                    gbs = moved / (us * 1e-6) / 1e9
+                    if b is None or gbs > b["GB/s"]:
+                        b = {"GB/s": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+                             "wgs_per_cu": wgs, "nontemporal": nt}
+                        if pf is not None:
+                            b["prefetch"] = pf
         return b
 
     out["read"] = best("read", lambda wgs, nt: rx.rxtest_stream(rx.RXTEST_READ, src, sink, nbytes, wgs, nt),
@@ -713,13 +719,13 @@ def stream_ceilings(torch, rx, timer):
     for k in (8, 3, 2):
         per = nbytes // k // 16 * 16
         srcs = [src.view(torch.uint8)[j * per:(j + 1) * per] for j in range(k)]
-        out[f"reduce{k}"] = best(f"reduce{k}", lambda wgs, nt, srcs=srcs, per=per: rx.rxtest_stream_mixed(
-            rx.RXTEST_MIXED_REDUCE, srcs, dst.view(torch.uint8)[:per], per, wgs, nt),
-            (k + 1) * per)
+        out[f"reduce{k}"] = best(f"reduce{k}", lambda wgs, nt, pf, srcs=srcs, per=per: rx.rxtest_stream_mixed(
+            rx.RXTEST_MIXED_REDUCE, srcs, dst.view(torch.uint8)[:per], per, wgs, nt, pf),
+            (k + 1) * per, pfs=(False, True))
     for kind, k in ((rx.RXTEST_MIXED_NARROW2, 2), (rx.RXTEST_MIXED_NARROW4, 4)):
-        out[f"narrow{k}"] = best(f"narrow{k}", lambda wgs, nt, kind=kind, k=k: rx.rxtest_stream_mixed(
-            kind, [src], dst.view(torch.uint8)[:nbytes // k], nbytes, wgs, nt),
-            nbytes + nbytes // k)
+        out[f"narrow{k}"] = best(f"narrow{k}", lambda wgs, nt, pf, kind=kind, k=k: rx.rxtest_stream_mixed(
+            kind, [src], dst.view(torch.uint8)[:nbytes // k], nbytes, wgs, nt, pf),
+            nbytes + nbytes // k, pfs=(False, True))
     del src, dst, sink
     torch.cuda.empty_cache()
     return out

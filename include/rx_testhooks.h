@@ -56,7 +56,8 @@ rx_status_t rxtest_group_max(const uint32_t* in, size_t nwaves, int g,
  *                   alone); src, dst and bytes are ignored apart from the
  *                   alignment check, and it launches even for bytes == 0.
  * Launch: wgs_per_cu (1..8) workgroups of 256 threads per compute unit,
- * grid-stride over wave tiles of 4 vectors per lane; nontemporal != 0 uses
+ * grid-stride over whole wave tiles of 4 vectors per lane, the partial last
+ * tile after the loop; nontemporal != 0 uses
  * nontemporal loads and stores. bytes, src and dst must be multiples of 16
  * (RX_ERR_ALIGN); src and dst must not overlap. */
 rx_status_t rxtest_stream(int kind, const void* src, void* dst, size_t bytes,
@@ -75,11 +76,14 @@ rx_status_t rxtest_stream(int kind, const void* src, void* dst, size_t bytes,
  *                    BF16 (2:1) and FP32 (4:1) input.
  * srcs is a host array of device pointers (16-B aligned); src_bytes a
  * multiple of 16. Launch as rxtest_stream: wgs_per_cu (1..8) workgroups of
- * 256 threads per compute unit, grid-stride over wave tiles of 4 vectors per
- * lane (2 for more than 8 sources); nontemporal != 0 uses nontemporal loads
- * and stores. dst must not overlap a source. */
+ * 256 threads per compute unit, grid-stride over wave tiles (reduce: 4
+ * vectors per lane, 2 for more than 8 sources; narrow: 4, or 8 with the
+ * prefetch), whole tiles in the loop and a partial last tile after it;
+ * nontemporal != 0 uses nontemporal loads and stores; prefetch (0 or 1)
+ * = 1 loads each wave's next tile into a second register buffer before it
+ * writes the current one. dst must not overlap a source. */
 rx_status_t rxtest_stream_mixed(int kind, const void* const* srcs, int nsrc, void* dst,
-                                size_t src_bytes, int wgs_per_cu, int nontemporal,
+                                size_t src_bytes, int wgs_per_cu, int nontemporal, int prefetch,
                                 hipStream_t stream);
 
 /* The tree step's memory pattern without its arithmetic (a floor for it):

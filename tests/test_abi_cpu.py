@@ -266,17 +266,18 @@ def test_stream_ceiling_validation():
     assert L.rxtest_stream_sink_bytes(9) == 0
     m = L.rxtest_stream_mixed
     two = ptrs(FAKE, FAKE + 4096)
-    assert m(3, two, 2, FAKE, 1024, 1, 0, None) == ARG          # kind
-    assert m(1, two, 2, FAKE, 1024, 1, 0, None) == ARG          # narrow takes one source
-    assert m(0, two, 0, FAKE, 1024, 1, 0, None) == ARG
-    assert m(0, ptrs(*[FAKE] * 17), 17, FAKE, 1024, 1, 0, None) == ARG
-    assert m(0, two, 2, FAKE, 1024, 9, 0, None) == ARG          # workgroups per CU
-    assert m(0, None, 2, FAKE, 1024, 1, 0, None) == NULL
-    assert m(0, two, 2, None, 1024, 1, 0, None) == NULL
-    assert m(0, ptrs(FAKE, 0), 2, FAKE, 1024, 1, 0, None) == NULL
-    assert m(0, ptrs(FAKE, FAKE + 8), 2, FAKE, 1024, 1, 0, None) == ALIGN
-    assert m(2, ptrs(FAKE), 1, FAKE, 1000, 1, 0, None) == ALIGN  # bytes % 16
-    assert m(0, two, 2, FAKE, 0, 1, 0, None) == OK               # nothing to do
+    assert m(3, two, 2, FAKE, 1024, 1, 0, 0, None) == ARG          # kind
+    assert m(1, two, 2, FAKE, 1024, 1, 0, 0, None) == ARG          # narrow takes one source
+    assert m(0, two, 0, FAKE, 1024, 1, 0, 0, None) == ARG
+    assert m(0, ptrs(*[FAKE] * 17), 17, FAKE, 1024, 1, 0, 0, None) == ARG
+    assert m(0, two, 2, FAKE, 1024, 9, 0, 0, None) == ARG          # workgroups per CU
+    assert m(0, two, 2, FAKE, 1024, 1, 0, 2, None) == ARG          # prefetch is 0 or 1
+    assert m(0, None, 2, FAKE, 1024, 1, 0, 0, None) == NULL
+    assert m(0, two, 2, None, 1024, 1, 0, 0, None) == NULL
+    assert m(0, ptrs(FAKE, 0), 2, FAKE, 1024, 1, 0, 0, None) == NULL
+    assert m(0, ptrs(FAKE, FAKE + 8), 2, FAKE, 1024, 1, 0, 0, None) == ALIGN
+    assert m(2, ptrs(FAKE), 1, FAKE, 1000, 1, 0, 0, None) == ALIGN  # bytes % 16
+    assert m(0, two, 2, FAKE, 0, 1, 0, 0, None) == OK               # nothing to do
     c = L.rxtest_copy_streams
     d2 = ptrs(FAKE + 8192, FAKE + 12288)
     assert c(two, d2, 0, 0, 1024, 1, 64, None) == ARG            # stream count

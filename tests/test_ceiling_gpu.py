@@ -58,17 +58,18 @@ def test_stream_empty_launch_touches_nothing():
 
 
 @pytest.mark.parametrize("nbytes", SIZES)
-@pytest.mark.parametrize("wgs,nt", [(1, False), (4, True)])
-def test_stream_mixed(nbytes, wgs, nt):
+@pytest.mark.parametrize("wgs,nt,pf", [(1, False, False), (4, True, False), (1, True, True), (2, False, True)])
+def test_stream_mixed(nbytes, wgs, nt, pf):
     """Mixed read/write ceilings: reduce over 1, 3, 8 and 16 sources (XOR of
     the sources, 16-byte word by word) and the 2:1 / 4:1 narrowing folds,
-    exactly over the range (guard bands intact)."""
-    log(f"mixed ceiling kernels bytes={nbytes} wgs={wgs} nt={nt}")
+    exactly over the range (guard bands intact), with and without the
+    next-tile prefetch."""
+    log(f"mixed ceiling kernels bytes={nbytes} wgs={wgs} nt={nt} prefetch={pf}")
     hosts = [random_bytes(nbytes, 7 * nbytes + r) for r in range(16)]
     srcs = [torch.from_numpy(h).to(DEV) for h in hosts]
     for nsrc in (1, 3, 8, 16):
         out = Guarded(nbytes, torch.uint8)
-        rx.rxtest_stream_mixed(rx.RXTEST_MIXED_REDUCE, srcs[:nsrc], out.t, nbytes, wgs, nt)
+        rx.rxtest_stream_mixed(rx.RXTEST_MIXED_REDUCE, srcs[:nsrc], out.t, nbytes, wgs, nt, pf)
         torch.cuda.synchronize()
         want = np.bitwise_xor.reduce(np.stack(hosts[:nsrc]), axis=0)
         assert np.array_equal(out.t.cpu().numpy(), want), f"reduce nsrc={nsrc}"
@@ -76,7 +77,7 @@ def test_stream_mixed(nbytes, wgs, nt):
     words = hosts[0].view(np.uint32).reshape(-1, 4)
     for kind, k in ((rx.RXTEST_MIXED_NARROW2, 2), (rx.RXTEST_MIXED_NARROW4, 4)):
         out = Guarded(nbytes // k, torch.uint8)
-        rx.rxtest_stream_mixed(kind, srcs[:1], out.t, nbytes, wgs, nt)
+        rx.rxtest_stream_mixed(kind, srcs[:1], out.t, nbytes, wgs, nt, pf)
         torch.cuda.synchronize()
         if k == 2:
             want = np.stack([words[:, 0] ^ words[:, 1], words[:, 2] ^ words[:, 3]], axis=1)

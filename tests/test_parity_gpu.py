@@ -90,16 +90,19 @@ def test_flat_in_place(dtype):
 
 
 @pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
-@pytest.mark.parametrize("n", [2, 8, 16])
-def test_flat_large_variant_ragged(n, dtype):
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8, 13, 16])
+@pytest.mark.parametrize("extra", [5, 1021 * 8 + 3])
+def test_flat_large_variant_ragged(n, dtype, extra):
     # above the decode-size threshold: wave tiles with deferred stores and a
-    # grid-stride loop; ragged element tail; also in place
-    count = 3 * (1 << 20) + 5
+    # grid-stride loop (whole tiles only for few sources or FP32 up to 8,
+    # the rest of the message in a second launch); ragged element tail; also
+    # in place
+    count = 3 * (1 << 20) + extra
     srcs = [G.fill(count, dtype, G.NORMAL_OUTLIER, seed=1500 + n, rank=r) for r in range(n)]
     ref = O.reduce_flat(srcs, dtype)
     g = Guarded(count, TD[dtype])
     ts = [to_gpu(s) for s in srcs]
-    log(f"flat large n={n} dtype={dtype}")
+    log(f"flat large n={n} dtype={dtype} count={count}")
     rx.rx_reduce_flat(ts, g.t)
     sync()
     got = to_host(g.t)
