@@ -19,6 +19,43 @@ LaunchPolicy policy_drr_fp32_out() { return {64u, 256u, 2u}; }
 // measured 14% faster than 2 at 8 x 512 MiB BF16 (6 and 8 slower again).
 LaunchPolicy policy_drr_one_source() { return {64u, 256u, 4u}; }
 
+// The range [lo, hi) of a as a range that starts at code 0: every pointer
+// offset to code lo (a block multiple), lo = 0, hi = hi - lo.
+DrrArgs from_lo(const DrrArgs& a, int nsrc)
+{
+    DrrArgs arg = a;
+    const size_t esz = a.hp_bf16 ? 2 : 4;
+    const size_t blk0 = a.lo / (size_t)a.block;
+    for (int j = 0; j < nsrc; ++j) {
+        arg.codes[j] = static_cast<const uint8_t*>(a.codes[j]) + a.lo;
+        arg.scales[j] = a.scales[j] + blk0;
+    }
+    for (int j = 0; j < kMaxSrc; ++j) {
+        if (a.out_codes[j]) arg.out_codes[j] = static_cast<uint8_t*>(a.out_codes[j]) + a.lo;
+        if (a.out_scales[j]) arg.out_scales[j] = a.out_scales[j] + blk0;
+        if (a.out_hps[j]) arg.out_hps[j] = static_cast<uint8_t*>(a.out_hps[j]) + a.lo * esz;
+    }
+    if (a.out_hp) arg.out_hp = static_cast<uint8_t*>(a.out_hp) + a.lo * esz;
+    arg.lo = 0;
+    arg.hi = a.hi - a.lo;
+    return arg;
+}
+
+// Codes [a.lo + done, a.hi) -- less than one tile -- in k_drr (fns' layout),
+// one 64-thread workgroup; nothing when done covers the range. done is a
+// multiple of the tile, so of the block.
+hipError_t launch_rest(const DrrArgs& a, int nsrc, int fmt, int r, size_t done, const DrrFns& fns, hipStream_t s)
+{
+    if (a.lo + done >= a.hi)
+        return hipSuccess;
+    DrrArgs arg = a;
+    arg.lo = a.lo + done;
+    arg.xcd_ranges = 0;
+    void* params[] = {&arg};
+    return launch_logged("k_drr (ragged remainder)", (const void*)fns.fn[fmt][r][nsrc - 1], dim3(1), dim3(kWave),
+                         params, s);
+}
+
 }  // namespace
 
 hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStream_t s)
@@ -65,43 +102,20 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
         // against 524 us); a ragged remainder (less than one tile) in the
         // unstaged 16 x 1 kernel, launched after it.
         const size_t whole = len / tile;
-        hipError_t e = hipSuccess;
         if (whole) {
             dim3 grid, blk;
             launch_geometry(whole * kWave, false, policy_drr(), grid, blk);
-            // every pointer offset to the start of the range: the staged
-            // kernel runs over [0, whole * 1024)
-            DrrArgs arg = a;
-            const size_t esz = a.hp_bf16 ? 2 : 4;
-            const size_t blk0 = a.lo / (size_t)a.block;   // lo is a block multiple
-            for (int j = 0; j < nsrc; ++j) {
-                arg.codes[j] = static_cast<const uint8_t*>(a.codes[j]) + a.lo;
-                arg.scales[j] = a.scales[j] + blk0;
-            }
-            for (int j = 0; j < kMaxSrc; ++j) {
-                if (a.out_codes[j]) arg.out_codes[j] = static_cast<uint8_t*>(a.out_codes[j]) + a.lo;
-                if (a.out_scales[j]) arg.out_scales[j] = a.out_scales[j] + blk0;
-                if (a.out_hps[j]) arg.out_hps[j] = static_cast<uint8_t*>(a.out_hps[j]) + a.lo * esz;
-            }
-            if (a.out_hp) arg.out_hp = static_cast<uint8_t*>(a.out_hp) + a.lo * esz;
-            arg.lo = 0;
+            DrrArgs arg = from_lo(a, nsrc);
             arg.hi = whole * tile;
             arg.xcd_ranges = whole <= (size_t)(a.hp_bf16 ? 512 : 128) * cus ? 1 : 0;
             void* params[] = {&arg};
-            e = launch_logged("k_drr_staged", (const void*)drr_fns_16x1_staged(a.hp_bf16).fn[fmt][r][nsrc - 1],
-                              grid, blk, params, s);
+            const hipError_t e = launch_logged("k_drr_staged",
+                                               (const void*)drr_fns_16x1_staged(a.hp_bf16).fn[fmt][r][nsrc - 1],
+                                               grid, blk, params, s);
             if (e != hipSuccess)
                 return e;
         }
-        if (len % tile) {
-            DrrArgs arg = a;
-            arg.lo = a.lo + whole * tile;      // a multiple of 1024, so of the block
-            arg.xcd_ranges = 0;
-            void* params[] = {&arg};
-            e = launch_logged("k_drr (ragged remainder)", (const void*)drr_fns_16x1().fn[fmt][r][nsrc - 1],
-                              dim3(1), dim3(kWave), params, s);
-        }
-        return e;
+        return launch_rest(a, nsrc, fmt, r, whole * tile, drr_fns_16x1(), s);
     }
     LaunchPolicy pol = (cpc == 4 && u == 4) ? policy_drr_fp32_out()
                      : nsrc == 1            ? policy_drr_one_source()
@@ -148,6 +162,26 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
         const size_t range = (lines + kXcds - 1) / kXcds * tiles_per_line;
         arg.xcd_ranges = (int)range;
         grid = dim3((unsigned)(kXcds * range));
+    }
+    if (!small && cpc == 16) {
+        // 16 x 1: whole tiles in k_drr_whole (no partial-tile path in its
+        // loop), then the ragged remainder (less than one tile) in k_drr.
+        // The one-source 4 x 4 and 8 x 2 layouts keep k_drr: as whole-tile
+        // kernels they measured slower (8 x 16M codes E4M3/128 to FP32
+        // 16.4 -> 17.3 us; 256M codes E5M2/256 to BF16 140.4 -> 142.2 us).
+        const size_t whole = len / tile;
+        if (whole) {
+            DrrArgs warg = from_lo(a, nsrc);
+            warg.hi = whole * tile;
+            warg.xcd_ranges = arg.xcd_ranges;
+            launch_geometry(whole * kWave, false, pol, grid, blk);
+            void* params[] = {&warg};
+            const hipError_t e = launch_logged("k_drr_whole", (const void*)drr_fns_16x1_whole().fn[fmt][r][nsrc - 1],
+                                               grid, blk, params, s);
+            if (e != hipSuccess)
+                return e;
+        }
+        return launch_rest(a, nsrc, fmt, r, whole * tile, drr_fns_16x1(), s);
     }
     void* params[] = {&arg};
     const DrrFn fn = cpc == 4 ? (u == 4 ? drr_fns_4x4().fn[fmt][r][nsrc - 1] : drr_fns_4x1().fn[fmt][r][nsrc - 1])

@@ -402,6 +402,28 @@ def test_drr_large_variant_ragged(fmt, block):
                 assert bits_equal(g, r), f"{name}: " + first_mismatch(g, r)
 
 
+@pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 256), (O.E4M3, 32),
+                                       (O.E5M2, 512), (O.E4M3, 1024)])
+def test_drr_one_source_large_ragged(fmt, block):
+    # one source above the decode-size threshold (the separate
+    # dequantization and a one-source requantization): whole tiles in the
+    # 4 x 4 (FP32 output, blocks up to 256), 8 x 2 (BF16 output, blocks up
+    # to 512) or 16 x 1 layout, then the ragged remainder in a second launch
+    count = (1 << 21) + 1000 * 8 + 7
+    srcs = [G.fill(count, O.FP32, G.LAPLACE, seed=4800 + block, rank=0)]
+    codes, scales = O.quant_fp8(srcs, O.FP32, fmt, block)
+    for mode, hp_dtype, want_hp in ((O.DRR_SUM, O.BF16, True), (O.DRR_SUM, O.FP32, True),
+                                    (O.DRR_REQUANT, O.FP32, False), (O.DRR_REQUANT, O.BF16, True),
+                                    (O.DRR_REQUANT, O.FP32, True)):
+        log(f"drr one source fmt={fmt} block={block} mode={mode} hp={hp_dtype}/{want_hp}")
+        got = _drr_gpu(codes, scales, fmt, block, mode, hp_dtype, want_hp, count)
+        ref = O.dequant_reduce_requant(codes, scales, fmt, block, mode, hp_dtype, want_hp)
+        for name, g, r in zip(("codes", "scales", "hp"), got, ref):
+            assert (g is None) == (r is None)
+            if g is not None:
+                assert bits_equal(g, r), f"{name}: " + first_mismatch(g, r)
+
+
 @pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 512)])
 def test_lp_tree_large_variant_ragged(fmt, block):
     # chunks above the decode-size threshold, ragged message end
