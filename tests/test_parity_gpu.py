@@ -792,6 +792,8 @@ def _lp_all(ts, fmt, block, n, count):
         hp=torch.empty(count, dtype=dt, device=DEV),
         lpc=[torch.empty(count, dtype=torch.uint8, device=DEV) for _ in range(n)],
         lps=[torch.empty(nb, dtype=torch.float32, device=DEV) for _ in range(n)],
+        oc2=torch.empty(count, dtype=torch.uint8, device=DEV),
+        osc2=torch.empty(nb, dtype=torch.float32, device=DEV),
     )
 
     def run():
@@ -802,6 +804,8 @@ def _lp_all(ts, fmt, block, n, count):
                                      out["oc"], out["osc"], out["hp"])
         rx.rx_lp_reduce_scatter_chunk_bcast(out["codes"], out["scales"], fmt, block, 2,
                                             out["lpc"], out["lps"])
+        rx.rx_dequant_reduce_requant(out["codes"], out["scales"], fmt, block, rx.RX_DRR_REQUANT,
+                                     out["oc2"], out["osc2"])
     return out, run
 
 
@@ -810,16 +814,19 @@ def _snapshot(out):
     return {k: [to_host(t).copy() for t in flat(v)] for k, v in out.items()}
 
 
-@pytest.mark.parametrize("count", [262_144, 3 * (1 << 20) + 77])
-def test_graph_replays_match_eager(count):
+@pytest.mark.parametrize("count,dtype", [(262_144, G.BF16), (3 * (1 << 20) + 77, G.BF16),
+                                         (3 * (1 << 20) + 77, G.FP32)])
+def test_graph_replays_match_eager(count, dtype):
     """All five entry points captured in one HIP graph (no memset nodes: the
-    library enqueues kernels only), replayed three times with new inputs
-    written eagerly between replays; every replay must equal an eager run on
-    the same inputs."""
-    n, fmt, block = 8, "e5m2", 256
-    inputs = [[to_gpu(G.fill(count, G.BF16, G.NORMAL, seed=6000 + 10 * k + count % 7, rank=r))
+    library enqueues kernels only; large ragged messages take two launches
+    in the quantizer, the FP32 flat reduce and DRR), replayed three times
+    with new inputs written eagerly between replays; every replay must equal
+    an eager run on the same inputs."""
+    n = 8
+    fmt, block = ("e5m2", 256) if dtype == G.BF16 else ("e4m3", 128)
+    inputs = [[to_gpu(G.fill(count, dtype, G.NORMAL, seed=6000 + 10 * k + count % 7, rank=r))
                for r in range(n)] for k in range(3)]
-    ts = [torch.empty(count, dtype=torch.bfloat16, device=DEV) for _ in range(n)]
+    ts = [torch.empty(count, dtype=TD[dtype], device=DEV) for _ in range(n)]
     out, run = _lp_all(ts, fmt, block, n, count)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -830,7 +837,7 @@ def test_graph_replays_match_eager(count):
                 t.zero_()
 
     for k in range(3):
-        log(f"graph replay {k} count={count}")
+        log(f"graph replay {k} count={count} dtype={dtype}")
         for t, x in zip(ts, inputs[k]):
             t.copy_(x)
         clear()
