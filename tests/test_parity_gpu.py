@@ -283,6 +283,22 @@ def test_quant_whole_tiles_ragged(dtype, fmt, block, mib):
             assert res is None, res
 
 
+@pytest.mark.parametrize("dtype,fmt,block", [(O.FP32, O.E4M3, 64), (O.BF16, O.E5M2, 512)])
+def test_quant_sixteen_sources_large(dtype, fmt, block):
+    # 16 sources (the most the argument tables hold) above the decode-size
+    # threshold: tile t of the whole-tile kernel belongs to source
+    # t / tiles_per_source, the ragged end of every source in a second launch
+    n = 16
+    count = (1 << 20) + 3 * block + 11
+    log(f"quant 16 sources dtype={dtype} fmt={fmt} block={block} count={count}")
+    srcs = [G.fill(count, dtype, G.NORMAL_OUTLIER, seed=3700 + r, rank=r) for r in range(n)]
+    gc, gs = _quant_gpu(srcs, dtype, fmt, block, count)
+    rc, rs = O.quant_fp8(srcs, dtype, fmt, block)
+    for j in range(n):
+        assert bits_equal(gc[j], rc[j]), f"codes src={j}: " + first_mismatch(gc[j], rc[j])
+        assert bits_equal(gs[j], rs[j]), f"scales src={j}: " + first_mismatch(gs[j], rs[j])
+
+
 def test_quant_degenerate_blocks():
     # zero blocks, tiny blocks (FMAX / A overflows), huge values, -0
     count, block = 1024, 128
