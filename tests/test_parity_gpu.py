@@ -792,6 +792,78 @@ def test_group_max_lane_layout():
 
 
 # ---------------------------------------------------------------------------
+# Launch-shape thresholds
+# ---------------------------------------------------------------------------
+
+# Counts at and beside the size thresholds at which the launchers change
+# kernel, tile or workgroups per CU on a 256-CU MI355X (on another device the
+# cases still hold, at other launch shapes): every side must give the
+# oracle's bits.
+_BOUNDARY_CASES = [
+    # flat reduce: decode-size below 131,072 16-byte vectors
+    ("flat", O.FP32, 8, (1 << 19) - 1), ("flat", O.FP32, 8, 1 << 19), ("flat", O.FP32, 8, (1 << 19) + 1),
+    ("flat", O.BF16, 3, (1 << 20) - 1), ("flat", O.BF16, 3, (1 << 20) + 1),
+    ("flat", O.BF16, 8, (1 << 20) + 1), ("flat", O.FP32, 13, (1 << 19) + 3),
+    # quantizer, 8 FP32 sources: decode-size below 2,048 tiles of 1024,
+    # four workgroups per CU below 16,384, two above
+    ("quant", O.FP32, 8, 255 * 1024), ("quant", O.FP32, 8, 255 * 1024 + 1), ("quant", O.FP32, 8, 256 * 1024),
+    ("quant", O.FP32, 8, 2047 * 1024), ("quant", O.FP32, 8, 2047 * 1024 + 1), ("quant", O.BF16, 8, 2048 * 1024 + 7),
+    # DRR: decode-size below 1,024 tiles of 1024 codes; codes only: four
+    # workgroups per CU below 8,192 tiles
+    ("drr", O.FP32, 8, 1023 * 1024), ("drr", O.FP32, 8, 1023 * 1024 + 1), ("drr", O.FP32, 8, 1024 * 1024 + 5),
+    ("drr", O.FP32, 8, 8191 * 1024 - 5), ("drr", O.FP32, 8, 8192 * 1024 + 3),
+    # one-pass LP allreduce: BF16 8-byte lanes up to 512 tiles of 512,
+    # 256-thread workgroups up to 4,096 tiles (FP32: tiles of 256)
+    ("lp", O.BF16, 8, 512 * 512), ("lp", O.BF16, 8, 512 * 512 + 1), ("lp", O.BF16, 8, 4096 * 512 + 1),
+    ("lp", O.FP32, 8, 4096 * 256), ("lp", O.FP32, 8, 4096 * 256 + 1),
+]
+
+
+@pytest.mark.parametrize("what,dtype,n,count", _BOUNDARY_CASES)
+def test_launch_policy_boundaries(what, dtype, n, count):
+    fmt, block = (O.E4M3, 128) if dtype == O.FP32 else (O.E5M2, 256)
+    log(f"boundary {what} dtype={dtype} n={n} count={count}")
+    srcs = [G.fill(count, dtype, G.NORMAL_OUTLIER, seed=9500 + r + count % 101, rank=r) for r in range(n)]
+    if what == "flat":
+        g = Guarded(count, TD[dtype])
+        rx.rx_reduce_flat([to_gpu(x) for x in srcs], g.t)
+        sync()
+        ref = O.reduce_flat(srcs, dtype)
+        got = to_host(g.t)
+        assert bits_equal(got, ref), first_mismatch(got, ref)
+        assert g.guards_intact()
+    elif what == "quant":
+        gc, gs = _quant_gpu(srcs, dtype, fmt, block, count)
+        rc, rs = O.quant_fp8(srcs, dtype, fmt, block)
+        for j in range(n):
+            assert bits_equal(gc[j], rc[j]), f"codes src={j}: " + first_mismatch(gc[j], rc[j])
+            assert bits_equal(gs[j], rs[j]), f"scales src={j}: " + first_mismatch(gs[j], rs[j])
+    elif what == "drr":
+        codes, scales = O.quant_fp8(srcs, dtype, fmt, block)
+        cases = ((codes, scales, O.DRR_REQUANT, O.FP32, False),      # codes only (16 x 1)
+                 (codes, scales, O.DRR_REQUANT, O.BF16, True),       # several sources: staged
+                 (codes[:1], scales[:1], O.DRR_SUM, O.FP32, True),   # one source, FP32 (4 x 4)
+                 (codes[:1], scales[:1], O.DRR_SUM, O.BF16, True))   # one source, BF16 (8 x 2)
+        for cs_, ss_, mode, hp_dtype, want_hp in cases:
+            got = _drr_gpu(cs_, ss_, fmt, block, mode, hp_dtype, want_hp, count)
+            ref = O.dequant_reduce_requant(cs_, ss_, fmt, block, mode, hp_dtype, want_hp)
+            for name, g_, r_ in zip(("codes", "scales", "hp"), got, ref):
+                assert (g_ is None) == (r_ is None)
+                if g_ is not None:
+                    assert bits_equal(g_, r_), f"mode={mode} n={len(cs_)} {name}: " + first_mismatch(g_, r_)
+    else:
+        ts = [to_gpu(x) for x in srcs]
+        ws = torch.empty(rx.rx_allreduce_local_workspace(n, count, block), dtype=torch.uint8, device=DEV)
+        rx.rx_allreduce_local(ts, rx.RX_ALGO_LOWPREC, FMTS[fmt], block, ws)
+        sync()
+        ref = [x.copy() for x in srcs]
+        O.allreduce_local(ref, dtype, O.ALGO_LOWPREC, fmt, block)
+        for j in range(n):
+            got = to_host(ts[j])
+            assert bits_equal(got, ref[j]), f"rank={j}: " + first_mismatch(got, ref[j])
+
+
+# ---------------------------------------------------------------------------
 # HIP graphs and concurrent streams
 # ---------------------------------------------------------------------------
 
