@@ -166,22 +166,51 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
     if (!small && cpc == 16) {
         // 16 x 1: whole tiles in k_drr_whole (no partial-tile path in its
         // loop), then the ragged remainder (less than one tile) in k_drr.
-        // The one-source 4 x 4 and 8 x 2 layouts keep k_drr: as whole-tile
-        // kernels they measured slower (8 x 16M codes E4M3/128 to FP32
-        // 16.4 -> 17.3 us; 256M codes E5M2/256 to BF16 140.4 -> 142.2 us).
+        // Codes only to one destination from 512 tiles per CU: the
+        // prefetching k_drr_pf at one workgroup per CU, XCD-contiguous
+        // (8 x 128M codes E5M2/256: 207.7 -> 204.6 us; 8 x 256M: 441.8 ->
+        // 425.4 us; at 8 x 16M it was 3% slower than k_drr_whole).
+        const bool pf = single_codes && tiles >= (size_t)512 * cus;
         const size_t whole = len / tile;
         if (whole) {
             DrrArgs warg = from_lo(a, nsrc);
             warg.hi = whole * tile;
-            warg.xcd_ranges = arg.xcd_ranges;
-            launch_geometry(whole * kWave, false, pol, grid, blk);
+            warg.xcd_ranges = pf ? 1 : arg.xcd_ranges;
+            LaunchPolicy wpol = pol;
+            if (pf)
+                wpol.max_wgs_per_cu = 1;
+            launch_geometry(whole * kWave, false, wpol, grid, blk);
             void* params[] = {&warg};
-            const hipError_t e = launch_logged("k_drr_whole", (const void*)drr_fns_16x1_whole().fn[fmt][r][nsrc - 1],
-                                               grid, blk, params, s);
+            const DrrFn wfn = pf ? drr_fns_pf().codes16[fmt][nsrc - 1] : drr_fns_16x1_whole().fn[fmt][r][nsrc - 1];
+            const hipError_t e = launch_logged(pf ? "k_drr_pf" : "k_drr_whole", (const void*)wfn, grid, blk, params, s);
             if (e != hipSuccess)
                 return e;
         }
         return launch_rest(a, nsrc, fmt, r, whole * tile, drr_fns_16x1(), s);
+    }
+    if (!small && r == kDrrSum && nsrc == 1 && ((cpc == 4 && u == 4) || (cpc == 8 && u == 2))) {
+        // The one-source dequantization in 4 x 4 (FP32) or 8 x 2 (BF16):
+        // whole tiles in the prefetching k_drr_pf at two workgroups per CU,
+        // XCD-contiguous (16M codes E4M3/128 to FP32: 16.36 -> 15.66 us, 64M:
+        // 59.2 -> 57.7 us; 64M codes E5M2/256 to BF16: 36.2 -> 35.0 us,
+        // 256M: 140.6 -> 139.6 us), then the ragged remainder in k_drr. As
+        // whole-tile kernels without the prefetch these layouts measured
+        // slower than k_drr (16M codes to FP32 16.4 -> 17.3 us).
+        const size_t whole = len / tile;
+        if (whole) {
+            DrrArgs warg = from_lo(a, nsrc);
+            warg.hi = whole * tile;
+            warg.xcd_ranges = 1;
+            LaunchPolicy wpol = pol;
+            wpol.max_wgs_per_cu = 2;
+            launch_geometry(whole * kWave, false, wpol, grid, blk);
+            void* params[] = {&warg};
+            const DrrFn wfn = cpc == 4 ? drr_fns_pf().sum44[fmt] : drr_fns_pf().sum82[fmt];
+            const hipError_t e = launch_logged("k_drr_pf (one source)", (const void*)wfn, grid, blk, params, s);
+            if (e != hipSuccess)
+                return e;
+        }
+        return launch_rest(a, nsrc, fmt, r, whole * tile, cpc == 4 ? drr_fns_4x4() : drr_fns_8x2(), s);
     }
     void* params[] = {&arg};
     const DrrFn fn = cpc == 4 ? (u == 4 ? drr_fns_4x4().fn[fmt][r][nsrc - 1] : drr_fns_4x1().fn[fmt][r][nsrc - 1])

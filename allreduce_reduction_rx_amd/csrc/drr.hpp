@@ -34,6 +34,15 @@ const DrrFns& drr_fns_4x1();
 const DrrFns& drr_fns_16x1_staged(int hp_bf16);
 // Whole-tile kernels (k_drr_whole), 16 x 1
 const DrrFns& drr_fns_16x1_whole();
+// Prefetching whole-tile kernels (k_drr_pf): codes only (one destination)
+// in 16 x 1, [fmt][nsrc - 1]; the one-source dequantization (SUM) in 4 x 4
+// and 8 x 2, [fmt]
+struct DrrPfFns {
+    DrrFn codes16[2][kMaxSrc];
+    DrrFn sum44[2];
+    DrrFn sum82[2];
+};
+const DrrPfFns& drr_fns_pf();
 
 namespace drr_detail {
 
@@ -262,54 +271,17 @@ __device__ __forceinline__ void staged_out(void* const* outs, size_t c_tile, u32
 // per rank (the low-precision tree step's push); kDrrRequantAll -> only the
 // dequantized result, into N buffers out_hps[j] (every rank's final values
 // in a one-device allreduce).
-// One wave tile of k_drr. WHOLE: every chunk of the tile lies inside the
-// range (all tiles but a ragged last one); that instance has no per-lane
-// bounds branches around its loads and stores.
-template <int F, int N, bool REQUANT, int CPC, int U, int OUT, bool WHOLE>
-__device__ __forceinline__ void drr_tile(const DrrArgs& a, uint32_t t, int lane, size_t c0,
-                                         size_t count, int bshift, int lpb)
+// The arithmetic and stores of one wave tile whose codes and scales are in
+// registers (x, sc: chunk u of source r; c, e, b: this lane's chunk index,
+// first code and block of chunk u; whole / valid: chunk u lies wholly /
+// partly inside the range): dequantize, sum in source order, then store the
+// sum (SUM) or requantize and store as OUT says.
+template <int F, int N, bool REQUANT, int CPC, int U, int OUT>
+__device__ __forceinline__ void drr_finish(const DrrArgs& a, const Chunk<CPC> (&x)[N][U], const float (&sc)[N][U],
+                                           const size_t (&c)[U], const size_t (&e)[U], const size_t (&b)[U],
+                                           const bool (&whole)[U], const bool (&valid)[U], size_t count, int lane,
+                                           int lpb)
 {
-    size_t c[U], e[U], b[U];
-    bool whole[U], valid[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        c[u] = c0 + ((size_t)t * U + u) * kWave + lane;  // this lane's chunk u
-        e[u] = c[u] * CPC;
-        whole[u] = WHOLE || e[u] + CPC <= count;
-        valid[u] = WHOLE || e[u] < count;
-        b[u] = e[u] >> bshift;
-    }
-
-    Chunk<CPC> x[N][U];
-    float sc[N][U];
-#pragma unroll
-    for (int r = 0; r < N; ++r) {
-        const uint8_t* cp = static_cast<const uint8_t*>(a.codes[r]);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if constexpr (WHOLE || CPC * U == 4) {
-                // whole tiles; and the decode-size layout's partial tile, byte
-                // by byte in every lane (4 loads per source, no branches, one
-                // wait for all sources)
-                x[r][u] = load_chunk<CPC>(cp, c[u], e[u], count, WHOLE);
-            } else {
-                // a large layout's partial tile: whole chunks load as vectors
-                // and only the chunk that straddles the end byte by byte
-                // (byte loads in every lane would hold CPC x U x N registers
-                // for the whole kernel)
-                if (whole[u])
-                    x[r][u] = load_chunk<CPC>(cp, c[u], e[u], count, true);
-                else if (valid[u])
-                    x[r][u] = load_chunk<CPC>(cp, c[u], e[u], count, false);
-                else {
-#pragma unroll
-                    for (int q = 0; q < CPC / 4; ++q) x[r][u].w[q] = 0u;
-                }
-            }
-            sc[r][u] = valid[u] ? a.scales[r][b[u]] : 0.0f;
-        }
-    }
-
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         float S[CPC];
@@ -372,6 +344,56 @@ __device__ __forceinline__ void drr_tile(const DrrArgs& a, uint32_t t, int lane,
     }
 }
 
+// One wave tile of k_drr. WHOLE: every chunk of the tile lies inside the
+// range (all tiles but a ragged last one); that instance has no per-lane
+// bounds branches around its loads and stores.
+template <int F, int N, bool REQUANT, int CPC, int U, int OUT, bool WHOLE>
+__device__ __forceinline__ void drr_tile(const DrrArgs& a, uint32_t t, int lane, size_t c0,
+                                         size_t count, int bshift, int lpb)
+{
+    size_t c[U], e[U], b[U];
+    bool whole[U], valid[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        c[u] = c0 + ((size_t)t * U + u) * kWave + lane;  // this lane's chunk u
+        e[u] = c[u] * CPC;
+        whole[u] = WHOLE || e[u] + CPC <= count;
+        valid[u] = WHOLE || e[u] < count;
+        b[u] = e[u] >> bshift;
+    }
+
+    Chunk<CPC> x[N][U];
+    float sc[N][U];
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+        const uint8_t* cp = static_cast<const uint8_t*>(a.codes[r]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if constexpr (WHOLE || CPC * U == 4) {
+                // whole tiles; and the decode-size layout's partial tile, byte
+                // by byte in every lane (4 loads per source, no branches, one
+                // wait for all sources)
+                x[r][u] = load_chunk<CPC>(cp, c[u], e[u], count, WHOLE);
+            } else {
+                // a large layout's partial tile: whole chunks load as vectors
+                // and only the chunk that straddles the end byte by byte
+                // (byte loads in every lane would hold CPC x U x N registers
+                // for the whole kernel)
+                if (whole[u])
+                    x[r][u] = load_chunk<CPC>(cp, c[u], e[u], count, true);
+                else if (valid[u])
+                    x[r][u] = load_chunk<CPC>(cp, c[u], e[u], count, false);
+                else {
+#pragma unroll
+                    for (int q = 0; q < CPC / 4; ++q) x[r][u].w[q] = 0u;
+                }
+            }
+            sc[r][u] = valid[u] ? a.scales[r][b[u]] : 0.0f;
+        }
+    }
+    drr_finish<F, N, REQUANT, CPC, U, OUT>(a, x, sc, c, e, b, whole, valid, count, lane, lpb);
+}
+
 template <int F, int N, bool REQUANT, int CPC, int U, int OUT>
 __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
 {
@@ -427,6 +449,87 @@ __global__ __launch_bounds__(256) void k_drr_whole(DrrArgs a)
     const int bshift = __builtin_ctz((unsigned)a.block);
     for (uint32_t t = wave; t < ntiles; t += step)
         drr_tile<F, N, REQUANT, CPC, U, OUT, true>(a, t, lane, 0, a.hi, bshift, lpb);
+}
+
+// Codes and scales of whole tile t (every chunk inside the range) into
+// registers.
+template <int N, int CPC, int U>
+__device__ __forceinline__ void drr_load_whole(Chunk<CPC> (&x)[N][U], float (&sc)[N][U], const DrrArgs& a, uint32_t t,
+                                               int lane, int bshift)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const size_t c = ((size_t)t * U + u) * kWave + lane;
+        const size_t e = c * CPC;
+#pragma unroll
+        for (int r = 0; r < N; ++r) {
+            x[r][u] = load_chunk<CPC>(static_cast<const uint8_t*>(a.codes[r]), c, e, a.hi, true);
+            sc[r][u] = a.scales[r][e >> bshift];
+        }
+    }
+}
+
+template <int F, int N, bool REQUANT, int CPC, int U, int OUT>
+__device__ __forceinline__ void drr_finish_whole(const Chunk<CPC> (&x)[N][U], const float (&sc)[N][U],
+                                                 const DrrArgs& a, uint32_t t, int lane, int bshift, int lpb)
+{
+    size_t c[U], e[U], b[U];
+    bool yes[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        c[u] = ((size_t)t * U + u) * kWave + lane;
+        e[u] = c[u] * CPC;
+        b[u] = e[u] >> bshift;
+        yes[u] = true;
+    }
+    drr_finish<F, N, REQUANT, CPC, U, OUT>(a, x, sc, c, e, b, yes, yes, a.hi, lane, lpb);
+}
+
+// k_drr_whole with the next tile's codes and scales loaded into a second
+// register buffer before the current tile's arithmetic (the two buffers in
+// turn and the wave's last tile peeled off, so that no register copy crosses
+// the loop and every prefetch in it is unconditional). With one or two
+// workgroups per CU a wave's arithmetic otherwise leaves its loads idle:
+// codes only, 8 x 256M codes E5M2/256: 441.8 -> 425.4 us (one workgroup per
+// CU); one source to FP32, 16M codes E4M3/128: 16.36 -> 15.66 us; to BF16,
+// 64M codes E5M2/256: 36.2 -> 35.0 us (two per CU).
+template <int F, int N, bool REQUANT, int CPC, int U, int OUT>
+__global__ __launch_bounds__(256) void k_drr_pf(DrrArgs a)
+{
+    const int lane = lane_id();
+    const uint32_t wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t waves_per_wg = blockDim.x / kWave;
+    constexpr size_t kTile = (size_t)kWave * CPC * U;
+    const uint32_t ntiles = (uint32_t)(a.hi / kTile);
+    const uint32_t wg = a.xcd_ranges ? xcd_contiguous(blockIdx.x, gridDim.x) : blockIdx.x;
+    uint32_t t = wg * waves_per_wg + wave_in_wg;
+    const uint32_t step = gridDim.x * waves_per_wg;
+    const int lpb = a.block / CPC;
+    const int bshift = __builtin_ctz((unsigned)a.block);
+    if (t >= ntiles)
+        return;
+    Chunk<CPC> xa[N][U], xb[N][U];
+    float sa[N][U], sb[N][U];
+    uint32_t n = (ntiles - t + step - 1) / step;   // tiles of this wave, >= 1
+    drr_load_whole<N, CPC, U>(xa, sa, a, t, lane, bshift);
+    for (;;) {
+        if (n == 1) {
+            drr_finish_whole<F, N, REQUANT, CPC, U, OUT>(xa, sa, a, t, lane, bshift, lpb);
+            break;
+        }
+        drr_load_whole<N, CPC, U>(xb, sb, a, t + step, lane, bshift);
+        drr_finish_whole<F, N, REQUANT, CPC, U, OUT>(xa, sa, a, t, lane, bshift, lpb);
+        t += step;
+        --n;
+        if (n == 1) {
+            drr_finish_whole<F, N, REQUANT, CPC, U, OUT>(xb, sb, a, t, lane, bshift, lpb);
+            break;
+        }
+        drr_load_whole<N, CPC, U>(xa, sa, a, t + step, lane, bshift);
+        drr_finish_whole<F, N, REQUANT, CPC, U, OUT>(xb, sb, a, t, lane, bshift, lpb);
+        t += step;
+        --n;
+    }
 }
 
 // The 16 x 1 layout with the high-precision output (FP32, or BF16 when
@@ -556,6 +659,25 @@ DrrFns make_whole_fns()
     fill_whole_row<1, true, CPC, U, kDrrRequant>(t.fn[1][kDrrRequant], seq);
     fill_whole_row<1, true, CPC, U, kDrrRequantPush>(t.fn[1][kDrrRequantPush], seq);
     fill_whole_row<1, true, CPC, U, kDrrRequantAll>(t.fn[1][kDrrRequantAll], seq);
+    return t;
+}
+
+template <int F, int... I>
+void fill_pf_codes_row(DrrFn* row, std::integer_sequence<int, I...>)
+{
+    ((row[I] = &k_drr_pf<F, I + 1, true, 16, 1, kDrrRequant>), ...);
+}
+
+inline DrrPfFns make_pf_fns()
+{
+    DrrPfFns t{};
+    const auto seq = std::make_integer_sequence<int, kMaxSrc>{};
+    fill_pf_codes_row<0>(t.codes16[0], seq);
+    fill_pf_codes_row<1>(t.codes16[1], seq);
+    t.sum44[0] = &k_drr_pf<0, 1, false, 4, 4, kDrrSum>;
+    t.sum44[1] = &k_drr_pf<1, 1, false, 4, 4, kDrrSum>;
+    t.sum82[0] = &k_drr_pf<0, 1, false, 8, 2, kDrrSum>;
+    t.sum82[1] = &k_drr_pf<1, 1, false, 8, 2, kDrrSum>;
     return t;
 }
 

@@ -69,7 +69,7 @@ _COMMON = ["rx_device.hpp", "rx_internal.hpp", "api.hip"]
 _FLAT = ["reduce.hip", "reduce_common.hpp"] + _COMMON
 _TREE = ["tree.hip", "reduce_common.hpp"] + _COMMON
 _QUANT = ["quant.hip"] + _COMMON
-_DRR = ["drr.hpp", "drr.hip", "drr_16x1.hip", "drr_16x1s.hip", "drr_16x1w.hip", "drr_8x2.hip",
+_DRR = ["drr.hpp", "drr.hip", "drr_16x1.hip", "drr_16x1s.hip", "drr_16x1w.hip", "drr_pf.hip", "drr_8x2.hip",
         "drr_4x4.hip", "drr_4x1.hip"] + _COMMON
 _LP = ["allreduce_lp.hip", "quant.hip", "drr.hpp", "drr.hip"] + _COMMON
 KERNEL_SOURCES = {

@@ -440,6 +440,54 @@ def test_drr_one_source_large_ragged(fmt, block):
                 assert bits_equal(g, r), f"{name}: " + first_mismatch(g, r)
 
 
+def test_drr_codes_only_prefetch_ragged():
+    """Codes only from 8 sources at 512 tiles of 1024 codes per CU and more
+    (on a 256-CU MI355X): the prefetching whole-tile kernel at one workgroup
+    per CU, then the ragged remainder. The codes come from the GPU's
+    quantizer on rxgen input and are checked against the oracle's quantizer
+    first; DRR is then compared with the oracle's DRR of the oracle's codes,
+    every code and scale, in windows of whole blocks on a thread pool."""
+    n, fmt, block = 8, O.E4M3, 128
+    count = (1 << 27) + 5003
+    nb = -(-count // block)
+    log(f"drr codes only prefetch count={count}")
+    srcs = [G.fill(count, O.BF16, G.LAPLACE, seed=4900 + r, rank=r) for r in range(n)]
+    ts = [to_gpu(x) for x in srcs]
+    codes = [torch.empty(count, dtype=torch.uint8, device=DEV) for _ in range(n)]
+    scales = [torch.empty(nb, dtype=torch.float32, device=DEV) for _ in range(n)]
+    rx.rx_quant_fp8(ts, FMTS[fmt], block, codes, scales)
+    del ts
+    oc = Guarded(count, torch.uint8)
+    osc = Guarded(nb, torch.float32)
+    rx.rx_dequant_reduce_requant(codes, scales, FMTS[fmt], block, rx.RX_DRR_REQUANT, oc.t, osc.t)
+    sync()
+    assert oc.guards_intact() and osc.guards_intact()
+    g_codes = [c.cpu().numpy() for c in codes]
+    g_scales = [q.cpu().numpy() for q in scales]
+    g_oc, g_os = to_host(oc.t), to_host(osc.t)
+    del codes, scales, oc, osc
+    torch.cuda.empty_cache()
+    win = 8192 * block
+
+    def check(i0):
+        i1 = min(i0 + win, count)
+        b0, b1 = i0 // block, -(-i1 // block)
+        rc, rs = O.quant_fp8([x[i0:i1] for x in srcs], O.BF16, fmt, block)
+        for r in range(n):
+            if not bits_equal(g_codes[r][i0:i1], rc[r]) or not bits_equal(g_scales[r][b0:b1], rs[r]):
+                return f"quantizer rank {r} window [{i0}, {i1})"
+        r_oc, r_os, _ = O.dequant_reduce_requant(rc, rs, fmt, block, O.DRR_REQUANT, O.FP32, False)
+        if not bits_equal(g_oc[i0:i1], r_oc):
+            return f"codes window [{i0}, {i1}): " + first_mismatch(g_oc[i0:i1], r_oc)
+        if not bits_equal(g_os[b0:b1], r_os):
+            return f"scales window [{i0}, {i1}): " + first_mismatch(g_os[b0:b1], r_os)
+        return None
+
+    with ThreadPoolExecutor(_pool_size()) as ex:
+        for res in ex.map(check, range(0, count, win)):
+            assert res is None, res
+
+
 @pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 512)])
 def test_lp_tree_large_variant_ragged(fmt, block):
     # chunks above the decode-size threshold, ragged message end
