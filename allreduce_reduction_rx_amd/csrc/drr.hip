@@ -101,17 +101,27 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
         // 152 us; BF16: 8 x 64M 119.8 against 122.1 us, 8 x 256M 513
         // against 524 us); a ragged remainder (less than one tile) in the
         // unstaged 16 x 1 kernel, launched after it.
+        // Requantization from 256 tiles per CU: the prefetching
+        // k_drr_staged_pf at one workgroup per CU in plain order (8 x 256M
+        // codes E5M2/256 with BF16 output 502.1 -> 481.4 us, 8 x 64M with FP32
+        // output 144.8 -> 143.3 us; at 8 x 16M, 64 tiles per CU, it was 1.7%
+        // slower).
         const size_t whole = len / tile;
         if (whole) {
+            const bool pf = r == kDrrRequant && whole >= (size_t)256 * cus;
+            LaunchPolicy pol = policy_drr();
+            if (pf)
+                pol.max_wgs_per_cu = 1;
             dim3 grid, blk;
-            launch_geometry(whole * kWave, false, policy_drr(), grid, blk);
+            launch_geometry(whole * kWave, false, pol, grid, blk);
             DrrArgs arg = from_lo(a, nsrc);
             arg.hi = whole * tile;
-            arg.xcd_ranges = whole <= (size_t)(a.hp_bf16 ? 512 : 128) * cus ? 1 : 0;
+            arg.xcd_ranges = !pf && whole <= (size_t)(a.hp_bf16 ? 512 : 128) * cus ? 1 : 0;
             void* params[] = {&arg};
-            const hipError_t e = launch_logged("k_drr_staged",
-                                               (const void*)drr_fns_16x1_staged(a.hp_bf16).fn[fmt][r][nsrc - 1],
-                                               grid, blk, params, s);
+            const DrrFn fn = pf ? drr_fns_pf().staged[a.hp_bf16 ? 1 : 0][fmt][nsrc - 1]
+                                : drr_fns_16x1_staged(a.hp_bf16).fn[fmt][r][nsrc - 1];
+            const hipError_t e = launch_logged(pf ? "k_drr_staged_pf" : "k_drr_staged", (const void*)fn, grid, blk,
+                                               params, s);
             if (e != hipSuccess)
                 return e;
         }

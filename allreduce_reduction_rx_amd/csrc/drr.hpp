@@ -36,11 +36,13 @@ const DrrFns& drr_fns_16x1_staged(int hp_bf16);
 const DrrFns& drr_fns_16x1_whole();
 // Prefetching whole-tile kernels (k_drr_pf): codes only (one destination)
 // in 16 x 1, [fmt][nsrc - 1]; the one-source dequantization (SUM) in 4 x 4
-// and 8 x 2, [fmt]
+// and 8 x 2, [fmt]; the staged requantization with a high-precision output
+// (k_drr_staged_pf), [hp_bf16][fmt][nsrc - 1]
 struct DrrPfFns {
     DrrFn codes16[2][kMaxSrc];
     DrrFn sum44[2];
     DrrFn sum82[2];
+    DrrFn staged[2][2][kMaxSrc];
 };
 const DrrPfFns& drr_fns_pf();
 
@@ -542,6 +544,78 @@ __global__ __launch_bounds__(256) void k_drr_pf(DrrArgs a)
 // for kDrrRequantAll). The range offset and an out_hp check, both removed
 // here, made the compiler schedule the loop 4% slower (8 x 64M codes
 // E5M2/256 with BF16 output: 127.3 against 121.7 us).
+// The staged kernel's tile t in two parts: its codes and scales into
+// registers, then the sums, requantization and stores (the output through
+// the wave's LDS stage).
+template <int N>
+__device__ __forceinline__ void drr_staged_load(Chunk<16> (&x)[N], float (&sc)[N], const DrrArgs& a, uint32_t t,
+                                                int lane, int bshift)
+{
+    const size_t c = (size_t)t * kWave + lane;
+    const size_t e = c * 16;
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+        x[r] = load_chunk<16>(static_cast<const uint8_t*>(a.codes[r]), c, e, a.hi, true);
+        sc[r] = a.scales[r][e >> bshift];
+    }
+}
+
+template <int F, int N, bool REQUANT, int OUT, bool BF16>
+__device__ __forceinline__ void drr_staged_finish(const Chunk<16> (&x)[N], const float (&sc)[N], const DrrArgs& a,
+                                                  uint32_t t, int lane, int lpb, int bshift, u32x4* stage)
+{
+    const size_t c_tile = (size_t)t * kWave;
+    const size_t c = c_tile + lane;
+    const size_t e = c * 16;
+    const size_t b = e >> bshift;
+    float S[16];
+    dequant<F, 16>(x[0].w, sc[0], S);
+#pragma unroll
+    for (int r = 1; r < N; ++r) {
+        float d[16];
+        dequant<F, 16>(x[r].w, sc[r], d);
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            S[k] = S[k] + d[k];
+    }
+    if constexpr (!REQUANT) {
+        staged_out<1, BF16>(&a.out_hp, c_tile, stage, lane, S);
+        return;
+    }
+    float m = __builtin_fabsf(S[0]);
+#pragma unroll
+    for (int k = 1; k < 16; ++k)
+        m = __builtin_fmaxf(m, __builtin_fabsf(S[k]));
+    const float A = bits_f32(group_max_rt(__builtin_bit_cast(uint32_t, m), lpb));
+    float s2, r2;
+    block_scale<F>(A, s2, r2);
+    uint32_t q[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        q[p] = f32x4_to_fp8<F>(clamp_fmax<F>(S[4 * p + 0] * r2), clamp_fmax<F>(S[4 * p + 1] * r2),
+                               clamp_fmax<F>(S[4 * p + 2] * r2), clamp_fmax<F>(S[4 * p + 3] * r2));
+    if constexpr (OUT == kDrrRequantPush) {
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+            store_codes<16>(static_cast<uint8_t*>(a.out_codes[j]), c, e, a.hi, true, q);
+        if ((lane % lpb) == 0) {
+#pragma unroll
+            for (int j = 0; j < N; ++j)
+                store_scale<false>(a.out_scales[j] + b, s2);
+        }
+    } else if constexpr (OUT == kDrrRequant) {
+        store_codes<16>(static_cast<uint8_t*>(a.out_codes[0]), c, e, a.hi, true, q);
+        if ((lane % lpb) == 0)
+            store_scale<false>(a.out_scales[0] + b, s2);
+    }
+    float h[16];
+    dequant<F, 16>(q, s2, h);
+    if constexpr (OUT == kDrrRequantAll)
+        staged_out<N, BF16>(a.out_hps, c_tile, stage, lane, h);
+    else
+        staged_out<1, BF16>(&a.out_hp, c_tile, stage, lane, h);
+}
+
 template <int F, int N, bool REQUANT, int OUT, bool BF16>
 __global__ __launch_bounds__(256) void k_drr_staged(DrrArgs a)
 {
@@ -557,63 +631,55 @@ __global__ __launch_bounds__(256) void k_drr_staged(DrrArgs a)
     u32x4* stage = stage_mem[wave_in_wg];
 
     for (uint32_t t = wave; t < ntiles; t += step) {
-        const size_t c_tile = (size_t)t * kWave;
-        const size_t c = c_tile + lane;
-        const size_t e = c * 16;
-        const size_t b = e >> bshift;
         Chunk<16> x[N];
         float sc[N];
-#pragma unroll
-        for (int r = 0; r < N; ++r) {
-            x[r] = load_chunk<16>(static_cast<const uint8_t*>(a.codes[r]), c, e, a.hi, true);
-            sc[r] = a.scales[r][b];
+        drr_staged_load<N>(x, sc, a, t, lane, bshift);
+        drr_staged_finish<F, N, REQUANT, OUT, BF16>(x, sc, a, t, lane, lpb, bshift, stage);
+    }
+}
+
+// k_drr_staged with the next tile's codes and scales loaded into a second
+// register buffer before the current tile's arithmetic (as k_drr_pf):
+// requantization with the output staged, from 256 tiles per CU at one
+// workgroup per CU (8 x 256M codes E5M2/256 with BF16 output: 500.4 ->
+// 478.1 us; 8 x 64M: 120.3 -> 119.3 us; at 8 x 16M codes with FP32 output,
+// 64 tiles per CU, 1.7% slower).
+template <int F, int N, bool REQUANT, int OUT, bool BF16>
+__global__ __launch_bounds__(256) void k_drr_staged_pf(DrrArgs a)
+{
+    __shared__ u32x4 stage_mem[256 / kWave][kStageSlots];   // one region per wave
+    const int lane = lane_id();
+    const uint32_t wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t wg = a.xcd_ranges ? xcd_contiguous(blockIdx.x, gridDim.x) : blockIdx.x;
+    uint32_t t = wg * (blockDim.x / kWave) + wave_in_wg;
+    const uint32_t step = gridDim.x * (blockDim.x / kWave);
+    const uint32_t ntiles = (uint32_t)(a.hi / ((size_t)kWave * 16));
+    const int lpb = a.block / 16;
+    const int bshift = __builtin_ctz((unsigned)a.block);
+    u32x4* stage = stage_mem[wave_in_wg];
+    if (t >= ntiles)
+        return;
+    Chunk<16> xa[N], xb[N];
+    float sa[N], sb[N];
+    uint32_t n = (ntiles - t + step - 1) / step;   // tiles of this wave, >= 1
+    drr_staged_load<N>(xa, sa, a, t, lane, bshift);
+    for (;;) {
+        if (n == 1) {
+            drr_staged_finish<F, N, REQUANT, OUT, BF16>(xa, sa, a, t, lane, lpb, bshift, stage);
+            break;
         }
-        float S[16];
-        dequant<F, 16>(x[0].w, sc[0], S);
-#pragma unroll
-        for (int r = 1; r < N; ++r) {
-            float d[16];
-            dequant<F, 16>(x[r].w, sc[r], d);
-#pragma unroll
-            for (int k = 0; k < 16; ++k)
-                S[k] = S[k] + d[k];
+        drr_staged_load<N>(xb, sb, a, t + step, lane, bshift);
+        drr_staged_finish<F, N, REQUANT, OUT, BF16>(xa, sa, a, t, lane, lpb, bshift, stage);
+        t += step;
+        --n;
+        if (n == 1) {
+            drr_staged_finish<F, N, REQUANT, OUT, BF16>(xb, sb, a, t, lane, lpb, bshift, stage);
+            break;
         }
-        if constexpr (!REQUANT) {
-            staged_out<1, BF16>(&a.out_hp, c_tile, stage, lane, S);
-            continue;
-        }
-        float m = __builtin_fabsf(S[0]);
-#pragma unroll
-        for (int k = 1; k < 16; ++k)
-            m = __builtin_fmaxf(m, __builtin_fabsf(S[k]));
-        const float A = bits_f32(group_max_rt(__builtin_bit_cast(uint32_t, m), lpb));
-        float s2, r2;
-        block_scale<F>(A, s2, r2);
-        uint32_t q[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-            q[p] = f32x4_to_fp8<F>(clamp_fmax<F>(S[4 * p + 0] * r2), clamp_fmax<F>(S[4 * p + 1] * r2),
-                                   clamp_fmax<F>(S[4 * p + 2] * r2), clamp_fmax<F>(S[4 * p + 3] * r2));
-        if constexpr (OUT == kDrrRequantPush) {
-#pragma unroll
-            for (int j = 0; j < N; ++j)
-                store_codes<16>(static_cast<uint8_t*>(a.out_codes[j]), c, e, a.hi, true, q);
-            if ((lane % lpb) == 0) {
-#pragma unroll
-                for (int j = 0; j < N; ++j)
-                    store_scale<false>(a.out_scales[j] + b, s2);
-            }
-        } else if constexpr (OUT == kDrrRequant) {
-            store_codes<16>(static_cast<uint8_t*>(a.out_codes[0]), c, e, a.hi, true, q);
-            if ((lane % lpb) == 0)
-                store_scale<false>(a.out_scales[0] + b, s2);
-        }
-        float h[16];
-        dequant<F, 16>(q, s2, h);
-        if constexpr (OUT == kDrrRequantAll)
-            staged_out<N, BF16>(a.out_hps, c_tile, stage, lane, h);
-        else
-            staged_out<1, BF16>(&a.out_hp, c_tile, stage, lane, h);
+        drr_staged_load<N>(xa, sa, a, t + step, lane, bshift);
+        drr_staged_finish<F, N, REQUANT, OUT, BF16>(xb, sb, a, t, lane, lpb, bshift, stage);
+        t += step;
+        --n;
     }
 }
 
@@ -668,12 +734,22 @@ void fill_pf_codes_row(DrrFn* row, std::integer_sequence<int, I...>)
     ((row[I] = &k_drr_pf<F, I + 1, true, 16, 1, kDrrRequant>), ...);
 }
 
+template <int F, bool BF16, int... I>
+void fill_pf_staged_row(DrrFn* row, std::integer_sequence<int, I...>)
+{
+    ((row[I] = &k_drr_staged_pf<F, I + 1, true, kDrrRequant, BF16>), ...);
+}
+
 inline DrrPfFns make_pf_fns()
 {
     DrrPfFns t{};
     const auto seq = std::make_integer_sequence<int, kMaxSrc>{};
     fill_pf_codes_row<0>(t.codes16[0], seq);
     fill_pf_codes_row<1>(t.codes16[1], seq);
+    fill_pf_staged_row<0, false>(t.staged[0][0], seq);
+    fill_pf_staged_row<1, false>(t.staged[0][1], seq);
+    fill_pf_staged_row<0, true>(t.staged[1][0], seq);
+    fill_pf_staged_row<1, true>(t.staged[1][1], seq);
     t.sum44[0] = &k_drr_pf<0, 1, false, 4, 4, kDrrSum>;
     t.sum44[1] = &k_drr_pf<1, 1, false, 4, 4, kDrrSum>;
     t.sum82[0] = &k_drr_pf<0, 1, false, 8, 2, kDrrSum>;

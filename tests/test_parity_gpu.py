@@ -488,6 +488,55 @@ def test_drr_codes_only_prefetch_ragged():
             assert res is None, res
 
 
+@pytest.mark.parametrize("hp_dtype", [O.FP32, O.BF16])
+def test_drr_staged_prefetch_ragged(hp_dtype):
+    """Requantization with the high-precision output staged, at 256 tiles of
+    1024 codes per CU and more (on a 256-CU MI355X): the prefetching staged
+    kernel at one workgroup per CU, then the ragged remainder. GPU quantizer
+    output checked against the oracle's first; DRR's codes, scales and output
+    against the oracle's DRR of the oracle's codes, in windows of whole
+    blocks on a thread pool."""
+    n, fmt, block = 3, O.E4M3, 128
+    count = (1 << 26) + 5003
+    nb = -(-count // block)
+    log(f"drr staged prefetch hp={hp_dtype} count={count}")
+    srcs = [G.fill(count, O.FP32, G.LAPLACE, seed=4950 + r, rank=r) for r in range(n)]
+    ts = [to_gpu(x) for x in srcs]
+    codes = [torch.empty(count, dtype=torch.uint8, device=DEV) for _ in range(n)]
+    scales = [torch.empty(nb, dtype=torch.float32, device=DEV) for _ in range(n)]
+    rx.rx_quant_fp8(ts, FMTS[fmt], block, codes, scales)
+    del ts
+    oc = Guarded(count, torch.uint8)
+    osc = Guarded(nb, torch.float32)
+    hp = Guarded(count, TD[hp_dtype])
+    rx.rx_dequant_reduce_requant(codes, scales, FMTS[fmt], block, rx.RX_DRR_REQUANT, oc.t, osc.t, hp.t)
+    sync()
+    assert oc.guards_intact() and osc.guards_intact() and hp.guards_intact()
+    g_codes = [c.cpu().numpy() for c in codes]
+    g_scales = [q.cpu().numpy() for q in scales]
+    g_oc, g_os, g_hp = to_host(oc.t), to_host(osc.t), to_host(hp.t)
+    del codes, scales, oc, osc, hp
+    torch.cuda.empty_cache()
+    win = 8192 * block
+
+    def check(i0):
+        i1 = min(i0 + win, count)
+        b0, b1 = i0 // block, -(-i1 // block)
+        rc, rs = O.quant_fp8([x[i0:i1] for x in srcs], O.FP32, fmt, block)
+        for r in range(n):
+            if not bits_equal(g_codes[r][i0:i1], rc[r]) or not bits_equal(g_scales[r][b0:b1], rs[r]):
+                return f"quantizer rank {r} window [{i0}, {i1})"
+        r_oc, r_os, r_hp = O.dequant_reduce_requant(rc, rs, fmt, block, O.DRR_REQUANT, hp_dtype, True)
+        for name, g_, r_ in (("codes", g_oc[i0:i1], r_oc), ("scales", g_os[b0:b1], r_os), ("hp", g_hp[i0:i1], r_hp)):
+            if not bits_equal(g_, r_):
+                return f"{name} window [{i0}, {i1}): " + first_mismatch(g_, r_)
+        return None
+
+    with ThreadPoolExecutor(_pool_size()) as ex:
+        for res in ex.map(check, range(0, count, win)):
+            assert res is None, res
+
+
 @pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 512)])
 def test_lp_tree_large_variant_ragged(fmt, block):
     # chunks above the decode-size threshold, ragged message end
