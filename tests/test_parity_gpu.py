@@ -183,11 +183,12 @@ def test_tree_shapes(n, dtype):
 @pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
 @pytest.mark.parametrize("n", [3, 8, 16])
 def test_tree_large_variant_ragged(n, dtype):
-    # chunks above the decode-size threshold (the tiled kernel for BF16),
-    # ragged message end, first and last rank
+    # chunks above the decode-size threshold (whole tiles and the rest of the
+    # chunk for BF16), ragged message end; ranks 0 and 1 (chunks from the
+    # start and from inside the message) and the last (a short chunk)
     count = n * (1 << 20) + 9
     srcs = [G.fill(count, dtype, G.NORMAL, seed=2500 + n, rank=r) for r in range(n)]
-    for k in (0, n - 1):
+    for k in (0, 1, n - 1):
         log(f"tree large n={n} dtype={dtype} rank={k}")
         _tree_case(srcs, dtype, count, k)
 
