@@ -228,6 +228,32 @@ __global__ __launch_bounds__(256) void k_quant(QuantArgs a)
     }
 }
 
+// Decode-size messages whose sources are whole tiles (count a multiple of
+// the tile): one tile per wave and no loop, XCD-contiguous workgroups,
+// nontemporal scale stores (as k_quant's SMALL instances, without the
+// grid-stride loop and the partial-tile path: 8 x 256K BF16 E5M2/256 3.12 ->
+// 3.07 us).
+template <int DT, int F, int BLOCK, int UL>
+__global__ __launch_bounds__(256) void k_quant_tile(QuantArgs a)
+{
+    using Sh = QuantShape<DT, F, BLOCK, UL>;
+    constexpr int U = Sh::kU;
+    const int lane = lane_id();
+    const uint32_t wave_in_wg = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t wg = xcd_contiguous(blockIdx.x, gridDim.x);
+    const uint32_t t = wg * (blockDim.x / kWave) + wave_in_wg;
+    const uint32_t tiles_per_src = (uint32_t)(a.count / Sh::kTileElems);
+    if (t >= tiles_per_src * (uint32_t)a.nsrc)
+        return;
+    const uint32_t j = t / tiles_per_src;
+    const size_t v0 = (size_t)(t - j * tiles_per_src) * Sh::kTileVec;
+    u32x4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        x[u] = ld16_stream(a.src[j], v0 + u * kWave + lane);
+    quant_tile<DT, F, BLOCK, U, true>(x, static_cast<uint8_t*>(a.codes[j]), a.scales[j], v0, a.count, true, lane);
+}
+
 // The U loads of tile t (tile t % tiles_per_src of source t / tiles_per_src).
 template <int DT, int F, int BLOCK, int U>
 __device__ __forceinline__ void load_whole_tile(u32x4 (&x)[U], const QuantArgs& a, uint32_t t,
@@ -306,11 +332,16 @@ __global__ __launch_bounds__(256) void k_quant_whole(QuantArgs a)
 
 using QuantFn = void (*)(QuantArgs);
 
-// Decode-size variant: U = the loads per block.
+// Decode-size variants: U = the loads per block.
 template <int DT, int F, int... L>
 constexpr std::array<QuantFn, sizeof...(L)> quant_row(std::integer_sequence<int, L...>)
 {
     return {{&k_quant<DT, F, (32 << L), loads_per_block<DT, (32 << L)>(), true>...}};
+}
+template <int DT, int F, int... L>
+constexpr std::array<QuantFn, sizeof...(L)> quant_tile_row(std::integer_sequence<int, L...>)
+{
+    return {{&k_quant_tile<DT, F, (32 << L), loads_per_block<DT, (32 << L)>()>...}};
 }
 
 template <int DT, int F, int U, bool PF, int... L>
@@ -333,7 +364,15 @@ struct QuantWholeTable {
         {quant_whole_row<1, 0, U, PF>(std::make_integer_sequence<int, 6>{}),
          quant_whole_row<1, 1, U, PF>(std::make_integer_sequence<int, 6>{})}};
 };
+struct QuantTileTable {
+    std::array<QuantFn, 6> fn[2][2] = {
+        {quant_tile_row<0, 0>(std::make_integer_sequence<int, 6>{}),
+         quant_tile_row<0, 1>(std::make_integer_sequence<int, 6>{})},
+        {quant_tile_row<1, 0>(std::make_integer_sequence<int, 6>{}),
+         quant_tile_row<1, 1>(std::make_integer_sequence<int, 6>{})}};
+};
 const QuantTable kQuantSmall;
+const QuantTileTable kQuantTile;
 const QuantWholeTable<4, false> kQuantWhole4;
 const QuantWholeTable<8, true> kQuantWhole8Pf;
 
@@ -354,8 +393,11 @@ hipError_t launch_quant_tiles(const QuantArgs& a, int src_dtype, int fmt, int bl
     launch_geometry(tiles * kWave, true, policy_quant(), grid, blk);
     QuantArgs arg = a;
     void* params[] = {&arg};
-    return launch_logged("k_quant (decode size)", (const void*)kQuantSmall.fn[src_dtype][fmt][lb], grid, blk,
-                         params, s);
+    // sources of whole tiles: the loop-free kernel (one launch either way)
+    const bool whole = a.count % tile_elems == 0;
+    return launch_logged(whole ? "k_quant_tile (decode size)" : "k_quant (decode size)",
+                         (const void*)(whole ? kQuantTile.fn[src_dtype][fmt][lb] : kQuantSmall.fn[src_dtype][fmt][lb]),
+                         grid, blk, params, s);
 }
 
 }  // namespace
