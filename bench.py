@@ -70,7 +70,7 @@ _FLAT = ["reduce.hip", "reduce_common.hpp"] + _COMMON
 _TREE = ["tree.hip", "reduce_common.hpp"] + _COMMON
 _QUANT = ["quant.hip"] + _COMMON
 _DRR = ["drr.hpp", "drr.hip", "drr_16x1.hip", "drr_16x1s.hip", "drr_16x1w.hip", "drr_pf.hip", "drr_8x2.hip",
-        "drr_4x4.hip", "drr_4x1.hip"] + _COMMON
+        "drr_4x4.hip", "drr_4x1.hip", "drr_4x1t.hip"] + _COMMON
 _LP = ["allreduce_lp.hip", "quant.hip", "drr.hpp", "drr.hip"] + _COMMON
 KERNEL_SOURCES = {
     "reduce_flat": _FLAT, "tree_step": _TREE, "quant_fp8": _QUANT,

@@ -538,6 +538,30 @@ def test_drr_staged_prefetch_ragged(hp_dtype):
             assert res is None, res
 
 
+@pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 256), (O.E4M3, 32)])
+@pytest.mark.parametrize("n", [1, 3, 8, 16])
+def test_drr_decode_whole_tiles(fmt, block, n):
+    # decode-size ranges of whole 256-code tiles (the loop-free kernel): every
+    # mode and output type, and the LP tree step's chunks, which start inside
+    # the message
+    count = 256 * 96
+    srcs = [G.fill(count, O.FP32, G.LAPLACE, seed=4990 + n + block, rank=r) for r in range(n)]
+    codes, scales = O.quant_fp8(srcs, O.FP32, fmt, block)
+    for mode, hp_dtype, want_hp in ((O.DRR_SUM, O.BF16, True), (O.DRR_SUM, O.FP32, True),
+                                    (O.DRR_REQUANT, O.FP32, False), (O.DRR_REQUANT, O.BF16, True),
+                                    (O.DRR_REQUANT, O.FP32, True)):
+        log(f"drr decode whole tiles fmt={fmt} block={block} n={n} mode={mode} hp={hp_dtype}/{want_hp}")
+        got = _drr_gpu(codes, scales, fmt, block, mode, hp_dtype, want_hp, count)
+        ref = O.dequant_reduce_requant(codes, scales, fmt, block, mode, hp_dtype, want_hp)
+        for name, g, r in zip(("codes", "scales", "hp"), got, ref):
+            assert (g is None) == (r is None)
+            if g is not None:
+                assert bits_equal(g, r), f"mode={mode} {name}: " + first_mismatch(g, r)
+    for k in range(n):
+        log(f"lp tree decode whole tiles fmt={fmt} block={block} n={n} rank={k}")
+        _lp_tree_case(codes, scales, fmt, block, k, count, hp_dtype=(None, O.BF16, O.FP32)[k % 3])
+
+
 @pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 512)])
 def test_lp_tree_large_variant_ragged(fmt, block):
     # chunks above the decode-size threshold, ragged message end
