@@ -34,7 +34,8 @@ const DrrFns& drr_fns_4x1();
 const DrrFns& drr_fns_16x1_staged(int hp_bf16);
 // Whole-tile kernels (k_drr_whole), 16 x 1
 const DrrFns& drr_fns_16x1_whole();
-// Decode-size kernels for ranges of whole tiles (k_drr_tile1), 4 x 1
+// Decode-size kernels for ranges of whole tiles (k_drr_tile1), 4 x 1, the
+// SUM and push modes (the other entries null)
 const DrrFns& drr_fns_4x1_tile1();
 // Prefetching whole-tile kernels (k_drr_pf): codes only (one destination)
 // in 16 x 1, [fmt][nsrc - 1]; the one-source dequantization (SUM) in 4 x 4
@@ -434,9 +435,11 @@ __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
 
 // Decode-size ranges of whole tiles: one tile per 64-thread workgroup, XCD
 // x taking tiles [x R, x R + R) (R = xcd_ranges, whole lines of block
-// scales), without k_drr's loop and partial-tile path: 8 x 256K codes
-// E5M2/256 with BF16 output 2.92 -> 2.84 us, the LP tree step's push of a
-// 32K-code chunk 2.54 -> 2.44 us.
+// scales), without k_drr's loop and partial-tile path. Used for the push
+// and SUM modes: the LP tree step's push of a 32K-code chunk 2.54 -> 2.44
+// us, the one-source dequantization and the flat LP sum about 1% faster.
+// The requantization into one destination measured 0.7% slower this way
+// (2.73 -> 2.75 us with the BF16 output) and keeps k_drr.
 template <int F, int N, bool REQUANT, int CPC, int U, int OUT>
 __global__ __launch_bounds__(256) void k_drr_tile1(DrrArgs a)
 {
@@ -737,19 +740,16 @@ void fill_tile1_row(DrrFn* row, std::integer_sequence<int, I...>)
     ((row[I] = &k_drr_tile1<F, I + 1, R, CPC, U, OUT>), ...);
 }
 
+// the SUM and push modes only (the other entries null)
 template <int CPC, int U>
 DrrFns make_tile1_fns()
 {
     DrrFns t{};
     const auto seq = std::make_integer_sequence<int, kMaxSrc>{};
     fill_tile1_row<0, false, CPC, U, kDrrSum>(t.fn[0][kDrrSum], seq);
-    fill_tile1_row<0, true, CPC, U, kDrrRequant>(t.fn[0][kDrrRequant], seq);
     fill_tile1_row<0, true, CPC, U, kDrrRequantPush>(t.fn[0][kDrrRequantPush], seq);
-    fill_tile1_row<0, true, CPC, U, kDrrRequantAll>(t.fn[0][kDrrRequantAll], seq);
     fill_tile1_row<1, false, CPC, U, kDrrSum>(t.fn[1][kDrrSum], seq);
-    fill_tile1_row<1, true, CPC, U, kDrrRequant>(t.fn[1][kDrrRequant], seq);
     fill_tile1_row<1, true, CPC, U, kDrrRequantPush>(t.fn[1][kDrrRequantPush], seq);
-    fill_tile1_row<1, true, CPC, U, kDrrRequantAll>(t.fn[1][kDrrRequantAll], seq);
     return t;
 }
 

@@ -1124,11 +1124,12 @@ def test_allreduce_local_lowprec_every_block(dtype, fmt):
     quantize into the workspace first; ragged counts, 1..16 ranks, and a rank
     of zeros (degenerate blocks, s = r = 1). On a 256-CU MI355X the counts
     reach every launch shape of the one-pass kernel: 8-byte lanes (BF16, up
-    to 512 tiles of 64 16-byte vectors), 256-thread workgroups (up to 4096
+    to 512 tiles of 64 16-byte vectors; one tile per wave without a loop
+    when the count is whole tiles), 256-thread workgroups (up to 4096
     tiles) and the grid-stride launch above."""
     for block in (32, 64, 128, 256, 512, 1024):
         for n, count in ((8, 70001), (3, 4096 + 17), (16, 1000), (1, 513), (4, 300_005),
-                         (8, (1 << 20) + 77)):
+                         (8, (1 << 20) + 77), (8, 65536)):
             log(f"allreduce_local lowprec dtype={dtype} fmt={fmt} block={block} n={n} count={count}")
             srcs = [G.fill(count, dtype, G.NORMAL_OUTLIER, seed=9100 + block + n, rank=r)
                     for r in range(n)]
