@@ -43,7 +43,9 @@ launch, a read and a copy of the decode message's 4 MiB, on one 1 GiB
 rotation) and the tree step's own memory pattern without its arithmetic
 (`tree_step_pattern_floor`, and cfg3's `pattern_floor`: each rank buffer's
 chunk copied into its own destination, the same 2N streams in the same
-allocations and rotation).
+allocations and rotation). cfg3's `offset_layout` times the step and that
+floor again on rank buffers spaced buffer size + 2 KiB apart in one
+allocation, so the 2N chunks do not share their offset modulo 4 MiB.
 """
 from __future__ import annotations
 
@@ -524,6 +526,7 @@ def cfg_tree(torch, rx, G, timer):
     tree["pattern_floor"] = tree_pattern_floor(rx, timer, lambda i: sets[i % nsets][0],
                                                lambda i: sets[i % nsets][1], chunks, e, reps, "tree")
     tree["frac_of_pattern_floor"] = round(tree["pattern_floor"]["us"] / med, 4)
+    tree["offset_layout"] = tree_offset_layout(torch, rx, timer, base, nsets, chunks, e, reps)
     fbytes = (n + 1) * count * e
     freps = auto_reps(fbytes, lo=100)
     flat_out = [torch.empty_like(base[0]) for _ in range(nsets)]
@@ -727,6 +730,42 @@ def stream_ceilings(torch, rx, timer):
             kind, [src], dst.view(torch.uint8)[:nbytes // k], nbytes, wgs, nt, pf),
             nbytes + nbytes // k, pfs=(False, True))
     del src, dst, sink
+    torch.cuda.empty_cache()
+    return out
+
+
+def tree_offset_layout(torch, rx, timer, base, nsets, chunks, e, reps):
+    """The tree step and its pattern floor on rank buffers carved from one
+    allocation at a stride of buffer size + 2 KiB. Separate allocations of a
+    power-of-two size sit at one offset modulo that size, so chunk k of all
+    2N buffers shares its low address bits; here each buffer starts 2 KiB
+    further along. The ranks of a node hold their buffers in their own GPUs'
+    memories, so the aliasing of the one-device layout has no counterpart
+    there; this entry shows what the step costs without it."""
+    n = len(base)
+    nbytes = base[0].numel() * e
+    stride = nbytes + 2048
+    big = torch.empty(nsets * 2 * n * stride, dtype=torch.uint8, device=base[0].device)
+
+    def view(i, j):
+        o = (i * 2 * n + j) * stride
+        return big[o:o + nbytes].view(base[0].dtype)
+
+    sets = [([view(i, j) for j in range(n)], [view(i, n + j) for j in range(n)]) for i in range(nsets)]
+    for srcs, _ in sets:
+        for s, b in zip(srcs, base):
+            s.copy_(b)
+    by_rank = []
+    for k in range(n):
+        by_rank.append(timer.us_per_launch(
+            [lambda i=i, k=k: rx.rx_reduce_scatter_chunk_bcast(sets[i % nsets][0], k, sets[i % nsets][1])
+             for i in range(reps)], f"tree/tree_step_offset@rank{k}"))
+    floor = tree_pattern_floor(rx, timer, lambda i: sets[i % nsets][0], lambda i: sets[i % nsets][1],
+                               chunks, e, reps, "tree_offset")
+    out = {"stride_bytes": stride, "us": round(sorted(by_rank)[n // 2], 3),
+           "us_by_rank": [round(x, 3) for x in by_rank], "pattern_floor": floor}
+    del sets, big
+    torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return out
 
