@@ -209,10 +209,13 @@ __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 // of once per XCD.
 constexpr uint32_t kXcds = 8;
 
-__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t g)
+// XCD x owns q + 1 ids from x (q + 1) if x < r, else q ids from
+// r (q + 1) + (x - r) q; both starts equal x q + min(x, r). Written without a
+// branch, so a kernel's scalar loads are not held behind one.
+__host__ __device__ constexpr uint32_t xcd_contiguous(uint32_t b, uint32_t g)
 {
     const uint32_t q = g / kXcds, r = g % kXcds, x = b % kXcds, i = b / kXcds;
-    return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+    return x * q + (x < r ? x : r) + i;
 }
 
 }  // namespace rx
