@@ -172,8 +172,8 @@ hipError_t launch_drr(const DrrArgs& a, int nsrc, int fmt, bool requant, hipStre
         const size_t range = (lines + kXcds - 1) / kXcds * tiles_per_line;
         arg.xcd_ranges = (int)range;
         grid = dim3((unsigned)(kXcds * range));
-        if (cpc == 4 && len % tile == 0 && (r == kDrrSum || r == kDrrRequantPush)) {
-            // a range of whole tiles, SUM or push: the loop-free kernel
+        if (cpc == 4 && len % tile == 0) {
+            // a range of whole tiles: the loop-free kernel
             void* params[] = {&arg};
             return launch_logged("k_drr_tile1 (decode size)", (const void*)drr_fns_4x1_tile1().fn[fmt][r][nsrc - 1],
                                  grid, blk, params, s);

@@ -34,8 +34,7 @@ const DrrFns& drr_fns_4x1();
 const DrrFns& drr_fns_16x1_staged(int hp_bf16);
 // Whole-tile kernels (k_drr_whole), 16 x 1
 const DrrFns& drr_fns_16x1_whole();
-// Decode-size kernels for ranges of whole tiles (k_drr_tile1), 4 x 1, the
-// SUM and push modes (the other entries null)
+// Decode-size kernels for ranges of whole tiles (k_drr_tile1), 4 x 1
 const DrrFns& drr_fns_4x1_tile1();
 // Prefetching whole-tile kernels (k_drr_pf): codes only (one destination)
 // in 16 x 1, [fmt][nsrc - 1]; the one-source dequantization (SUM) in 4 x 4
@@ -324,14 +323,14 @@ __device__ __forceinline__ void drr_finish(const DrrArgs& a, const Chunk<CPC> (&
 #pragma unroll
             for (int j = 0; j < N; ++j)
                 store_codes<CPC>(static_cast<uint8_t*>(a.out_codes[j]), c[u], e[u], count, whole[u], q);
-            if (valid[u] && (lane % lpb) == 0) {
+            if (valid[u] && (lane & (lpb - 1)) == 0) {
 #pragma unroll
                 for (int j = 0; j < N; ++j)
                     store_scale<CPC == 4 && U == 1>(a.out_scales[j] + b[u], s2);
             }
         } else if constexpr (OUT == kDrrRequant) {
             store_codes<CPC>(static_cast<uint8_t*>(a.out_codes[0]), c[u], e[u], count, whole[u], q);
-            if (valid[u] && (lane % lpb) == 0)
+            if (valid[u] && (lane & (lpb - 1)) == 0)
                 store_scale<CPC == 4 && U == 1>(a.out_scales[0] + b[u], s2);
         }
 
@@ -433,20 +432,39 @@ __global__ __launch_bounds__(256) void k_drr(DrrArgs a)
     }
 }
 
-// Decode-size ranges of whole tiles: one tile per 64-thread workgroup, XCD
-// x taking tiles [x R, x R + R) (R = xcd_ranges, whole lines of block
-// scales), without k_drr's loop and partial-tile path. Used for the push
-// and SUM modes: the LP tree step's push of a 32K-code chunk 2.54 -> 2.44
-// us, the one-source dequantization and the flat LP sum about 1% faster.
-// The requantization into one destination measured 0.7% slower this way
-// (2.73 -> 2.75 us with the BF16 output) and keeps k_drr.
+// True if a source's code or scale pointer is null (never, for a validated
+// call). A kernel that adds it to its exit test has every source pointer
+// loaded before that branch, together with the range, instead of after it:
+// one scalar round trip before the first code load instead of two. Written
+// as a minimum over the pointers (two scalar instructions each).
+template <int N>
+__device__ __forceinline__ bool any_source_null(const DrrArgs& a)
+{
+    uint32_t m = ~0u;
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+        const uint32_t c = ptr_nonzero(a.codes[r]), s = ptr_nonzero(a.scales[r]);
+        m = m < c ? m : c;
+        m = m < s ? m : s;
+    }
+    return m == 0;
+}
+
+// Decode-size ranges of whole tiles, every mode: one tile per 64-thread
+// workgroup, XCD x taking tiles [x R, x R + R) (R = xcd_ranges, whole lines
+// of block scales), without k_drr's loop and partial-tile path, and with
+// the source pointers in the exit test (their loads go out with the
+// range's). Against k_drr: the LP tree step's push of a 32K-code chunk
+// 2.54 -> 2.41 us, the requantization of 8 x 256K codes into one
+// destination with the BF16 output 2.73 -> 2.66 us, the one-source
+// dequantization 2.02 -> 1.97 us; the 8-source flat LP sum 2.33 -> 2.34.
 template <int F, int N, bool REQUANT, int CPC, int U, int OUT>
 __global__ __launch_bounds__(256) void k_drr_tile1(DrrArgs a)
 {
     constexpr size_t kTile = (size_t)kWave * CPC * U;
     const uint32_t ntiles = (uint32_t)((a.hi - a.lo) / kTile);
     const uint32_t t = (blockIdx.x % kXcds) * (uint32_t)a.xcd_ranges + blockIdx.x / kXcds;
-    if (t >= ntiles)
+    if ((t >= ntiles) | any_source_null<N>(a))
         return;
     drr_tile<F, N, REQUANT, CPC, U, OUT, true>(a, t, lane_id(), a.lo / CPC, a.hi, __builtin_ctz((unsigned)a.block),
                                                a.block / CPC);
@@ -620,14 +638,14 @@ __device__ __forceinline__ void drr_staged_finish(const Chunk<16> (&x)[N], const
 #pragma unroll
         for (int j = 0; j < N; ++j)
             store_codes<16>(static_cast<uint8_t*>(a.out_codes[j]), c, e, a.hi, true, q);
-        if ((lane % lpb) == 0) {
+        if ((lane & (lpb - 1)) == 0) {
 #pragma unroll
             for (int j = 0; j < N; ++j)
                 store_scale<false>(a.out_scales[j] + b, s2);
         }
     } else if constexpr (OUT == kDrrRequant) {
         store_codes<16>(static_cast<uint8_t*>(a.out_codes[0]), c, e, a.hi, true, q);
-        if ((lane % lpb) == 0)
+        if ((lane & (lpb - 1)) == 0)
             store_scale<false>(a.out_scales[0] + b, s2);
     }
     float h[16];
@@ -740,16 +758,20 @@ void fill_tile1_row(DrrFn* row, std::integer_sequence<int, I...>)
     ((row[I] = &k_drr_tile1<F, I + 1, R, CPC, U, OUT>), ...);
 }
 
-// the SUM and push modes only (the other entries null)
+// every mode
 template <int CPC, int U>
 DrrFns make_tile1_fns()
 {
     DrrFns t{};
     const auto seq = std::make_integer_sequence<int, kMaxSrc>{};
     fill_tile1_row<0, false, CPC, U, kDrrSum>(t.fn[0][kDrrSum], seq);
+    fill_tile1_row<0, true, CPC, U, kDrrRequant>(t.fn[0][kDrrRequant], seq);
     fill_tile1_row<0, true, CPC, U, kDrrRequantPush>(t.fn[0][kDrrRequantPush], seq);
+    fill_tile1_row<0, true, CPC, U, kDrrRequantAll>(t.fn[0][kDrrRequantAll], seq);
     fill_tile1_row<1, false, CPC, U, kDrrSum>(t.fn[1][kDrrSum], seq);
+    fill_tile1_row<1, true, CPC, U, kDrrRequant>(t.fn[1][kDrrRequant], seq);
     fill_tile1_row<1, true, CPC, U, kDrrRequantPush>(t.fn[1][kDrrRequantPush], seq);
+    fill_tile1_row<1, true, CPC, U, kDrrRequantAll>(t.fn[1][kDrrRequantAll], seq);
     return t;
 }
 

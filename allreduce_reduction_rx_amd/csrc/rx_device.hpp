@@ -218,4 +218,14 @@ __host__ __device__ constexpr uint32_t xcd_contiguous(uint32_t b, uint32_t g)
     return x * q + (x < r ? x : r) + i;
 }
 
+// Nonzero iff p is not null. A kernel that tests its pointers for null in
+// the same condition as its range check has them loaded before that branch,
+// together with the other kernel arguments, instead of after it (one scalar
+// round trip less before its first global load).
+__device__ __forceinline__ uint32_t ptr_nonzero(const void* p)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    return (uint32_t)v | (uint32_t)(v >> 32);
+}
+
 }  // namespace rx
