@@ -71,7 +71,18 @@ __global__ __launch_bounds__(256) void k_tree_half(TreeArgs a)
     const size_t v1 = a.hi / VE;
     const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t h = 2 * v0 + gid;
-    if (h < 2 * v1) {
+    // the pointers' null test in the bounds test: every source and
+    // destination pointer is loaded before its branch, with the range (eight
+    // in-place launches over 8 x 512 KiB, the one-device TREE allreduce:
+    // 19.9 -> 18.7 us; the step on separate buffers 2.24 -> 2.25 us)
+    uint32_t m = ~0u;
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+        const uint32_t p = ptr_nonzero(a.src[r]), q = ptr_nonzero(a.dst[r]);
+        m = m < p ? m : p;
+        m = m < q ? m : q;
+    }
+    if ((h < 2 * v1) & (m != 0)) {
         u32x2 x[N];
 #pragma unroll
         for (int r = 0; r < N; ++r)
