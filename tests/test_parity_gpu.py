@@ -237,6 +237,28 @@ def test_quant_shapes(dtype, fmt, block):
             assert bits_equal(gs[j], rs[j]), f"scales count={count} src={j}: " + first_mismatch(gs[j], rs[j])
 
 
+@pytest.mark.parametrize("dtype,fmt,block", [(O.FP32, O.E4M3, 128), (O.BF16, O.E5M2, 256),
+                                             (O.FP32, O.E5M2, 1024), (O.BF16, O.E4M3, 32)])
+def test_quant_decode_whole_tile_rows(dtype, fmt, block):
+    # decode-size sources of whole tiles (the loop-free kernel, one grid row
+    # per source, rows padded to a multiple of 8 workgroups of 4 tiles):
+    # tile counts that leave the last workgroup partly idle or pad the row,
+    # with 1 to 16 sources; unwritten codes or scales keep the sentinel
+    ve = 4 if dtype == O.FP32 else 8
+    lanes = block // ve
+    tile = (1 if lanes <= 64 else lanes // 64) * 64 * ve
+    for n in (1, 3, 8, 16):
+        for t in (1, 2, 3, 4, 5, 7, 8, 9, 31, 32, 33, 37):
+            count = t * tile
+            log(f"quant whole-tile rows dtype={dtype} fmt={fmt} block={block} n={n} tiles={t}")
+            srcs = [G.fill(count, dtype, G.NORMAL_OUTLIER, seed=3700 + 41 * t + n, rank=r) for r in range(n)]
+            gc, gs = _quant_gpu(srcs, dtype, fmt, block, count)
+            rc, rs = O.quant_fp8(srcs, dtype, fmt, block)
+            for j in range(n):
+                assert bits_equal(gc[j], rc[j]), f"codes n={n} tiles={t} src={j}: " + first_mismatch(gc[j], rc[j])
+                assert bits_equal(gs[j], rs[j]), f"scales n={n} tiles={t} src={j}: " + first_mismatch(gs[j], rs[j])
+
+
 @pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
 @pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 256), (O.E4M3, 1024), (O.E5M2, 32)])
 def test_quant_large_variant_ragged(dtype, fmt, block):
