@@ -259,6 +259,23 @@ def test_quant_decode_whole_tile_rows(dtype, fmt, block):
                 assert bits_equal(gs[j], rs[j]), f"scales n={n} tiles={t} src={j}: " + first_mismatch(gs[j], rs[j])
 
 
+@pytest.mark.parametrize("dtype,fmt,block,extra", [(O.BF16, O.E5M2, 256, 512), (O.BF16, O.E5M2, 256, 1536),
+                                                   (O.FP32, O.E4M3, 128, 256), (O.FP32, O.E5M2, 64, 768)])
+def test_quant_large_rest_whole_tiles(dtype, fmt, block, extra):
+    # a large message (whole-tile kernel over 4-load tiles) whose rest is a
+    # whole number of decode-size tiles: the rest runs the loop-free kernel
+    # through pointers offset into the message
+    n = 8
+    count = 4 * 64 * (4 if dtype == O.FP32 else 8) * 256 + extra
+    log(f"quant large rest whole tiles dtype={dtype} fmt={fmt} block={block} count={count}")
+    srcs = [G.fill(count, dtype, G.NORMAL_OUTLIER, seed=3800 + extra, rank=r) for r in range(n)]
+    gc, gs = _quant_gpu(srcs, dtype, fmt, block, count)
+    rc, rs = O.quant_fp8(srcs, dtype, fmt, block)
+    for j in range(n):
+        assert bits_equal(gc[j], rc[j]), f"codes src={j}: " + first_mismatch(gc[j], rc[j])
+        assert bits_equal(gs[j], rs[j]), f"scales src={j}: " + first_mismatch(gs[j], rs[j])
+
+
 @pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
 @pytest.mark.parametrize("fmt,block", [(O.E4M3, 128), (O.E5M2, 256), (O.E4M3, 1024), (O.E5M2, 32)])
 def test_quant_large_variant_ragged(dtype, fmt, block):
