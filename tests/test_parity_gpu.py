@@ -92,12 +92,15 @@ def test_flat_in_place(dtype):
 @pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8, 13, 16])
 @pytest.mark.parametrize("extra", [5, 1021 * 8 + 3])
-def test_flat_large_variant_ragged(n, dtype, extra):
-    # above the decode-size threshold: wave tiles with deferred stores and a
-    # grid-stride loop (whole tiles only for few sources or FP32 up to 8,
-    # the rest of the message in a second launch); ragged element tail; also
-    # in place
-    count = 3 * (1 << 20) + extra
+@pytest.mark.parametrize("mib", [3, 9])
+def test_flat_large_variant_ragged(n, dtype, extra, mib):
+    # above the decode-size threshold. 3M elements: medium (up to 16 whole
+    # tiles per CU on a 256-CU MI355X), a wave per whole tile for up to 8
+    # sources; 9M: large, wave tiles with deferred stores and a grid-stride
+    # loop (whole tiles only for few sources or FP32 up to 8); 13 and 16
+    # sources the checked tile kernel at both sizes; the rest of the message
+    # in a second launch; ragged element tail; also in place
+    count = mib * (1 << 20) + extra
     srcs = [G.fill(count, dtype, G.NORMAL_OUTLIER, seed=1500 + n, rank=r) for r in range(n)]
     ref = O.reduce_flat(srcs, dtype)
     g = Guarded(count, TD[dtype])
@@ -965,6 +968,11 @@ _BOUNDARY_CASES = [
     ("flat", O.FP32, 8, (1 << 19) - 1), ("flat", O.FP32, 8, 1 << 19), ("flat", O.FP32, 8, (1 << 19) + 1),
     ("flat", O.BF16, 3, (1 << 20) - 1), ("flat", O.BF16, 3, (1 << 20) + 1),
     ("flat", O.BF16, 8, (1 << 20) + 1), ("flat", O.FP32, 13, (1 << 19) + 3),
+    # flat reduce: medium up to 16 whole tiles per CU (4096 tiles of 256
+    # vectors), large above
+    ("flat", O.BF16, 8, (1 << 23) + 3), ("flat", O.BF16, 8, (1 << 23) + 2048 + 1),
+    ("flat", O.FP32, 5, (1 << 22) + 1), ("flat", O.FP32, 5, (1 << 22) + 1024 + 3),
+    ("flat", O.BF16, 6, (1 << 20) - 8 + 1), ("flat", O.BF16, 2, (1 << 20) + 2048 * 3 + 7),
     # quantizer, 8 FP32 sources: decode-size below 2,048 tiles of 1024,
     # four workgroups per CU below 16,384, two above
     ("quant", O.FP32, 8, 255 * 1024), ("quant", O.FP32, 8, 255 * 1024 + 1), ("quant", O.FP32, 8, 256 * 1024),
