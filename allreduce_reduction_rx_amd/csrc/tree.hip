@@ -118,7 +118,8 @@ __global__ __launch_bounds__(256) void k_tree_half(TreeArgs a)
         tree_tail<DT, N>(a, v1 > v0 ? v1 : v0, gid);
 }
 
-// Large BF16 chunks: whole tiles of 64 vectors (one per lane) from lo; the
+// Large BF16 chunks, and chunks of either type of 6 to 8 tiles per CU (a
+// wave per tile; see launch_tree): whole tiles of 64 vectors (one per lane) from lo; the
 // N loads of a lane first, then the fold, then its N stores; no bounds check
 // in the loop (the rest of the chunk goes to k_tree). Launched as four
 // 64-thread workgroups per CU: 8 x 16M BF16 in place (the one-device FLAT
@@ -177,8 +178,10 @@ const std::array<TreeFn, kMaxSrc> kTreeHalf[2][2] = {
      tree_half_table<0, true>(std::make_integer_sequence<int, kMaxSrc>{})},
     {tree_half_table<1, false>(std::make_integer_sequence<int, kMaxSrc>{}),
      tree_half_table<1, true>(std::make_integer_sequence<int, kMaxSrc>{})}};
-// BF16 only (large FP32 chunks run k_tree)
-const std::array<TreeFn, kMaxSrc> kTreeWhole = tree_whole_table<1>(std::make_integer_sequence<int, kMaxSrc>{});
+// [dtype][nsrc - 1]: medium chunks of either type, large BF16 chunks (large
+// FP32 chunks run k_tree)
+const std::array<TreeFn, kMaxSrc> kTreeWhole[2] = {tree_whole_table<0>(std::make_integer_sequence<int, kMaxSrc>{}),
+                                                   tree_whole_table<1>(std::make_integer_sequence<int, kMaxSrc>{})};
 
 // Decode-size chunks run 64-thread workgroups (at 8 x 4 MiB, 2.98 us
 // against 3.06 us with 128 threads).
@@ -192,16 +195,33 @@ hipError_t launch_tree(const TreeArgs& a, int nsrc, int dtype, hipStream_t s)
     const int ve = dtype == 0 ? 4 : 8;
     const size_t nvec = (a.hi - a.lo) / ve;
     const bool small = small_job(nvec);
+    const size_t cus = (size_t)device_cu_count();
+    const size_t tiles = nvec / kWave;
+    // Chunks of 6 to 8 whole 64-vector tiles per CU (around the decode-size
+    // threshold): k_tree_whole with a wave for every tile, 64-thread
+    // workgroups, 256-thread ones from 8 tiles per CU. Against the
+    // two-lanes-per-vector kernel below 8 and the grid-stride launch at 8,
+    // for 2, 4 and 8 sources of either type: 2-27% faster (8 sources, 8
+    // tiles per CU: BF16 8.28 -> 6.68 us, FP32 8.62 -> 6.96); at 4-5 tiles
+    // per CU and at 10 and more it was not faster.
+    const bool medium = tiles >= 6 * cus && tiles <= 8 * cus;
     dim3 grid, block;
-    if (!small && dtype != 0) {
-        // large BF16 chunks: whole tiles of 64 vectors, then the rest of the
-        // chunk (fewer than 64 vectors and the element tail) in k_tree
-        const size_t tiles = nvec / kWave;
-        launch_geometry(tiles * kWave, false, policy_tree_whole(), grid, block);
+    if (medium || (!small && dtype != 0)) {
+        // medium chunks, and large BF16 chunks: whole tiles of 64 vectors,
+        // then the rest of the chunk (fewer than 64 vectors and the element
+        // tail) in k_tree
+        if (medium) {
+            const unsigned wg = tiles >= 8 * cus ? 256u : 64u;
+            grid = dim3((unsigned)((tiles * kWave + wg - 1) / wg));
+            block = dim3(wg);
+        } else {
+            launch_geometry(tiles * kWave, false, policy_tree_whole(), grid, block);
+        }
         TreeArgs arg = a;
         arg.hi = a.lo + tiles * kWave * ve;
         void* params[] = {&arg};
-        const hipError_t e = launch_logged("k_tree_whole", (const void*)kTreeWhole[nsrc - 1], grid, block, params, s);
+        const hipError_t e = launch_logged(medium ? "k_tree_whole (medium)" : "k_tree_whole",
+                                           (const void*)kTreeWhole[dtype][nsrc - 1], grid, block, params, s);
         if (e != hipSuccess || arg.hi == a.hi)
             return e;
         TreeArgs rest = a;

@@ -184,12 +184,28 @@ def test_tree_shapes(n, dtype):
 
 
 @pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
+@pytest.mark.parametrize("n", [2, 5, 8])
+@pytest.mark.parametrize("tiles_per_cu", [6, 7, 8])
+def test_tree_medium_band(n, dtype, tiles_per_cu):
+    # chunks of 6 to 8 whole 64-vector tiles per CU on a 256-CU MI355X: a
+    # wave per tile, then the rest of the chunk; ragged message end; ranks
+    # 0 and 1 and the last (a short chunk, below the band)
+    ve = 4 if dtype == O.FP32 else 8
+    count = n * tiles_per_cu * 256 * 64 * ve + 9
+    srcs = [G.fill(count, dtype, G.NORMAL, seed=2600 + 10 * n + tiles_per_cu, rank=r) for r in range(n)]
+    for k in (0, 1, n - 1):
+        log(f"tree medium n={n} dtype={dtype} tiles/CU={tiles_per_cu} rank={k}")
+        _tree_case(srcs, dtype, count, k)
+
+
+@pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
 @pytest.mark.parametrize("n", [3, 8, 16])
 def test_tree_large_variant_ragged(n, dtype):
-    # chunks above the decode-size threshold (whole tiles and the rest of the
-    # chunk for BF16), ragged message end; ranks 0 and 1 (chunks from the
-    # start and from inside the message) and the last (a short chunk)
-    count = n * (1 << 20) + 9
+    # chunks above the medium band (whole tiles and the rest of the chunk
+    # for BF16; FP32 two lanes per vector), ragged message end; ranks 0 and 1
+    # (chunks from the start and from inside the message) and the last (a
+    # short chunk)
+    count = n * (1 << 21) + 9
     srcs = [G.fill(count, dtype, G.NORMAL, seed=2500 + n, rank=r) for r in range(n)]
     for k in (0, 1, n - 1):
         log(f"tree large n={n} dtype={dtype} rank={k}")
