@@ -993,6 +993,10 @@ _BOUNDARY_CASES = [
     # four workgroups per CU below 16,384, two above
     ("quant", O.FP32, 8, 255 * 1024), ("quant", O.FP32, 8, 255 * 1024 + 1), ("quant", O.FP32, 8, 256 * 1024),
     ("quant", O.FP32, 8, 2047 * 1024), ("quant", O.FP32, 8, 2047 * 1024 + 1), ("quant", O.BF16, 8, 2048 * 1024 + 7),
+    # whole decode-size tiles: the loop-free kernel up to 16 (BF16) or 8
+    # (FP32) large tiles per CU, the large kernels above and for ragged counts
+    ("quant", O.BF16, 8, 1 << 20), ("quant", O.BF16, 8, (1 << 20) + 512), ("quant", O.BF16, 8, (1 << 20) - 509),
+    ("quant", O.FP32, 8, 288 * 1024),
     # DRR: decode-size below 1,024 tiles of 1024 codes; codes only: four
     # workgroups per CU below 8,192 tiles
     ("drr", O.FP32, 8, 1023 * 1024), ("drr", O.FP32, 8, 1023 * 1024 + 1), ("drr", O.FP32, 8, 1024 * 1024 + 5),
