@@ -196,6 +196,18 @@ def test_tree_medium_band(n, dtype, tiles_per_cu):
     for k in (0, 1, n - 1):
         log(f"tree medium n={n} dtype={dtype} tiles/CU={tiles_per_cu} rank={k}")
         _tree_case(srcs, dtype, count, k)
+    # in place (the one-device TREE allreduce's use): sources are the
+    # destinations
+    k = 1
+    log(f"tree medium in place n={n} dtype={dtype} tiles/CU={tiles_per_cu} rank={k}")
+    ts = [to_gpu(s) for s in srcs]
+    rx.rx_reduce_scatter_chunk_bcast(ts, k, ts)
+    sync()
+    ref = [s.copy() for s in srcs]
+    O.reduce_scatter_chunk_bcast(srcs, dtype, k, ref)
+    for j in range(n):
+        got = to_host(ts[j])
+        assert bits_equal(got, ref[j]), f"in place dst {j}: " + first_mismatch(got, ref[j])
 
 
 @pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
