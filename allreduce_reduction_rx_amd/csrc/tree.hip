@@ -57,24 +57,24 @@ __global__ __launch_bounds__(256) void k_tree(TreeArgs a)
 }
 
 // Small chunks (up to one 64-thread workgroup of half-vector lanes per CU):
-// each lane folds one 8-byte half of a 16-byte vector over all N sources and
-// stores it into all N destinations; no load is issued twice (8 x 512 KiB
-// messages, chunk 64 KiB: 2.26 us against 2.30 us for two lanes per vector).
-// The grid holds a lane for every half vector, so there is no loop (8 x 512
-// KiB BF16 messages, chunk 64 KiB: 2.34 us against 2.44 us for the same
-// lanes in a grid-stride loop that runs once).
+// each lane folds one 4-byte word (one FP32 or two BF16 elements) over all N
+// sources and stores it into all N destinations; no load is issued twice.
+// Four lanes per 16-byte vector spread a decode-size chunk over every CU
+// (8 x 512 KiB BF16 messages, chunk 64 KiB: 2.33 -> 2.14 us against
+// 8-byte lanes, which filled half the CUs; chunks of 32 and 128 KiB 7% and 3%
+// faster). The grid holds a lane for every word, so there is no loop. The
+// pointers' null test in the bounds test loads every source and destination
+// pointer before its branch, with the range (eight in-place launches over
+// 8 x 512 KiB, the one-device TREE allreduce: 19.9 -> 18.7 us). TAIL: a BF16
+// chunk that ends on an odd element; its last element is folded alone.
 template <int DT, int N, bool TAIL>
-__global__ __launch_bounds__(256) void k_tree_half(TreeArgs a)
+__global__ __launch_bounds__(256) void k_tree_word(TreeArgs a)
 {
-    constexpr int VE = Elem<DT>::kVE;
-    const size_t v0 = a.lo / VE;
-    const size_t v1 = a.hi / VE;
+    constexpr int WE = DT == 0 ? 1 : 2;        // elements per 4-byte word
+    const size_t w0 = a.lo / WE;               // lo is a vector multiple
+    const size_t w1 = a.hi / WE;
     const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t h = 2 * v0 + gid;
-    // the pointers' null test in the bounds test: every source and
-    // destination pointer is loaded before its branch, with the range (eight
-    // in-place launches over 8 x 512 KiB, the one-device TREE allreduce:
-    // 19.9 -> 18.7 us; the step on separate buffers 2.24 -> 2.25 us)
+    const size_t w = w0 + gid;
     uint32_t m = ~0u;
 #pragma unroll
     for (int r = 0; r < N; ++r) {
@@ -82,40 +82,41 @@ __global__ __launch_bounds__(256) void k_tree_half(TreeArgs a)
         m = m < p ? m : p;
         m = m < q ? m : q;
     }
-    if ((h < 2 * v1) & (m != 0)) {
-        u32x2 x[N];
+    if ((w < w1) & (m != 0)) {
+        uint32_t x[N];
 #pragma unroll
         for (int r = 0; r < N; ++r)
-            x[r] = __builtin_nontemporal_load(static_cast<const u32x2*>(a.src[r]) + h);
-        u32x2 y;
+            x[r] = __builtin_nontemporal_load(static_cast<const uint32_t*>(a.src[r]) + w);
+        uint32_t y;
         if constexpr (DT == 0) {
+            float acc = bits_f32(x[0]);
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                float acc = bits_f32(x[0][k]);
-#pragma unroll
-                for (int r = 1; r < N; ++r)
-                    acc = acc + bits_f32(x[r][k]);
-                y[k] = __builtin_bit_cast(uint32_t, acc);
-            }
+            for (int r = 1; r < N; ++r)
+                acc = acc + bits_f32(x[r]);
+            y = __builtin_bit_cast(uint32_t, acc);
         } else {
+            float lo = bf16_lo(x[0]);
+            float hi = bf16_hi(x[0]);
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                float lo = bf16_lo(x[0][k]);
-                float hi = bf16_hi(x[0][k]);
-#pragma unroll
-                for (int r = 1; r < N; ++r) {
-                    lo = lo + bf16_lo(x[r][k]);
-                    hi = hi + bf16_hi(x[r][k]);
-                }
-                y[k] = pack_bf16(lo, hi);
+            for (int r = 1; r < N; ++r) {
+                lo = lo + bf16_lo(x[r]);
+                hi = hi + bf16_hi(x[r]);
             }
+            y = pack_bf16(lo, hi);
         }
 #pragma unroll
         for (int j = 0; j < N; ++j)
-            __builtin_nontemporal_store(y, static_cast<u32x2*>(a.dst[j]) + h);
+            __builtin_nontemporal_store(y, static_cast<uint32_t*>(a.dst[j]) + w);
     }
-    if constexpr (TAIL)
-        tree_tail<DT, N>(a, v1 > v0 ? v1 : v0, gid);
+    if constexpr (TAIL) {
+        const size_t i = (w1 > w0 ? w1 : w0) * WE + gid;
+        if (i >= a.lo && i < a.hi) {
+            const float z = fold_vec_tail<DT, N>(a.src, i);
+#pragma unroll
+            for (int j = 0; j < N; ++j)
+                store_elem<DT>(a.dst[j], i, z);
+        }
+    }
 }
 
 // Large BF16 chunks, and chunks of either type of 6 to 8 tiles per CU (a
@@ -156,9 +157,9 @@ constexpr std::array<TreeFn, sizeof...(I)> tree_table(std::integer_sequence<int,
     return {{&k_tree<DT, I + 1, TAIL>...}};
 }
 template <int DT, bool TAIL, int... I>
-constexpr std::array<TreeFn, sizeof...(I)> tree_half_table(std::integer_sequence<int, I...>)
+constexpr std::array<TreeFn, sizeof...(I)> tree_word_table(std::integer_sequence<int, I...>)
 {
-    return {{&k_tree_half<DT, I + 1, TAIL>...}};
+    return {{&k_tree_word<DT, I + 1, TAIL>...}};
 }
 template <int DT, int... I>
 constexpr std::array<TreeFn, sizeof...(I)> tree_whole_table(std::integer_sequence<int, I...>)
@@ -173,11 +174,12 @@ const std::array<TreeFn, kMaxSrc> kTree[2][2] = {
      tree_table<0, true>(std::make_integer_sequence<int, kMaxSrc>{})},
     {tree_table<1, false>(std::make_integer_sequence<int, kMaxSrc>{}),
      tree_table<1, true>(std::make_integer_sequence<int, kMaxSrc>{})}};
-const std::array<TreeFn, kMaxSrc> kTreeHalf[2][2] = {
-    {tree_half_table<0, false>(std::make_integer_sequence<int, kMaxSrc>{}),
-     tree_half_table<0, true>(std::make_integer_sequence<int, kMaxSrc>{})},
-    {tree_half_table<1, false>(std::make_integer_sequence<int, kMaxSrc>{}),
-     tree_half_table<1, true>(std::make_integer_sequence<int, kMaxSrc>{})}};
+// [dtype][tail][nsrc - 1]; tail: a BF16 chunk ending on an odd element
+const std::array<TreeFn, kMaxSrc> kTreeWord[2][2] = {
+    {tree_word_table<0, false>(std::make_integer_sequence<int, kMaxSrc>{}),
+     tree_word_table<0, true>(std::make_integer_sequence<int, kMaxSrc>{})},
+    {tree_word_table<1, false>(std::make_integer_sequence<int, kMaxSrc>{}),
+     tree_word_table<1, true>(std::make_integer_sequence<int, kMaxSrc>{})}};
 // [dtype][nsrc - 1]: medium chunks of either type, large BF16 chunks (large
 // FP32 chunks run k_tree)
 const std::array<TreeFn, kMaxSrc> kTreeWhole[2] = {tree_whole_table<0>(std::make_integer_sequence<int, kMaxSrc>{}),
@@ -231,18 +233,23 @@ hipError_t launch_tree(const TreeArgs& a, int nsrc, int dtype, hipStream_t s)
         void* rparams[] = {&rest};
         return launch_logged("k_tree (rest)", (const void*)kTree[dtype][tail][nsrc - 1], grid, block, rparams, s);
     }
-    const int tail = a.hi % (size_t)ve != 0 ? 1 : 0;   // lo is a vector multiple
-    // small chunks: half-vector lanes while they fit one 64-thread workgroup
-    // per CU, two lanes per vector above that; a small launch's grid is not
-    // capped, so k_tree_half gets a lane for every half vector
-    const bool half = small && 2 * nvec <= (size_t)64 * (size_t)device_cu_count();
-    launch_geometry(small ? 2 * nvec : nvec, small, policy_tree(), grid, block);
-    if (half && (size_t)grid.x * block.x < 2 * nvec)
-        return hipErrorInvalidConfiguration;
     TreeArgs arg = a;
     void* params[] = {&arg};
-    const TreeFn fn = half ? kTreeHalf[dtype][tail][nsrc - 1] : kTree[dtype][tail][nsrc - 1];
-    return launch_logged(half ? "k_tree_half" : "k_tree", (const void*)fn, grid, block, params, s);
+    // small chunks: 4-byte-word lanes while 8-byte lanes would fit one
+    // 64-thread workgroup per CU, two lanes per vector above that; a small
+    // launch's grid is not capped, so k_tree_word gets a lane for every word
+    if (small && 2 * nvec <= (size_t)64 * cus) {
+        const size_t we = dtype == 0 ? 1 : 2;            // elements per word
+        const size_t words = a.hi / we - a.lo / we;      // lo is a vector multiple
+        const int wtail = a.hi % we != 0 ? 1 : 0;
+        launch_geometry(words, true, policy_tree(), grid, block);
+        if ((size_t)grid.x * block.x < words)
+            return hipErrorInvalidConfiguration;
+        return launch_logged("k_tree_word", (const void*)kTreeWord[dtype][wtail][nsrc - 1], grid, block, params, s);
+    }
+    const int tail = a.hi % (size_t)ve != 0 ? 1 : 0;   // lo is a vector multiple
+    launch_geometry(small ? 2 * nvec : nvec, small, policy_tree(), grid, block);
+    return launch_logged("k_tree", (const void*)kTree[dtype][tail][nsrc - 1], grid, block, params, s);
 }
 
 }  // namespace rx
