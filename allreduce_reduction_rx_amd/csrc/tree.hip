@@ -180,8 +180,8 @@ const std::array<TreeFn, kMaxSrc> kTreeWord[2][2] = {
      tree_word_table<0, true>(std::make_integer_sequence<int, kMaxSrc>{})},
     {tree_word_table<1, false>(std::make_integer_sequence<int, kMaxSrc>{}),
      tree_word_table<1, true>(std::make_integer_sequence<int, kMaxSrc>{})}};
-// [dtype][nsrc - 1]: medium chunks of either type, large BF16 chunks (large
-// FP32 chunks run k_tree)
+// [dtype][nsrc - 1]: medium chunks of either type, large BF16 chunks, large
+// FP32 chunks from 64 tiles per CU
 const std::array<TreeFn, kMaxSrc> kTreeWhole[2] = {tree_whole_table<0>(std::make_integer_sequence<int, kMaxSrc>{}),
                                                    tree_whole_table<1>(std::make_integer_sequence<int, kMaxSrc>{})};
 
@@ -207,11 +207,15 @@ hipError_t launch_tree(const TreeArgs& a, int nsrc, int dtype, hipStream_t s)
     // tiles per CU: BF16 8.28 -> 6.68 us, FP32 8.62 -> 6.96); at 4-5 tiles
     // per CU and at 10 and more it was not faster.
     const bool medium = tiles >= 6 * cus && tiles <= 8 * cus;
+    // Large FP32 chunks from 64 tiles per CU also take k_tree_whole (8 x 32M
+    // FP32 46.5 -> 45.4 us, 8 x 64M 93.5 -> 90.4; at 48 tiles per CU and
+    // below k_tree was as fast or up to 2% faster)
+    const bool whole = medium || (!small && (dtype != 0 || tiles >= 64 * cus));
     dim3 grid, block;
-    if (medium || (!small && dtype != 0)) {
-        // medium chunks, and large BF16 chunks: whole tiles of 64 vectors,
-        // then the rest of the chunk (fewer than 64 vectors and the element
-        // tail) in k_tree
+    if (whole) {
+        // medium chunks, large BF16 chunks, large FP32 chunks from 64 tiles
+        // per CU: whole tiles of 64 vectors, then the rest of the chunk
+        // (fewer than 64 vectors and the element tail) in k_tree
         if (medium) {
             const unsigned wg = tiles >= 8 * cus ? 256u : 64u;
             grid = dim3((unsigned)((tiles * kWave + wg - 1) / wg));

@@ -210,6 +210,18 @@ def test_tree_medium_band(n, dtype, tiles_per_cu):
         assert bits_equal(got, ref[j]), f"in place dst {j}: " + first_mismatch(got, ref[j])
 
 
+@pytest.mark.parametrize("n", [3, 8])
+def test_tree_large_fp32_whole_tiles(n):
+    # FP32 chunks of 64 and more 64-vector tiles per CU on a 256-CU MI355X:
+    # whole tiles with four 64-thread workgroups per CU, then the rest of the
+    # chunk; ragged message end; ranks 0 and the last
+    count = n * 64 * 256 * 64 * 4 + 9
+    srcs = [G.fill(count, O.FP32, G.NORMAL, seed=2700 + n, rank=r) for r in range(n)]
+    for k in (0, n - 1):
+        log(f"tree large fp32 whole n={n} rank={k}")
+        _tree_case(srcs, O.FP32, count, k)
+
+
 @pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
 @pytest.mark.parametrize("n", [3, 8, 16])
 def test_tree_large_variant_ragged(n, dtype):
