@@ -119,13 +119,14 @@ __global__ __launch_bounds__(256) void k_tree_word(TreeArgs a)
     }
 }
 
-// Large BF16 chunks, and chunks of either type of 6 to 8 tiles per CU (a
-// wave per tile; see launch_tree): whole tiles of 64 vectors (one per lane) from lo; the
-// N loads of a lane first, then the fold, then its N stores; no bounds check
-// in the loop (the rest of the chunk goes to k_tree). Launched as four
-// 64-thread workgroups per CU: 8 x 16M BF16 in place (the one-device FLAT
-// allreduce) 97.7 -> 89.6 us, 8 x 256M 1579 -> 1524 us, against 2-vector
-// tiles with bounds checks in one 256-thread workgroup per CU.
+// Large BF16 chunks, large FP32 chunks from 64 tiles per CU, and chunks of
+// either type of 6 to 8 tiles per CU (a wave per tile; see launch_tree):
+// whole tiles of 64 vectors (one per lane) from lo; the N loads of a lane
+// first, then the fold, then its N stores; no bounds check in the loop (the
+// rest of the chunk goes to k_tree). Large chunks launch four 64-thread
+// workgroups per CU: 8 x 16M BF16 in place (the one-device FLAT allreduce)
+// 97.7 -> 89.6 us, 8 x 256M 1579 -> 1524 us, against 2-vector tiles with
+// bounds checks in one 256-thread workgroup per CU.
 template <int DT, int N>
 __global__ __launch_bounds__(256) void k_tree_whole(TreeArgs a)
 {
