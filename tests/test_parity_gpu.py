@@ -184,7 +184,7 @@ def test_tree_shapes(n, dtype):
 
 
 @pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
-@pytest.mark.parametrize("n", [2, 5, 8])
+@pytest.mark.parametrize("n", [2, 5, 8, 16])
 @pytest.mark.parametrize("tiles_per_cu", [6, 7, 8])
 def test_tree_medium_band(n, dtype, tiles_per_cu):
     # chunks of 6 to 8 whole 64-vector tiles per CU on a 256-CU MI355X: a
