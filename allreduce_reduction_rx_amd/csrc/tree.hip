@@ -240,10 +240,13 @@ hipError_t launch_tree(const TreeArgs& a, int nsrc, int dtype, hipStream_t s)
     }
     TreeArgs arg = a;
     void* params[] = {&arg};
-    // small chunks: 4-byte-word lanes while 8-byte lanes would fit one
-    // 64-thread workgroup per CU, two lanes per vector above that; a small
-    // launch's grid is not capped, so k_tree_word gets a lane for every word
-    if (small && 2 * nvec <= (size_t)64 * cus) {
+    // small chunks: 4-byte-word lanes while the words fit six waves per CU
+    // (8 x 1M BF16, chunk 128K elements: 2.65 -> 2.41 us, chunk 192K 2.78 ->
+    // 2.63; at eight waves per CU, 8 x 2M BF16, two lanes per vector were
+    // faster, 2.97 against 3.16 us), two lanes per vector above that; a
+    // small launch's grid is not capped, so k_tree_word gets a lane for
+    // every word
+    if (small && 4 * nvec <= (size_t)6 * kWave * cus) {
         const size_t we = dtype == 0 ? 1 : 2;            // elements per word
         const size_t words = a.hi / we - a.lo / we;      // lo is a vector multiple
         const int wtail = a.hi % we != 0 ? 1 : 0;

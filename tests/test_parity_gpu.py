@@ -236,6 +236,21 @@ def test_tree_large_variant_ragged(n, dtype):
         _tree_case(srcs, dtype, count, k)
 
 
+@pytest.mark.parametrize("dtype", [O.FP32, O.BF16])
+@pytest.mark.parametrize("extra_vectors,extra", [(0, 0), (0, 9), (1, 0), (1, 3)])
+def test_tree_word_lane_boundary(dtype, extra_vectors, extra):
+    # decode-size chunks: 4-byte-word lanes while the words fit six waves per
+    # CU on a 256-CU MI355X (24,576 16-byte vectors), two lanes per vector
+    # above; chunks at the limit and one vector past it, whole and ragged
+    n = 8
+    ve = 4 if dtype == O.FP32 else 8
+    count = n * (24576 + extra_vectors) * ve + extra
+    srcs = [G.fill(count, dtype, G.NORMAL, seed=2800 + 10 * extra_vectors + extra, rank=r) for r in range(n)]
+    for k in (0, n - 1):
+        log(f"tree word-lane boundary dtype={dtype} count={count} rank={k}")
+        _tree_case(srcs, dtype, count, k)
+
+
 def test_tree_in_place():
     n, count, dtype = 8, 65536 + 24, O.BF16
     srcs = [G.fill(count, dtype, G.NORMAL, seed=99, rank=r) for r in range(n)]
