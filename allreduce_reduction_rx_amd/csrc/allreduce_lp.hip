@@ -272,9 +272,11 @@ const LpNarrowTable<1> kLpB16E5Narrow = make_lp_narrow_table<1>();
 
 // Launch shape by the number of 16-byte-lane tiles T (measured on MI355X,
 // 8 ranks, HBM-cold rotating buffers):
-//  - T <= 2 per CU, BF16, blocks <= 256: 8-byte lanes, one tile per wave in
+//  - T <= 8 per CU, BF16, blocks <= 256: 8-byte lanes, one tile per wave in
 //    256-thread workgroups, each XCD a contiguous range (8 x 512 KiB
-//    E5M2/256: 4.2 us against 4.8 us with 16-byte lanes);
+//    E5M2/256: 4.2 us against 4.8 us with 16-byte lanes; 8 x 1 MiB 5.09 ->
+//    4.89 us, 8 x 2 MiB 7.26 -> 7.16 against 16-byte lanes below; at 16 per
+//    CU 16-byte lanes were faster, 14.6 against 15.2 us at 8 x 4 MiB);
 //  - T <= 16 per CU: 256-thread workgroups, at most 2 per CU (8 x 2 MiB FP32
 //    E4M3/128: 6.9 us against 9.5 us; 8 x 4 MiB BF16: 14.8 against 15.3);
 //  - larger: four 64-thread workgroups per CU (one wave per SIMD),
@@ -301,7 +303,7 @@ hipError_t launch_allreduce_lp(const AllreduceLpArgs& a, int nsrc, int dtype, in
     const size_t cus = (size_t)device_cu_count();
     const size_t ve = dtype == 0 ? 4 : 8;
     const size_t tiles = (a.count + 64 * ve - 1) / (64 * ve);     // 16-byte-lane tiles
-    const bool narrow = dtype == 1 && block <= 256 && tiles <= 2 * cus;
+    const bool narrow = dtype == 1 && block <= 256 && tiles <= 8 * cus;
     const bool medium = !narrow && tiles <= 16 * cus;
     dim3 grid, blk;
     AllreduceLpArgs arg = a;

@@ -1040,9 +1040,10 @@ _BOUNDARY_CASES = [
     # workgroups per CU below 8,192 tiles
     ("drr", O.FP32, 8, 1023 * 1024), ("drr", O.FP32, 8, 1023 * 1024 + 1), ("drr", O.FP32, 8, 1024 * 1024 + 5),
     ("drr", O.FP32, 8, 8191 * 1024 - 5), ("drr", O.FP32, 8, 8192 * 1024 + 3),
-    # one-pass LP allreduce: BF16 8-byte lanes up to 512 tiles of 512,
+    # one-pass LP allreduce: BF16 8-byte lanes up to 2,048 tiles of 512,
     # 256-thread workgroups up to 4,096 tiles (FP32: tiles of 256)
     ("lp", O.BF16, 8, 512 * 512), ("lp", O.BF16, 8, 512 * 512 + 1), ("lp", O.BF16, 8, 4096 * 512 + 1),
+    ("lp", O.BF16, 8, 2048 * 512), ("lp", O.BF16, 8, 2048 * 512 - 3), ("lp", O.BF16, 8, 2048 * 512 + 1),
     ("lp", O.FP32, 8, 4096 * 256), ("lp", O.FP32, 8, 4096 * 256 + 1),
 ]
 
